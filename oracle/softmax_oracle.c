@@ -1,0 +1,141 @@
+/*
+ * softmax_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU reference for the numerically stable row
+ * softmax, computed in double precision.  It exists to check the GPU library;
+ * it is not part of the product.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no source, header,
+ * table or helper with the HIP library, and includes no HIP header.
+ *
+ * What it computes (the plain definition, written out):
+ *   for every row i:   m_i  = max_j x_ij
+ *                      y_ij = exp(x_ij - m_i) / sum_k exp(x_ik - m_i)
+ * Sources:
+ *   - "I Wrote My First GPU Kernel", section "What Fusion Actually Does":
+ *     subtract the row max before exponentiating so that large entries
+ *     (the page's example is 100) cannot overflow; then normalise by the sum.
+ *   - "fused-softmax-roofline" (henryhe.ai), the row-softmax fragment:
+ *     shift by the row max, exponentiate, divide by the sum.
+ *   - "GPU Kernels - Implementing and optimizing Softmax", section
+ *     "Baseline & Triton Softmax kernel": max, subtract, exp, sum, divide,
+ *     and the remark that exp(-inf) = 0 so masked columns add nothing.
+ *   - "Dissecting Memory Bandwidth & SRAM Tiling in Triton", section
+ *     "The Mathematical Remedy: Online Softmax Tiling": the two-pass form
+ *     m = max x, l = sum exp(x - m), p = exp(x - m) / l.
+ *
+ * Readings where the pages are silent (each is listed with the design notes):
+ *   - a row whose entries are all -inf has no finite maximum; its outputs
+ *     are all +0 (the pages' masking rule, under which a masked column
+ *     contributes and receives zero, applied to every column);
+ *   - +inf and NaN inputs are outside the contract and are not special-cased;
+ *   - fp16 and bf16 inputs are decoded exactly from their bit patterns by
+ *     the two decoders below (IEEE 754 binary16, and bfloat16 = the upper 16
+ *     bits of an IEEE 754 binary32).
+ *
+ * Precision: every step runs in double.  The sum is a plain left-to-right
+ * double sum; its relative error is at most cols * 2^-53 (about 2e-12 at
+ * 16384 columns), far below any tolerance the GPU path is held to.
+ *
+ * Build: gcc -O2 -std=c11 -shared -fPIC, never with -ffast-math (the -inf
+ * handling relies on IEEE semantics).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_F16 1
+#define ORACLE_BF16 2
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_decode_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);               /* subnormal: frac * 2^-14 / 2^10 */
+    } else if (expo == 31) {
+        v = (frac == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/2^10) * 2^(expo-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_decode_bf16(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int expo = (b >> 7) & 0xff;
+    int frac = b & 0x7f;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -133);              /* subnormal: frac * 2^-126 / 2^7 */
+    } else if (expo == 255) {
+        v = (frac == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(128 + frac), expo - 134); /* (1 + frac/2^7) * 2^(expo-127) */
+    }
+    return sign ? -v : v;
+}
+
+/* Element (i, j) of the input, exactly as a double. */
+static double load_element(const void *in, int dtype, int64_t index)
+{
+    if (dtype == ORACLE_F32) {
+        float f;
+        memcpy(&f, (const char *)in + index * 4, 4);
+        return (double)f;
+    } else {
+        uint16_t bits;
+        memcpy(&bits, (const char *)in + index * 2, 2);
+        return dtype == ORACLE_F16 ? oracle_decode_f16(bits) : oracle_decode_bf16(bits);
+    }
+}
+
+/*
+ * Row softmax of a rows x cols matrix stored row-major with a row stride of
+ * row_stride elements.  out receives rows * cols doubles, dense (row i at
+ * out + i * cols).  Returns 0 on success, -1 on a bad argument.
+ */
+int oracle_softmax(const void *in, int dtype, int64_t rows, int64_t cols,
+                   int64_t row_stride, double *out)
+{
+    if (rows < 0 || cols < 0 || row_stride < cols) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (rows == 0 || cols == 0) return 0;
+    if (in == NULL || out == NULL) return -1;
+
+    for (int64_t i = 0; i < rows; ++i) {
+        double *y = out + i * cols;
+
+        /* Decode the row once; y doubles as storage for x and then e. */
+        for (int64_t j = 0; j < cols; ++j)
+            y[j] = load_element(in, dtype, i * row_stride + j);
+
+        /* Row maximum, seeded with -inf. */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < cols; ++j)
+            if (y[j] > m) m = y[j];
+
+        /* All entries -inf: no finite maximum, every output is +0. */
+        if (m == -INFINITY) {
+            for (int64_t j = 0; j < cols; ++j) y[j] = 0.0;
+            continue;
+        }
+
+        /* Shifted exponentials and their sum; exp(-inf) is exactly +0. */
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            y[j] = exp(y[j] - m);
+            s += y[j];
+        }
+
+        /* Normalise with a true division. */
+        for (int64_t j = 0; j < cols; ++j)
+            y[j] = y[j] / s;
+    }
+    return 0;
+}

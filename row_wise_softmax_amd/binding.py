@@ -1,0 +1,193 @@
+"""ctypes binding of the HIP row-softmax library (argument marshalling only).
+
+Every step of the softmax runs in the library's HIP kernels; this module only
+turns torch tensors into pointers, sizes and the current stream, and maps
+status codes to exceptions.  There is no CPU or PyTorch fallback: if the
+library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "librow_wise_softmax.so"
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "lib", LIB_NAME)
+
+
+# dtype codes of the C ABI
+F32, F16, BF16 = 0, 1, 2
+# kernel variants of the C ABI
+VARIANT_NAMES = {0: "packed", 1: "row", 2: "online"}
+
+_lib = None
+
+
+class SoftmaxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _status_string(status) if _lib is not None else f"status {status}"
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"row_wise_softmax_amd: HIP library not built ({path} missing); "
+            "run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.softmax_fwd.restype = i32
+    lib.softmax_fwd.argtypes = [vp, vp, i64, i64, i64, i32, vp]
+    lib.softmax_fwd_kernel.restype = i32
+    lib.softmax_fwd_kernel.argtypes = [i32, vp, vp, i64, i64, i64, i32, vp]
+    lib.softmax_select.restype = i32
+    lib.softmax_select.argtypes = [vp, vp, i64, i64, i64, i32, ctypes.POINTER(i32)]
+    lib.softmax_num_kernels.restype = i32
+    lib.softmax_num_kernels.argtypes = []
+    lib.softmax_kernel_info.restype = i32
+    lib.softmax_kernel_info.argtypes = [i32] + [ctypes.POINTER(i32)] * 7 + [ctypes.POINTER(i64)]
+    lib.softmax_kernel_name.restype = ctypes.c_char_p
+    lib.softmax_kernel_name.argtypes = [i32]
+    lib.softmax_kernel_fits.restype = i32
+    lib.softmax_kernel_fits.argtypes = [i32, vp, vp, i64, i64, i32]
+    lib.softmax_status_string.restype = ctypes.c_char_p
+    lib.softmax_status_string.argtypes = [i32]
+    lib.softmax_version.restype = ctypes.c_char_p
+    lib.softmax_version.argtypes = []
+    lib.softmax_bench_copy.restype = i32
+    lib.softmax_bench_copy.argtypes = [vp, vp, i64, vp]
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    return _lib.softmax_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise SoftmaxError(status, where)
+
+
+def softmax_fwd(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int,
+                dtype: int, stream: int = 0) -> None:
+    """Raw entry point: device pointers as ints, the stream as an int handle."""
+    lib = _load()
+    _check(lib.softmax_fwd(in_ptr, out_ptr, rows, cols, row_stride, dtype, stream), "softmax_fwd")
+
+
+def softmax_fwd_kernel(kernel_id: int, in_ptr: int, out_ptr: int, rows: int, cols: int,
+                       row_stride: int, dtype: int, stream: int = 0) -> None:
+    """Raw entry point that forces one compiled kernel of the library's table."""
+    lib = _load()
+    _check(lib.softmax_fwd_kernel(kernel_id, in_ptr, out_ptr, rows, cols, row_stride, dtype, stream),
+           "softmax_fwd_kernel")
+
+
+def softmax_select(in_ptr: int, out_ptr: int, cols: int, row_stride: int, dtype: int,
+                   rows: int = 1) -> int:
+    """The kernel id the library's width dispatch picks for this call."""
+    lib = _load()
+    kid = ctypes.c_int(-1)
+    _check(lib.softmax_select(in_ptr, out_ptr, rows, cols, row_stride, dtype, ctypes.byref(kid)),
+           "softmax_select")
+    return kid.value
+
+
+def bench_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None:
+    """Plain 16-byte-vector device copy (the achievable-bandwidth reference)."""
+    lib = _load()
+    _check(lib.softmax_bench_copy(src_ptr, dst_ptr, nbytes, stream), "softmax_bench_copy")
+
+
+@dataclass(frozen=True)
+class KernelInfo:
+    kid: int
+    name: str
+    dtype: int
+    variant: str
+    vec_elems: int      # elements per load
+    lanes: int          # lanes per row (packed) or threads per row (row/online)
+    vecs_per_lane: int  # loads per lane per row (or per chunk, online)
+    groups: int         # row groups per wave (packed)
+    block: int          # threads per workgroup (packed: maximum)
+    max_cols: int       # widest row it handles (-1: any)
+
+
+def kernel_table() -> list[KernelInfo]:
+    lib = _load()
+    out = []
+    for kid in range(lib.softmax_num_kernels()):
+        ints = [ctypes.c_int() for _ in range(7)]
+        mc = ctypes.c_int64()
+        _check(lib.softmax_kernel_info(kid, *[ctypes.byref(v) for v in ints], ctypes.byref(mc)),
+               "softmax_kernel_info")
+        dt, var, ve, lanes, vpl, groups, block = (v.value for v in ints)
+        out.append(KernelInfo(kid, lib.softmax_kernel_name(kid).decode(), dt, VARIANT_NAMES[var],
+                              ve, lanes, vpl, groups, block, mc.value))
+    return out
+
+
+def kernel_fits(kid: int, in_ptr: int, out_ptr: int, cols: int, row_stride: int, dtype: int) -> bool:
+    return bool(_load().softmax_kernel_fits(kid, in_ptr, out_ptr, cols, row_stride, dtype))
+
+
+def version() -> str:
+    return _load().softmax_version().decode()
+
+
+# ---------------------------------------------------------------- torch layer
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"softmax: unsupported dtype {t.dtype} (fp32, fp16, bf16 only)")
+    return codes[t.dtype]
+
+
+def _as_rows(t):
+    if t.dim() < 1:
+        raise ValueError("softmax: input must have at least one dimension")
+    if t.dim() == 1:
+        return 1, t.shape[0], t.shape[0]
+    if t.stride(-1) != 1:
+        raise ValueError("softmax: the last dimension must be contiguous")
+    cols = t.shape[-1]
+    if t.dim() == 2:
+        return t.shape[0], cols, (t.stride(0) if t.shape[0] > 1 else cols)
+    if not t.is_contiguous():
+        raise ValueError("softmax: inputs of rank > 2 must be contiguous")
+    return t.numel() // max(cols, 1), cols, cols
+
+
+def softmax(x, out=None, kernel_id: int | None = None):
+    """Row softmax over the last dimension of a CUDA (HIP) tensor.
+
+    ``out`` (optional) must match ``x`` in shape, dtype and strides; it may be
+    ``x`` itself (in place).  The call is asynchronous on torch's current stream.
+    """
+    import torch
+    if not x.is_cuda:
+        raise ValueError("softmax: input must be a GPU tensor")
+    code = _torch_dtype_code(x)
+    rows, cols, stride = _as_rows(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or out.stride() != x.stride() or out.device != x.device:
+        raise ValueError("softmax: out must match the input's shape, dtype, strides and device")
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    if kernel_id is None:
+        softmax_fwd(x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
+    else:
+        softmax_fwd_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
+    return out

@@ -1,0 +1,230 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests re-types the oracle's formula: expected values come from
+50-digit decimal arithmetic, closed forms, numpy's own fp16 decoding, the
+bfloat16 definition (upper half of an IEEE binary32), or invariants of the
+softmax definition (rows sum to one, shift invariance, permutation
+equivariance, exact zeros at -inf).
+"""
+import decimal
+import math
+
+import numpy as np
+import pytest
+
+from row_wise_softmax_amd import workloads as W
+
+D = decimal.Decimal
+
+
+def _decimal_softmax(row):
+    """Softmax of a list of floats at 50 significant digits (decimal.exp)."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 50
+        finite = [D(float(v)) for v in row if math.isfinite(v)]
+        if not finite:
+            return [0.0] * len(row)
+        m = max(finite)
+        e = [(D(float(v)) - m).exp() if math.isfinite(v) else D(0) for v in row]
+        s = sum(e)
+        return [float(v / s) for v in e]
+
+
+def _decoded(x, dtype):
+    if dtype == "f32":
+        return x.astype(np.float64)
+    if dtype == "f16":
+        return x.view(np.float16).astype(np.float64)
+    return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------- decoding
+
+def test_decode_f16_every_bit_pattern(oracle_mod):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.decode(bits, "f16")
+    want = bits.view(np.float16).astype(np.float64)  # numpy's binary16 decoding
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_decode_bf16_every_bit_pattern(oracle_mod):
+    bits = np.arange(65536, dtype=np.uint32)
+    got = oracle_mod.decode(bits.astype(np.uint16), "bf16")
+    with np.errstate(invalid="ignore"):
+        want = (bits << np.uint32(16)).view(np.float32).astype(np.float64)  # bf16 = upper half of fp32
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+# -------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+def test_brute_force_against_50_digit_decimal(oracle_mod, dtype, n):
+    x = W.random_matrix(seed=11, rows=6, cols=n, dtype=dtype, sigma=4.0)
+    got = oracle_mod.softmax(x, dtype)
+    xd = _decoded(x, dtype)
+    for i in range(x.shape[0]):
+        want = np.array(_decimal_softmax(list(xd[i])))
+        assert np.allclose(got[i], want, rtol=2e-15, atol=0.0), (i, got[i], want)
+
+
+def test_rows_are_not_mixed_up(oracle_mod):
+    # A non-square matrix with very different rows: a transposed or shifted
+    # row index would give visibly different numbers.
+    x = np.array([[0.0, 1.0, 2.0, 3.0, 4.0],
+                  [4.0, 3.0, 2.0, 1.0, 0.0],
+                  [-20.0, 0.0, 20.0, -1.0, 1.5]], dtype=np.float32)
+    got = oracle_mod.softmax(x, "f32")
+    for i in range(3):
+        assert np.allclose(got[i], _decimal_softmax(list(x[i].astype(np.float64))), rtol=2e-15, atol=0)
+
+
+# ------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("weights", [[1, 2, 3], [1, 1, 2, 4], [5, 3, 2, 1, 7], [1, 1000]])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_log_weights_give_normalised_weights(oracle_mod, weights, dtype):
+    # x_j = ln a_j  =>  y_j = a_j / sum(a).  The input is ln a_j rounded to the
+    # element type, which perturbs y_j by at most 2 max_j |x_j - ln a_j| (relative).
+    a = np.array(weights, dtype=np.float64)
+    x = W.cast(np.log(a)[None, :], dtype)
+    dx = np.max(np.abs(_decoded(x, dtype)[0] - np.log(a)))
+    got = oracle_mod.softmax(x, dtype)[0]
+    want = a / a.sum()
+    assert np.allclose(got, want, rtol=2.2 * dx + 1e-15, atol=0.0)
+
+
+@pytest.mark.parametrize("n", [1, 7, 1000, 4096])
+@pytest.mark.parametrize("value", [0.5, -3.25, 88.0])
+def test_constant_row_gives_one_over_n(oracle_mod, n, value):
+    x = np.full((1, n), value, dtype=np.float32)
+    got = oracle_mod.softmax(x, "f32")[0]
+    want = 1.0 / n
+    assert np.all(np.abs(got - want) <= np.spacing(want))
+    if n == 1:
+        assert got[0] == 1.0
+
+
+def test_c1_constant_row_zero(oracle_mod):
+    x = W.WORKLOADS["c1"].generate()
+    got = oracle_mod.softmax(x, "f32")
+    assert np.all(np.abs(got[0] - 1e-3) <= np.spacing(1e-3))
+
+
+def test_two_large_entries_logistic(oracle_mod):
+    # exp(1000) overflows even in fp64: finite results prove the max is subtracted.
+    x = np.array([[1000.0, 999.0]], dtype=np.float32)
+    got = oracle_mod.softmax(x, "f32")[0]
+    want = _decimal_softmax([1000.0, 999.0])
+    assert np.all(np.isfinite(got))
+    assert np.allclose(got, want, rtol=2e-15, atol=0)
+
+
+def test_entry_100_does_not_overflow(oracle_mod):
+    x = W.WORKLOADS["c1"].generate()
+    got = oracle_mod.softmax(x, "f32")[1]
+    assert np.all(np.isfinite(got))
+    want = _decimal_softmax(list(x[1].astype(np.float64)))
+    assert np.allclose(got, want, rtol=2e-15, atol=1e-300)
+    assert got[-1] > 0.999999
+
+
+# ---------------------------------------------------------------- masking
+
+def test_neg_inf_positions_are_exact_positive_zero(oracle_mod):
+    x = W.WORKLOADS["c1"].generate()
+    got = oracle_mod.softmax(x, "f32")[2]
+    assert np.all(got[800:] == 0.0) and not np.any(np.signbit(got[800:]))
+    assert abs(got[:800].sum() - 1.0) <= 1e-14
+    want = _decimal_softmax(list(x[2, :800].astype(np.float64)))
+    assert np.allclose(got[:800], want, rtol=2e-15, atol=0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_all_neg_inf_row_gives_zeros(oracle_mod, dtype):
+    x = np.full((2, 9), W.neg_inf(dtype), dtype=W.storage_dtype(dtype))
+    got = oracle_mod.softmax(x, dtype)
+    assert np.all(got == 0.0) and not np.any(np.signbit(got))
+
+
+def test_causal_rows(oracle_mod):
+    x = W.WORKLOADS["c2"].generate(rows=64)
+    got = oracle_mod.softmax(x, "f32")
+    assert got[0, 0] == 1.0 and np.all(got[0, 1:] == 0.0)
+    for i in (1, 2, 63):
+        assert np.all(got[i, i + 1:] == 0.0)
+        want = _decimal_softmax(list(x[i, :i + 1].astype(np.float64)))
+        assert np.allclose(got[i, :i + 1], want, rtol=2e-15, atol=0)
+
+
+# -------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("key,rows", [("c1", 128), ("c2", 256), ("c3", 32), ("c4", 32),
+                                      ("c5_bf16_32", 512), ("c5_f32_3000", 16)])
+def test_rows_sum_to_one(oracle_mod, key, rows):
+    wl = W.WORKLOADS[key]
+    x = wl.generate(rows=rows)
+    got = oracle_mod.softmax(x, wl.dtype)
+    finite_rows = np.isfinite(_decoded(x, wl.dtype)).any(axis=1)
+    sums = got.sum(axis=1)
+    assert np.all(np.abs(sums[finite_rows] - 1.0) <= 1e-14)
+    assert np.all(got >= 0.0)
+
+
+@pytest.mark.parametrize("c", [-50.0, 3.0, 100.0])
+def test_shift_invariance(oracle_mod, c):
+    # Inputs on a 1/8 grid, so x + c is exact in fp32.
+    rng = np.random.default_rng(7)
+    x = (rng.integers(-64, 65, size=(4, 37)) / 8.0).astype(np.float32)
+    y0 = oracle_mod.softmax(x, "f32")
+    y1 = oracle_mod.softmax((x + np.float32(c)).astype(np.float32), "f32")
+    assert np.allclose(y0, y1, rtol=1e-15, atol=0)
+
+
+def test_permutation_equivariance(oracle_mod):
+    x = W.random_matrix(seed=3, rows=3, cols=257, dtype="f32", sigma=3.0)
+    perm = np.random.default_rng(5).permutation(257)
+    y = oracle_mod.softmax(x, "f32")
+    yp = oracle_mod.softmax(np.ascontiguousarray(x[:, perm]), "f32")
+    # Only the summation order changes: relative differences stay below n * 2^-53 (twice, for margin).
+    assert np.allclose(yp, y[:, perm], rtol=2 * 257 * 2.0**-53, atol=1e-300)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_row_stride_padding_is_ignored(oracle_mod, dtype):
+    x = W.random_matrix(seed=4, rows=5, cols=13, dtype=dtype, row_stride=24)  # NaN padding
+    dense = np.ascontiguousarray(x[:, :13])
+    assert np.array_equal(oracle_mod.softmax(x, dtype, cols=13), oracle_mod.softmax(dense, dtype))
+
+
+def test_bad_arguments_rejected(oracle_mod):
+    x = np.zeros((2, 4), dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle_mod.softmax(x, "f32", cols=5)  # row stride 4 < cols 5
+    empty = oracle_mod.softmax(np.zeros((0, 4), dtype=np.float32), "f32")
+    assert empty.shape == (0, 4)
+
+
+# ------------------------------------------------- figures printed on pages
+
+def test_page_traffic_and_flop_figures():
+    import json
+    import os
+    fig = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+    t = fig["fused_traffic_4096x4096_f32"]
+    assert t["rows"] * t["cols"] * W.elem_size(t["dtype"]) == t["tensor_bytes"]
+    assert W.algorithmic_bytes(t["rows"], t["cols"], t["dtype"]) == t["fused_bytes"]
+    assert 4 * W.algorithmic_bytes(t["rows"], t["cols"], t["dtype"]) == t["five_op_bytes"]
+    f = fig["flops_4096x4096"]
+    assert round(f["rows"] * f["cols"] * f["flop_per_element"] / 1e6) == f["mflop"]
+    h = fig["fused_traffic_8192x4096_f16"]
+    assert round(W.algorithmic_bytes(h["rows"], h["cols"], h["dtype"]) / 1e6, 1) == h["fused_megabytes_decimal"]
+    c = fig["copy_ceiling_example"]
+    gbps = W.algorithmic_bytes(c["rows"], c["cols"], c["dtype"]) / (c["fused_ms"] * 1e-3) / 1e9
+    assert abs(gbps - c["fused_gbps"]) / c["fused_gbps"] < 0.01
