@@ -1,0 +1,152 @@
+/*
+ * row_wise_softmax.h -- C ABI of the MI355X (gfx950) fused row-softmax library.
+ *
+ * The operation (every entry point that computes): for each row i of a
+ * row-major matrix x with `cols` columns,
+ *
+ *     y[i, j] = exp(x[i, j] - m_i) / sum_k exp(x[i, k] - m_i),   m_i = max_k x[i, k]
+ *
+ * -- the softmax with the row max subtracted first so that large entries
+ * cannot overflow ("I Wrote My First GPU Kernel", section "What Fusion
+ * Actually Does"; "fused-softmax-roofline", the row-softmax fragment), fused
+ * into one pass that reads each element once and writes it once (same two
+ * pages), with -inf entries contributing exactly 0 and receiving exactly +0
+ * ("GPU Kernels - Implementing and optimizing Softmax", section "Baseline &
+ * Triton Softmax kernel").  A row whose entries are all -inf gets all +0.
+ * Arithmetic is fp32 for every storage type; fp16 and bf16 outputs are rounded
+ * to nearest even.  +inf and NaN inputs are outside the contract.
+ *
+ * Layout: row i occupies elements [i * row_stride, i * row_stride + cols) of
+ * its buffer; `row_stride` counts ELEMENTS and is shared by input and output
+ * (the single stride of "Kernel Fusion", section "A fused softmax in Triton").
+ * Elements between `cols` and `row_stride` are never read or written.
+ *
+ * Ownership: the caller owns both device buffers.  The library allocates no
+ * device memory, keeps no pointer after returning, never synchronises the host
+ * and never pre-fills `out` (it writes every out[i, j < cols] exactly once;
+ * "I Wrote My First GPU Kernel", section "The Honest Part", on the cost of
+ * zero-filling an output the kernel overwrites anyway).
+ *
+ * Aliasing: in == out (exactly in place) is allowed; any other overlap of the
+ * two extents is rejected with SOFTMAX_ERR_OVERLAP.
+ *
+ * Asynchrony: computing calls enqueue work on `stream` (a hipStream_t passed
+ * as void*; NULL is the default stream) and return.  SOFTMAX_OK means the
+ * launch was accepted; a fault during execution surfaces as a HIP error at the
+ * caller's next synchronisation.  Calls are stateless and thread-safe, and
+ * make no allocation or memset, so they may be captured in a hipGraph.
+ *
+ * Errors: every entry point returns a status and never prints, throws or
+ * aborts.  Arguments are validated before any HIP call.  rows == 0 or
+ * cols == 0 returns SOFTMAX_OK without launching (pointers may then be NULL).
+ */
+#ifndef ROW_WISE_SOFTMAX_H
+#define ROW_WISE_SOFTMAX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage types (input and output share one). */
+#define SOFTMAX_F32 0
+#define SOFTMAX_F16 1
+#define SOFTMAX_BF16 2
+
+/* Status codes. */
+#define SOFTMAX_OK 0
+#define SOFTMAX_ERR_NULL_POINTER 1 /* rows * cols > 0 with a NULL buffer, or a NULL out-parameter */
+#define SOFTMAX_ERR_BAD_SHAPE 2    /* negative dims, row_stride < cols, cols > 2^30, or a byte extent past INT64_MAX */
+#define SOFTMAX_ERR_BAD_DTYPE 3    /* dtype not one of SOFTMAX_F32 / F16 / BF16 */
+#define SOFTMAX_ERR_OVERLAP 4      /* in and out overlap without being equal */
+#define SOFTMAX_ERR_BAD_KERNEL 5   /* forced kernel id unknown, of another dtype, or unable to take this width / alignment */
+#define SOFTMAX_ERR_HIP 6          /* the HIP runtime refused the launch */
+
+/* Kernel variants of the compiled table. */
+#define SOFTMAX_VARIANT_PACKED 0 /* L lanes of a wave per row, 64/L rows per wave (narrow rows) */
+#define SOFTMAX_VARIANT_ROW 1    /* one workgroup per row, row held in registers (single pass) */
+#define SOFTMAX_VARIANT_ONLINE 2 /* one workgroup per row, two reads + one write (any width) */
+
+/*
+ * softmax_fwd -- the fused row softmax, with the library's width dispatch.
+ *   in, out     device pointers to rows x row_stride elements of `dtype`
+ *               (the last row needs only `cols`); 16-byte-aligned pointers and
+ *               16-byte-multiple row pitches take the vector path, anything
+ *               else a scalar path of the same results.
+ *   rows, cols  matrix shape; the softmax runs along each row.
+ *   row_stride  elements between the starts of consecutive rows (>= cols).
+ *   dtype       SOFTMAX_F32, SOFTMAX_F16 or SOFTMAX_BF16.
+ *   stream      hipStream_t as void*.
+ * The width dispatch follows the pages' advice to pick the path by measured
+ * width crossovers ("fused-softmax-roofline", the closing discussion of
+ * where the fused kernel loses) and to tune block shape per width rather than
+ * by one formula ("GPU Kernels - Implementing and optimizing Softmax",
+ * sections "CUDA scaling threads" and "Autotuning").
+ */
+int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
+                int dtype, void *stream);
+
+/*
+ * softmax_fwd_kernel -- the same operation through one forced entry of the
+ * compiled kernel table (for width sweeps and tests).  Same arguments and
+ * errors as softmax_fwd, plus SOFTMAX_ERR_BAD_KERNEL when `kernel_id` is out of
+ * range, is compiled for another dtype, or cannot take this width, stride or
+ * pointer alignment (see softmax_kernel_fits).
+ */
+int softmax_fwd_kernel(int kernel_id, const void *in, void *out, int64_t rows, int64_t cols,
+                       int64_t row_stride, int dtype, void *stream);
+
+/*
+ * softmax_select -- the kernel id softmax_fwd would launch for these
+ * arguments, written to *kernel_id.  Validates like softmax_fwd (rows only
+ * matters for validation and launch shape); launches nothing.
+ */
+int softmax_select(const void *in, const void *out, int64_t rows, int64_t cols, int64_t row_stride,
+                   int dtype, int *kernel_id);
+
+/* Number of entries in the compiled kernel table (ids 0 .. n-1). */
+int softmax_num_kernels(void);
+
+/*
+ * softmax_kernel_info -- the parameters of table entry `kernel_id`:
+ *   dtype, variant (SOFTMAX_VARIANT_*), vec_elems (elements per memory access),
+ *   lanes (packed: lanes per row; row/online: threads per row),
+ *   vecs_per_lane (accesses per lane per row, or per chunk for online),
+ *   groups (packed: row groups per wave in flight; else 1),
+ *   block (threads per workgroup; packed: the maximum), and
+ *   max_cols (widest row it takes; -1 for any).
+ * Any out-pointer may be NULL.  Returns SOFTMAX_ERR_BAD_KERNEL for an unknown id.
+ */
+int softmax_kernel_info(int kernel_id, int *dtype, int *variant, int *vec_elems, int *lanes,
+                        int *vecs_per_lane, int *groups, int *block, int64_t *max_cols);
+
+/* Static, human-readable name of table entry `kernel_id` (NULL if unknown). */
+const char *softmax_kernel_name(int kernel_id);
+
+/* 1 if table entry `kernel_id` can run these arguments, else 0.  Launches nothing. */
+int softmax_kernel_fits(int kernel_id, const void *in, const void *out, int64_t cols,
+                        int64_t row_stride, int dtype);
+
+/* Static description of a status code. */
+const char *softmax_status_string(int status);
+
+/* Static version string of the library. */
+const char *softmax_version(void);
+
+/*
+ * softmax_bench_copy -- a plain device copy of `bytes` bytes with 16-byte
+ * accesses (src and dst 16-byte aligned, bytes a multiple of 16, no overlap).
+ * It is the achievable read-once/write-once bandwidth a finished softmax is
+ * measured against ("Kernel Fusion", section "What interviewers are listening
+ * for": a fused kernel running at device-copy bandwidth is done).
+ * Errors: NULL_POINTER, BAD_SHAPE (negative, or not a multiple of 16, or
+ * misaligned), OVERLAP, HIP.
+ */
+int softmax_bench_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROW_WISE_SOFTMAX_H */

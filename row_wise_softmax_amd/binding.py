@@ -39,6 +39,11 @@ def _load():
     if _lib is not None:
         return _lib
     path = library_path()
+    # torch ships its own HIP runtime under the same soname as ROCm's.  Load
+    # it first so this library binds to that one runtime: loaded the other way
+    # round, a process holds two HIP runtimes and torch's streams are invalid
+    # handles to ours.
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise RuntimeError(
             f"row_wise_softmax_amd: HIP library not built ({path} missing); "

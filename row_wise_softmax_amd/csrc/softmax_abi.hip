@@ -1,0 +1,294 @@
+// softmax_abi.hip -- the C ABI of include/row_wise_softmax.h: argument
+// validation, the width dispatch and the launches.
+//
+// Dispatch by width, following the pages' two lessons on shapes: a fused
+// kernel that gives each row a whole program wastes the machine on narrow rows
+// (launch and scheduling costs dominate, "fused-softmax-roofline", the
+// discussion of shapes where it loses), and a fixed block size starves wide
+// rows of loads in flight ("GPU Kernels - Implementing and optimizing
+// Softmax", sections "Results for this specific kernel" and "CUDA scaling
+// threads").  So narrow rows share a wave (packed), mid-size rows get a wave
+// or a workgroup that holds the row in registers (row), and rows past the
+// register budget stream twice (online).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kernel_table.hpp"
+#include "row_wise_softmax.h"
+#include "softmax_kernels.hpp"
+
+namespace {
+
+using rws::Entry;
+
+constexpr int64_t kMaxGrid = int64_t(1) << 20;  // workgroups per launch; kernels loop past it
+constexpr int64_t kMaxCols = int64_t(1) << 30;  // keeps every in-row index, chunk offset included, in int
+
+int elem_bytes(int dtype) { return dtype == SOFTMAX_F32 ? 4 : 2; }
+
+const Entry* table_of(int dtype, int* n) {
+    switch (dtype) {
+        case SOFTMAX_F32: *n = rws::kTableF32Size; return rws::kTableF32;
+        case SOFTMAX_F16: *n = rws::kTableF16Size; return rws::kTableF16;
+        case SOFTMAX_BF16: *n = rws::kTableBF16Size; return rws::kTableBF16;
+        default: *n = 0; return nullptr;
+    }
+}
+
+int total_kernels() { return rws::kTableF32Size + rws::kTableF16Size + rws::kTableBF16Size; }
+
+// Global kernel id -> entry (ids run over the f32, f16 and bf16 tables in order).
+const Entry* entry_by_id(int id) {
+    if (id < 0) return nullptr;
+    if (id < rws::kTableF32Size) return &rws::kTableF32[id];
+    id -= rws::kTableF32Size;
+    if (id < rws::kTableF16Size) return &rws::kTableF16[id];
+    id -= rws::kTableF16Size;
+    if (id < rws::kTableBF16Size) return &rws::kTableBF16[id];
+    return nullptr;
+}
+
+int id_of(const Entry* e) {
+    int base = 0;
+    for (int dt = SOFTMAX_F32; dt <= SOFTMAX_BF16; ++dt) {
+        int n;
+        const Entry* t = table_of(dt, &n);
+        if (e >= t && e < t + n) return base + int(e - t);
+        base += n;
+    }
+    return -1;
+}
+
+// Widest row an entry holds: lanes (or threads) x accesses each x elements per access.
+int64_t max_cols_of(const Entry& e) {
+    if (e.variant == SOFTMAX_VARIANT_ONLINE) return -1;
+    return int64_t(e.lanes) * e.vpl * e.vec;
+}
+
+bool fits(const Entry& e, const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype) {
+    if (e.dtype != dtype) return false;
+    if (e.vec > 1) {
+        const uintptr_t acc = uintptr_t(e.vec) * elem_bytes(dtype);
+        if (uintptr_t(in) % acc || uintptr_t(out) % acc) return false;
+        if ((uint64_t(row_stride) * elem_bytes(dtype)) % acc) return false;
+        if (cols % e.vec) return false;
+    }
+    const int64_t mc = max_cols_of(e);
+    return mc < 0 || cols <= mc;
+}
+
+const Entry* find(int dtype, int variant, int vec, int lanes, int vpl, int groups) {
+    int n;
+    const Entry* t = table_of(dtype, &n);
+    for (int i = 0; i < n; ++i) {
+        const Entry& e = t[i];
+        if (e.variant == variant && e.vec == vec && e.lanes == lanes && e.vpl == vpl && e.groups == groups)
+            return &e;
+    }
+    return nullptr;
+}
+
+// 16-byte accesses need 16-byte-aligned pointers, a 16-byte-multiple row
+// pitch and a width that is a whole number of accesses.
+bool aligned16(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype) {
+    const int64_t esz = elem_bytes(dtype);
+    return uintptr_t(in) % 16 == 0 && uintptr_t(out) % 16 == 0 && (row_stride * esz) % 16 == 0 &&
+           (cols * esz) % 16 == 0;
+}
+
+int pow2_at_least(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// The width dispatch rule.  `nacc` is the row length in 16-byte accesses.
+const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype) {
+    const int vec16 = 16 / elem_bytes(dtype);
+    if (aligned16(in, out, cols, row_stride, dtype)) {
+        const int64_t nacc = cols / vec16;
+        const Entry* e = nullptr;
+        if (nacc <= 32) {
+            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, pow2_at_least(nacc), 1, 4);
+        } else if (nacc <= 64 * 16) {
+            const int v = pow2_at_least((nacc + 63) / 64);
+            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, 64, v, 1);
+        } else {
+            // Register-resident if some workgroup shape of the table holds the row
+            // at 4 or more accesses per thread; else stream it twice.
+            for (int v = 4; v <= 16 && e == nullptr; v *= 2) {
+                const int w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
+                if (w <= 16) e = find(dtype, SOFTMAX_VARIANT_ROW, vec16, 64 * w, v, 1);
+            }
+            if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, vec16, 64 * 16, 4, 1);
+        }
+        if (e && fits(*e, in, out, cols, row_stride, dtype)) return e;
+    }
+    // Any alignment: scalar accesses, streamed twice.
+    const int w = cols <= 64 * 8 ? 1 : (cols <= 4 * 64 * 8 * 4 ? 4 : 16);
+    return find(dtype, SOFTMAX_VARIANT_ONLINE, 1, 64 * w, 8, 1);
+}
+
+// Shared validation.  Returns SOFTMAX_OK, or an error; *empty is set when
+// there is nothing to launch.
+int validate(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+             bool* empty) {
+    *empty = false;
+    if (dtype != SOFTMAX_F32 && dtype != SOFTMAX_F16 && dtype != SOFTMAX_BF16) return SOFTMAX_ERR_BAD_DTYPE;
+    if (rows < 0 || cols < 0) return SOFTMAX_ERR_BAD_SHAPE;
+    if (rows == 0 || cols == 0) {
+        *empty = true;
+        return SOFTMAX_OK;
+    }
+    if (in == nullptr || out == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    if (row_stride < cols) return SOFTMAX_ERR_BAD_SHAPE;
+    if (cols > kMaxCols) return SOFTMAX_ERR_BAD_SHAPE;
+    const int64_t esz = elem_bytes(dtype);
+    // extent = ((rows - 1) * row_stride + cols) * esz must fit in int64.
+    if (rows - 1 > (INT64_MAX / esz - cols) / row_stride) return SOFTMAX_ERR_BAD_SHAPE;
+    const int64_t extent = ((rows - 1) * row_stride + cols) * esz;
+    if (in != out) {
+        const uintptr_t a = uintptr_t(in), b = uintptr_t(out);
+        if (a < b + uint64_t(extent) && b < a + uint64_t(extent)) return SOFTMAX_ERR_OVERLAP;
+    }
+    return SOFTMAX_OK;
+}
+
+int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
+           hipStream_t stream) {
+    rws::Args a;
+    a.in = in;
+    a.out = out;
+    a.rows = rows;
+    a.stride = row_stride / e.vec;
+    a.nacc = int(cols / e.vec);
+    int block;
+    if (e.variant == SOFTMAX_VARIANT_PACKED) {
+        const int64_t rows_per_wave = int64_t(64 / e.lanes) * e.groups;
+        const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+        int wpb = e.block / 64;
+        while (wpb > 1 && (waves + wpb - 1) / wpb < 1024) wpb /= 2;  // small jobs: more, smaller workgroups
+        block = wpb * 64;
+        a.nblocks = (waves + wpb - 1) / wpb;
+    } else {
+        block = e.block;
+        a.nblocks = rows;
+    }
+    const int64_t grid = a.nblocks < kMaxGrid ? a.nblocks : kMaxGrid;
+    void* args[] = {&a};
+    hipError_t rc = hipLaunchKernel(e.fn, dim3(unsigned(grid)), dim3(unsigned(block)), args, 0, stream);
+    if (rc != hipSuccess) {
+        (void)hipGetLastError();  // do not leave our failure for the caller's next check
+        return SOFTMAX_ERR_HIP;
+    }
+    return SOFTMAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK || empty) return st;
+    const Entry* e = select_entry(in, out, cols, row_stride, dtype);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    return launch(*e, in, out, rows, cols, row_stride, static_cast<hipStream_t>(stream));
+}
+
+int softmax_fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols,
+                       int64_t row_stride, int dtype, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    const Entry* e = entry_by_id(kernel_id);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    if (empty) return e->dtype == dtype ? SOFTMAX_OK : SOFTMAX_ERR_BAD_KERNEL;
+    if (!fits(*e, in, out, cols, row_stride, dtype)) return SOFTMAX_ERR_BAD_KERNEL;
+    return launch(*e, in, out, rows, cols, row_stride, static_cast<hipStream_t>(stream));
+}
+
+int softmax_select(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                   int* kernel_id) {
+    if (kernel_id == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    const Entry* e = select_entry(in, out, cols > 0 ? cols : 1, row_stride > 0 ? row_stride : 1, dtype);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    *kernel_id = id_of(e);
+    return SOFTMAX_OK;
+}
+
+int softmax_num_kernels(void) { return total_kernels(); }
+
+int softmax_kernel_info(int kernel_id, int* dtype, int* variant, int* vec_elems, int* lanes, int* vecs_per_lane,
+                        int* groups, int* block, int64_t* max_cols) {
+    const Entry* e = entry_by_id(kernel_id);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    if (dtype) *dtype = e->dtype;
+    if (variant) *variant = e->variant;
+    if (vec_elems) *vec_elems = e->vec;
+    if (lanes) *lanes = e->lanes;
+    if (vecs_per_lane) *vecs_per_lane = e->vpl;
+    if (groups) *groups = e->groups;
+    if (block) *block = e->block;
+    if (max_cols) *max_cols = max_cols_of(*e);
+    return SOFTMAX_OK;
+}
+
+const char* softmax_kernel_name(int kernel_id) {
+    const Entry* e = entry_by_id(kernel_id);
+    return e ? e->name : nullptr;
+}
+
+int softmax_kernel_fits(int kernel_id, const void* in, const void* out, int64_t cols, int64_t row_stride,
+                        int dtype) {
+    const Entry* e = entry_by_id(kernel_id);
+    if (e == nullptr || cols < 0 || row_stride < cols || cols > kMaxCols) return 0;
+    return fits(*e, in, out, cols, row_stride, dtype) ? 1 : 0;
+}
+
+const char* softmax_status_string(int status) {
+    switch (status) {
+        case SOFTMAX_OK: return "ok";
+        case SOFTMAX_ERR_NULL_POINTER: return "null pointer";
+        case SOFTMAX_ERR_BAD_SHAPE: return "bad shape (negative dims, row_stride < cols, cols > 2^30 or extent overflow)";
+        case SOFTMAX_ERR_BAD_DTYPE: return "bad dtype (expected 0 = fp32, 1 = fp16, 2 = bf16)";
+        case SOFTMAX_ERR_OVERLAP: return "input and output overlap without being equal";
+        case SOFTMAX_ERR_BAD_KERNEL: return "kernel id unknown or unable to take this dtype, width, stride or alignment";
+        case SOFTMAX_ERR_HIP: return "HIP runtime refused the launch";
+        default: return "unknown status";
+    }
+}
+
+const char* softmax_version(void) { return "row_wise_softmax_amd 0.1.0 (gfx950)"; }
+
+int softmax_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16) return SOFTMAX_ERR_BAD_SHAPE;
+    if (bytes == 0) return SOFTMAX_OK;
+    if (src == nullptr || dst == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    if (uintptr_t(src) % 16 || uintptr_t(dst) % 16) return SOFTMAX_ERR_BAD_SHAPE;
+    const uintptr_t a = uintptr_t(src), b = uintptr_t(dst);
+    if (a < b + uint64_t(bytes) && b < a + uint64_t(bytes)) return SOFTMAX_ERR_OVERLAP;
+    constexpr int kU = 4;
+    const int64_t n = bytes / 16;
+    int64_t grid = (n + 256 * kU - 1) / (256 * kU);
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    const rws::u32x4* s = static_cast<const rws::u32x4*>(src);
+    rws::u32x4* d = static_cast<rws::u32x4*>(dst);
+    void* args[] = {&s, &d, const_cast<int64_t*>(&n)};
+    hipError_t rc = hipLaunchKernel((const void*)&rws::copy16<kU>, dim3(unsigned(grid)), dim3(256), args, 0,
+                                    static_cast<hipStream_t>(stream));
+    if (rc != hipSuccess) {
+        (void)hipGetLastError();
+        return SOFTMAX_ERR_HIP;
+    }
+    return SOFTMAX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,514 @@
+// softmax_kernels.hpp -- HIP kernels (gfx950 / CDNA4) for the fused, numerically
+// stable row softmax  y[i,j] = exp(x[i,j] - m_i) / sum_k exp(x[i,k] - m_i),
+// m_i = max_k x[i,k], with fp32 accumulation for fp32, fp16 and bf16 data.
+//
+// The method: fuse max, exp, sum and normalise into one kernel so that each
+// element crosses HBM once in and once out ("I Wrote My First GPU Kernel",
+// section "What Fusion Actually Does"; "fused-softmax-roofline", the
+// row-softmax fragment), subtract the row max first, let masked columns carry
+// -inf so they contribute exactly 0 ("GPU Kernels - Implementing and
+// optimizing Softmax", section "Baseline & Triton Softmax kernel"), take one
+// reciprocal of the sum per row instead of dividing per element (same page,
+// section "CUDA optimized for block per row"), and for rows too wide to keep on
+// chip use the running-max/rescaled-sum form and its pairwise merge
+// ("Dissecting Memory Bandwidth & SRAM Tiling in Triton", section "The
+// Mathematical Remedy: Online Softmax Tiling").
+//
+// Three kernel shapes, all built on 16-byte coalesced accesses and wave64
+// cross-lane reductions (DPP, ds_swizzle, readlane), with no MFMA (there is
+// no contraction here):
+//   * packed  -- L lanes of one wave per row (L = 1..64), 64/L rows per wave,
+//                G row groups per wave in flight; no LDS, no barrier;
+//   * row     -- one workgroup of W waves per row, the row held in registers,
+//                one LDS slot per wave for the cross-wave combine;
+//   * online  -- one workgroup per row of any width: pass 1 streams the row in
+//                chunks keeping a per-lane (max, sum) pair, pass 2 re-reads,
+//                normalises and writes.
+//
+// Arithmetic (all fp32).  In the single-pass kernels the exponentials are
+// 2^(x*log2(e) - a) with one FMA and v_exp_f32, where a = m * log2(e) rounded
+// to fp32 is the row's "frame".  Every exponential of a row uses the same
+// frame, so the rounding of a cancels in the ratio; only the FMA's own
+// rounding of each argument remains.  A row whose entries are all -inf gets
+// frame 0, so every exponential is exp2(-inf) = +0, the sum is 0, the
+// reciprocal is taken as 0 and every output is +0.  The reciprocal of the sum
+// is v_rcp_f32 (about 1 ulp; the sum is at least 1 whenever the row has a
+// finite max, since the max itself contributes 1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rws {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ element types
+
+struct F32 { static constexpr int kBytes = 4; };
+struct F16 { static constexpr int kBytes = 2; };
+struct BF16 { static constexpr int kBytes = 2; };
+
+// One memory access of N elements (N * kBytes in {2, 4, 8, 16} bytes).
+template <int Bytes> struct RawOf;
+template <> struct RawOf<16> { typedef u32x4 type; };
+template <> struct RawOf<8> { typedef u32x2 type; };
+template <> struct RawOf<4> { typedef unsigned type; };
+template <> struct RawOf<2> { typedef unsigned short type; };
+
+template <class E, int N>
+struct Access {
+    static constexpr int kN = N;
+    typedef typename RawOf<N * E::kBytes>::type raw;
+};
+
+// Widen one dword holding one fp32 or two 16-bit values.
+__device__ inline float u32_as_f32(unsigned d) { return __builtin_bit_cast(float, d); }
+
+template <class E> __device__ inline void widen_dword(unsigned d, float* f);
+template <> __device__ inline void widen_dword<F32>(unsigned d, float* f) { f[0] = u32_as_f32(d); }
+template <> __device__ inline void widen_dword<F16>(unsigned d, float* f) {
+    f[0] = (float)__builtin_bit_cast(_Float16, (unsigned short)(d & 0xffffu));
+    f[1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(d >> 16));
+}
+template <> __device__ inline void widen_dword<BF16>(unsigned d, float* f) {
+    f[0] = u32_as_f32(d << 16);           // bf16 is the upper half of an fp32
+    f[1] = u32_as_f32(d & 0xffff0000u);
+}
+
+// Narrow fp32 -> one dword, rounding to nearest even (v_cvt_pk_*_f32 on gfx950).
+template <class E> __device__ inline unsigned narrow_dword(const float* f);
+template <> __device__ inline unsigned narrow_dword<F32>(const float* f) { return __builtin_bit_cast(unsigned, f[0]); }
+template <> __device__ inline unsigned narrow_dword<F16>(const float* f) {
+    f32x2 v = {f[0], f[1]};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, h16x2));
+}
+template <> __device__ inline unsigned narrow_dword<BF16>(const float* f) {
+    f32x2 v = {f[0], f[1]};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, b16x2));
+}
+
+template <class E> __device__ inline float widen_half(unsigned short h);
+template <> __device__ inline float widen_half<F16>(unsigned short h) { return (float)__builtin_bit_cast(_Float16, h); }
+template <> __device__ inline float widen_half<BF16>(unsigned short h) { return u32_as_f32((unsigned)h << 16); }
+template <class E> __device__ inline unsigned short narrow_half(float f);
+template <> __device__ inline unsigned short narrow_half<F16>(float f) { return __builtin_bit_cast(unsigned short, (_Float16)f); }
+template <> __device__ inline unsigned short narrow_half<BF16>(float f) { return __builtin_bit_cast(unsigned short, (__bf16)f); }
+
+// Load / store N elements at p (an address aligned to the access size).
+template <class E, int N>
+__device__ inline void load_elems(const typename Access<E, N>::raw* p, float* f) {
+    constexpr int kBytes = N * E::kBytes;
+    if constexpr (kBytes == 16) {
+        u32x4 r = *p;
+        constexpr int per = 4 / E::kBytes;
+        widen_dword<E>(r.x, f); widen_dword<E>(r.y, f + per);
+        widen_dword<E>(r.z, f + 2 * per); widen_dword<E>(r.w, f + 3 * per);
+    } else if constexpr (kBytes == 8) {
+        u32x2 r = *p;
+        constexpr int per = 4 / E::kBytes;
+        widen_dword<E>(r.x, f); widen_dword<E>(r.y, f + per);
+    } else if constexpr (kBytes == 4) {
+        widen_dword<E>(*p, f);
+    } else {
+        f[0] = widen_half<E>(*p);
+    }
+}
+
+template <class E, int N>
+__device__ inline void store_elems(typename Access<E, N>::raw* p, const float* f) {
+    constexpr int kBytes = N * E::kBytes;
+    if constexpr (kBytes == 16) {
+        constexpr int per = 4 / E::kBytes;
+        u32x4 r = {narrow_dword<E>(f), narrow_dword<E>(f + per), narrow_dword<E>(f + 2 * per),
+                   narrow_dword<E>(f + 3 * per)};
+        *p = r;
+    } else if constexpr (kBytes == 8) {
+        constexpr int per = 4 / E::kBytes;
+        u32x2 r = {narrow_dword<E>(f), narrow_dword<E>(f + per)};
+        *p = r;
+    } else if constexpr (kBytes == 4) {
+        *p = narrow_dword<E>(f);
+    } else {
+        *p = narrow_half<E>(f[0]);
+    }
+}
+
+// ------------------------------------------------------- cross-lane steps
+
+__device__ inline float as_f(int v) { return __builtin_bit_cast(float, v); }
+__device__ inline int as_i(float v) { return __builtin_bit_cast(int, v); }
+
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2] and [2,3,0,1] swap
+// neighbours at distance 1 and 2; row_half_mirror reverses each 8-lane half
+// row, row_mirror each 16-lane row.  Once every group of 2^k lanes holds one
+// value, a mirror pairs each lane with a lane of the sibling group, which is
+// all an all-reduce needs.
+template <int Ctrl>
+__device__ inline float dpp(float v) {
+    return as_f(__builtin_amdgcn_update_dpp(0, as_i(v), Ctrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// ds_swizzle in bit mode with and_mask 0x1f, xor_mask 0x10: partner = lane ^ 16.
+__device__ inline float swap16(float v) { return as_f(__builtin_amdgcn_ds_swizzle(as_i(v), 0x401F)); }
+
+struct OpMax { __device__ static float apply(float a, float b) { return fmaxf(a, b); } };
+struct OpSum { __device__ static float apply(float a, float b) { return a + b; } };
+
+// All-reduce over each aligned group of L consecutive lanes (L a power of two
+// <= 64).  Every lane of a group ends with the same bits: each step combines a
+// lane with a partner holding the same partial, and both operations commute.
+template <int L, class Op>
+__device__ inline float group_reduce(float v) {
+    if constexpr (L >= 2) v = Op::apply(v, dpp<kDppXor1>(v));
+    if constexpr (L >= 4) v = Op::apply(v, dpp<kDppXor2>(v));
+    if constexpr (L >= 8) v = Op::apply(v, dpp<kDppHalfMirror>(v));
+    if constexpr (L >= 16) v = Op::apply(v, dpp<kDppMirror>(v));
+    if constexpr (L >= 32) v = Op::apply(v, swap16(v));
+    if constexpr (L >= 64) {
+        float lo = as_f(__builtin_amdgcn_readlane(as_i(v), 0));
+        float hi = as_f(__builtin_amdgcn_readlane(as_i(v), 32));
+        v = Op::apply(lo, hi);
+    }
+    return v;
+}
+
+// Merge of two (max, sum) pairs, each sum taken relative to its own max:
+//   m = max(m1, m2),  s = s1 * e^(m1 - m) + s2 * e^(m2 - m);
+// a max of -inf marks an empty pair (sum 0).
+__device__ inline float exp_diff(float d) { return __builtin_amdgcn_exp2f(d * kLog2e); }
+
+__device__ inline void merge_pair(float& m, float& s, float m2, float s2) {
+    float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;  // both empty
+    s = s * exp_diff(m - mn) + s2 * exp_diff(m2 - mn);
+    m = mn;
+}
+
+template <int Ctrl>
+__device__ inline void pair_step_dpp(float& m, float& s) {
+    merge_pair(m, s, dpp<Ctrl>(m), dpp<Ctrl>(s));
+}
+
+// All-reduce of (max, sum) pairs over a whole wave.
+__device__ inline void wave_reduce_pair(float& m, float& s) {
+    pair_step_dpp<kDppXor1>(m, s);
+    pair_step_dpp<kDppXor2>(m, s);
+    pair_step_dpp<kDppHalfMirror>(m, s);
+    pair_step_dpp<kDppMirror>(m, s);
+    merge_pair(m, s, swap16(m), swap16(s));
+    float m_lo = as_f(__builtin_amdgcn_readlane(as_i(m), 0));
+    float s_lo = as_f(__builtin_amdgcn_readlane(as_i(s), 0));
+    float m_hi = as_f(__builtin_amdgcn_readlane(as_i(m), 32));
+    float s_hi = as_f(__builtin_amdgcn_readlane(as_i(s), 32));
+    merge_pair(m_lo, s_lo, m_hi, s_hi);
+    m = m_lo;
+    s = s_lo;
+}
+
+// The row's frame from its max: m * log2 e, or 0 for an all -inf row.
+__device__ inline float frame_of(float m) { return m == -INFINITY ? 0.0f : m * kLog2e; }
+
+// The one-FMA form needs m * log2 e finite in fp32, i.e. |m| below about
+// 2.36e38 (reachable in fp32 and bf16 only).
+__device__ inline bool frame_fits(float m) { return fabsf(m) <= 2.0e38f || m == -INFINITY; }
+
+__device__ inline float exp_in_frame(float x, float frame) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -frame));
+}
+
+// A row whose max m has |m| > 2e38: every other fp32 value of the row is at
+// least ulp(2e38) = 2^104 below m, so its exponential is exactly 0 in fp32 and
+// the softmax is 1/count on the entries equal to m.  Rewriting the row as
+// 0 where x == m and -inf elsewhere (m := 0) gives exactly that through the
+// ordinary path.  The test is a ballot, so common rows pay one scalar branch.
+template <int n>
+__device__ inline void tame_huge_max(float* x, float& m) {
+    if (__builtin_amdgcn_ballot_w64(!frame_fits(m)) != 0) {
+        if (!frame_fits(m)) {
+#pragma unroll
+            for (int i = 0; i < n; ++i) x[i] = x[i] == m ? 0.0f : -INFINITY;
+            m = 0.0f;
+        }
+    }
+}
+
+// Replace x[0..n) by its exponentials relative to the row max m (|m| <= 2e38
+// or -inf); returns their sum.
+template <int n>
+__device__ inline float exp_and_sum(float* x, float m) {
+    const float fr = frame_of(m);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        x[i] = exp_in_frame(x[i], fr);
+        s += x[i];
+    }
+    return s;
+}
+
+// 1 / s for s >= 1 (a row with a finite max always has s >= 1), 0 for s == 0.
+__device__ inline float recip_sum(float s) { return s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f; }
+
+// ---------------------------------------------------------------- arguments
+
+struct Args {
+    const void* in;
+    void* out;
+    int64_t rows;
+    int64_t stride;   // row stride in accesses (elements / access width)
+    int64_t nblocks;  // logical workgroups; the grid may be smaller and loop
+    int nacc;         // accesses per row (cols / access width)
+};
+
+// ------------------------------------------------------------ packed kernel
+//
+// Lane l of a group of L lanes owns accesses l, l + L, l + 2L, ... of its row,
+// so one load instruction of a wave reads 64 consecutive 16-byte chunks: the
+// rows of a group are adjacent when the row stride equals the width.
+template <class E, int N, int L, int V, int G>
+__global__ void __launch_bounds__(256) softmax_packed(Args a) {
+    typedef typename Access<E, N>::raw raw;
+    constexpr int kRowsPerGroup = kWave / L;
+    constexpr int kRowsPerWave = kRowsPerGroup * G;
+    const raw* in = static_cast<const raw*>(a.in);
+    raw* out = static_cast<raw*>(a.out);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int waves = blockDim.x / kWave;
+    const int sub = lane / L;
+    const int l = lane % L;
+
+    for (int64_t b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+        const int64_t row0 = (b * waves + wave) * kRowsPerWave + sub;
+        float x[G][V][N];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t row = row0 + g * kRowsPerGroup;
+            const raw* p = in + row * a.stride + l;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (row < a.rows && v * L + l < a.nacc) {
+                    load_elems<E, N>(p + v * L, x[g][v]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < N; ++e) x[g][v][e] = -INFINITY;
+                }
+            }
+        }
+        float mx[G], r[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float m = x[g][0][0];
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int e = 0; e < N; ++e) m = fmaxf(m, x[g][v][e]);
+            mx[g] = group_reduce<L, OpMax>(m);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            tame_huge_max<V * N>(&x[g][0][0], mx[g]);
+            const float s = exp_and_sum<V * N>(&x[g][0][0], mx[g]);
+            r[g] = recip_sum(group_reduce<L, OpSum>(s));
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t row = row0 + g * kRowsPerGroup;
+            raw* p = out + row * a.stride + l;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (row < a.rows && v * L + l < a.nacc) {
+#pragma unroll
+                    for (int e = 0; e < N; ++e) x[g][v][e] *= r[g];
+                    store_elems<E, N>(p + v * L, x[g][v]);
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------- row kernel
+//
+// One workgroup of W waves per row; thread t owns accesses t, t + 64W, ...
+// The row stays in registers between the max, the exponentials and the
+// store.  Two barriers per row: after the per-wave maxima reach LDS and after
+// the per-wave sums do (separate slots, so no third barrier guards reuse).
+template <class E, int N, int W, int V>
+__global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
+    typedef typename Access<E, N>::raw raw;
+    constexpr int kThreads = W * kWave;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const raw* in = static_cast<const raw*>(a.in);
+    raw* out = static_cast<raw*>(a.out);
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const raw* p = in + row * a.stride + t;
+        float x[V][N];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (v * kThreads + t < a.nacc) {
+                load_elems<E, N>(p + v * kThreads, x[v]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) x[v][e] = -INFINITY;
+            }
+        }
+        float m = x[0][0];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int e = 0; e < N; ++e) m = fmaxf(m, x[v][e]);
+        m = group_reduce<kWave, OpMax>(m);
+        if (lane == 0) red_max[wave] = m;
+        __syncthreads();
+        m = red_max[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) m = fmaxf(m, red_max[w]);
+
+        tame_huge_max<V * N>(&x[0][0], m);
+        float s = exp_and_sum<V * N>(&x[0][0], m);
+        s = group_reduce<kWave, OpSum>(s);
+        if (lane == 0) red_sum[wave] = s;
+        __syncthreads();
+        s = red_sum[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) s += red_sum[w];
+        const float r = recip_sum(s);
+
+        raw* q = out + row * a.stride + t;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (v * kThreads + t < a.nacc) {
+#pragma unroll
+                for (int e = 0; e < N; ++e) x[v][e] *= r;
+                store_elems<E, N>(q + v * kThreads, x[v]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ online kernel
+//
+// One workgroup of W waves per row of any width.  Pass 1 walks the row in
+// chunks of V accesses per thread; per chunk each lane takes the chunk max,
+// rescales its running sum to the new max once (not once per element), and
+// adds the chunk's exponentials.  The per-lane (max, sum) pairs are merged
+// across the wave and then across waves through LDS.  Pass 2 re-reads the
+// row and writes e^(x - m) / sum.  Traffic: two reads and one write per
+// element (the second read may hit L2 or the Infinity Cache).
+//
+// Exponentials here are 2^((x - m) log2 e), two operations: each lane's sum is
+// relative to that lane's own max, and the subtraction keeps the terms of
+// different lanes and both passes consistent without a shared frame.
+template <class E, int N, int W, int V>
+__global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
+    typedef typename Access<E, N>::raw raw;
+    constexpr int kThreads = W * kWave;
+    constexpr int kChunk = kThreads * V;
+    __shared__ float red_m[W];
+    __shared__ float red_s[W];
+    const raw* in = static_cast<const raw*>(a.in);
+    raw* out = static_cast<raw*>(a.out);
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const raw* p = in + row * a.stride + t;
+        float lm = -INFINITY;  // lane running max; -inf: nothing finite seen yet
+        float ls = 0.0f;       // lane sum of e^(x - lm)
+        for (int c = 0; c < a.nacc; c += kChunk) {
+            float x[V][N];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (c + v * kThreads + t < a.nacc) {
+                    load_elems<E, N>(p + c + v * kThreads, x[v]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < N; ++e) x[v][e] = -INFINITY;
+                }
+            }
+            float cm = x[0][0];
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int e = 0; e < N; ++e) cm = fmaxf(cm, x[v][e]);
+            if (cm == -INFINITY) continue;  // nothing finite in this chunk for this lane
+            if (cm > lm) {
+                ls *= exp_diff(lm - cm);  // lm = -inf: 0 * 0
+                lm = cm;
+            }
+            float s = 0.0f;
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int e = 0; e < N; ++e) s += exp_diff(x[v][e] - lm);
+            ls += s;
+        }
+        wave_reduce_pair(lm, ls);
+        if (lane == 0) {
+            red_m[wave] = lm;
+            red_s[wave] = ls;
+        }
+        __syncthreads();
+        lm = red_m[0];
+        ls = red_s[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) merge_pair(lm, ls, red_m[w], red_s[w]);
+        const float m = lm == -INFINITY ? 0.0f : lm;  // all -inf row: every term exp(-inf) = 0
+        const float r = recip_sum(ls);
+
+        raw* q = out + row * a.stride + t;
+        for (int c = 0; c < a.nacc; c += kChunk) {
+            float x[V][N];
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (c + v * kThreads + t < a.nacc) load_elems<E, N>(p + c + v * kThreads, x[v]);
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (c + v * kThreads + t < a.nacc) {
+#pragma unroll
+                    for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m) * r;
+                    store_elems<E, N>(q + c + v * kThreads, x[v]);
+                }
+            }
+        }
+        __syncthreads();  // red_m / red_s are rewritten for the next row
+    }
+}
+
+// ------------------------------------------------------------- copy kernel
+//
+// Plain 16-byte copy, U accesses per thread in flight: the achievable
+// read-once/write-once bandwidth that a finished softmax is compared with.
+template <int U>
+__global__ void __launch_bounds__(256) copy16(const u32x4* src, u32x4* dst, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; base < n; base += stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + (int64_t)u * blockDim.x < n) v[u] = src[base + (int64_t)u * blockDim.x];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + (int64_t)u * blockDim.x < n) dst[base + (int64_t)u * blockDim.x] = v[u];
+    }
+}
+
+}  // namespace rws

@@ -1,0 +1,136 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments before any HIP call.  Nothing here launches work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from row_wise_softmax_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "row_wise_softmax.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = binding.library_path()
+    if not os.path.exists(path):
+        pytest.fail(f"HIP library not built: {path}")
+    return binding._load()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    for want in ("softmax_fwd", "softmax_fwd_kernel", "softmax_select", "softmax_num_kernels",
+                 "softmax_kernel_info", "softmax_kernel_name", "softmax_kernel_fits",
+                 "softmax_status_string", "softmax_version", "softmax_bench_copy"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(binding.library_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), f"{name} declared in the header but not exported"
+
+
+def test_library_is_built_for_gfx950():
+    blob = open(binding.library_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in binding.version()
+    for st in range(7):
+        assert lib.softmax_status_string(st)
+    assert lib.softmax_status_string(99) == b"unknown status"
+
+
+def _fwd(lib, in_ptr, out_ptr, rows, cols, stride, dtype):
+    return lib.softmax_fwd(in_ptr, out_ptr, rows, cols, stride, dtype, None)
+
+
+# Host addresses only: every case below is rejected (or is empty) before the
+# library touches the device, so no address is ever dereferenced.
+A, B = 0x100000, 0x900000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, 4, 8, 8, 7), 3),            # bad dtype
+    ((A, B, 4, 8, 8, -1), 3),
+    ((A, B, -1, 8, 8, 0), 2),           # negative rows
+    ((A, B, 4, -8, 8, 0), 2),           # negative cols
+    ((A, B, 4, 8, 7, 0), 2),            # row_stride < cols
+    ((A, B, 4, 2**30 + 1, 2**31, 0), 2),  # cols > 2^30
+    ((A, B, 2**40, 2**30, 2**30, 0), 2),  # byte extent past INT64_MAX
+    ((0, B, 4, 8, 8, 0), 1),            # null input
+    ((A, 0, 4, 8, 8, 0), 1),            # null output
+    ((A, A + 16, 4, 8, 8, 0), 4),       # partial overlap
+    ((A + 16, A, 4, 8, 8, 1), 4),
+    ((A, B, 0, 8, 8, 0), 0),            # empty: nothing to do
+    ((A, B, 4, 0, 8, 0), 0),
+    ((0, 0, 0, 0, 0, 2), 0),
+])
+def test_argument_errors_before_any_launch(lib, args, status):
+    assert _fwd(lib, *args) == status
+
+
+def test_forced_kernel_errors(lib):
+    n = lib.softmax_num_kernels()
+    assert n > 100
+    assert lib.softmax_fwd_kernel(-1, A, B, 4, 8, 8, 0, None) == 5
+    assert lib.softmax_fwd_kernel(n, A, B, 4, 8, 8, 0, None) == 5
+    table = binding.kernel_table()
+    f16 = next(k for k in table if k.dtype == 1)
+    assert lib.softmax_fwd_kernel(f16.kid, A, B, 4, 8, 8, 0, None) == 5  # wrong dtype
+    narrow = next(k for k in table if k.dtype == 0 and k.max_cols == 4)
+    assert lib.softmax_fwd_kernel(narrow.kid, A, B, 4, 8, 8, 0, None) == 5  # too wide
+    vec = next(k for k in table if k.dtype == 0 and k.vec_elems == 4)
+    assert lib.softmax_fwd_kernel(vec.kid, A + 4, B, 4, 8, 8, 0, None) == 5  # misaligned
+
+
+def test_kernel_table_is_consistent(lib):
+    table = binding.kernel_table()
+    names = [k.name for k in table]
+    assert len(set(names)) == len(names)
+    for k in table:
+        assert k.variant in ("packed", "row", "online")
+        assert k.dtype in (0, 1, 2)
+        if k.variant == "online":
+            assert k.max_cols == -1
+        else:
+            assert k.max_cols == k.lanes * k.vecs_per_lane * k.vec_elems
+        if k.vec_elems > 1:
+            assert k.vec_elems * (4 if k.dtype == 0 else 2) == 16
+    # every dtype has the scalar (any-alignment) path
+    for dt in (0, 1, 2):
+        assert any(k.dtype == dt and k.vec_elems == 1 for k in table)
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("cols", [1, 3, 8, 32, 64, 100, 256, 1000, 1001, 2048, 3000, 4096, 8192,
+                                  16384, 32768, 65536, 131072, 1 << 18])
+def test_dispatch_always_picks_a_fitting_kernel(lib, dtype, cols):
+    kid = binding.softmax_select(A, B, cols, cols, dtype, rows=4)
+    assert binding.kernel_fits(kid, A, B, cols, cols, dtype)
+    info = binding.kernel_table()[kid]
+    esz = 4 if dtype == 0 else 2
+    if (cols * esz) % 16 == 0:
+        assert info.vec_elems * esz == 16, "aligned rows must take 16-byte accesses"
+    # misaligned pointers fall back to the scalar path
+    kid2 = binding.softmax_select(A + 2, B + 2, cols, cols, dtype, rows=4)
+    assert binding.kernel_table()[kid2].vec_elems == 1
+
+
+def test_bench_copy_argument_errors(lib):
+    assert lib.softmax_bench_copy(A, B, 15, None) == 2
+    assert lib.softmax_bench_copy(A + 4, B, 16, None) == 2
+    assert lib.softmax_bench_copy(0, B, 16, None) == 1
+    assert lib.softmax_bench_copy(A, A + 16, 64, None) == 4
+    assert lib.softmax_bench_copy(A, B, 0, None) == 0

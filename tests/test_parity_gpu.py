@@ -1,0 +1,252 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every case prints what it runs before touching the GPU, so a failing run
+names its case.  Inputs are the seeded workloads and seeded edge shapes; the
+oracle computes every expected value.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from row_wise_softmax_amd import binding
+from row_wise_softmax_amd import workloads as W
+
+from gpu_util import TOL, check, check_padding_untouched, decode, run, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    binding._load()  # fails loudly if the HIP library is missing
+
+
+# --------------------------------------------------------- the five configs
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4"])
+def test_config_full_parity(key):
+    wl = W.WORKLOADS[key]
+    _say(f"{key} {wl.name}")
+    x = wl.generate()
+    y = run(x, wl.dtype)
+    ref = O.softmax(x, wl.dtype)
+    err = check(y, x, wl.dtype, ref, label=wl.name)
+    _say(f"{key} max abs err {err:.3e}")
+
+
+def test_c1_special_rows():
+    wl = W.WORKLOADS["c1"]
+    x = wl.generate()
+    y = decode(run(x, "f32"), "f32")
+    assert np.all(np.abs(y[0] - 1e-3) <= 2e-6)          # constant row -> 1/n
+    assert np.isfinite(y[1]).all() and y[1, -1] > 0.999  # the 100.0 entry dominates
+    assert np.all(y[2, 800:] == 0.0)                     # -inf tail -> exact zeros
+    assert abs(y[2, :800].sum() - 1.0) <= 1e-5
+
+
+def test_c2_causal_first_rows():
+    x = W.WORKLOADS["c2"].generate()
+    y = decode(run(x, "f32"), "f32")
+    assert y[0, 0] == 1.0 and np.all(y[0, 1:] == 0.0)
+    for i in (1, 7, 2047):
+        assert np.all(y[i, i + 1:] == 0.0)
+
+
+def _sample_rows(rows, n=192, seed=0):
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([np.arange(min(64, rows)), np.arange(max(0, rows - 64), rows),
+                                    rng.integers(0, rows, size=n - 128 if rows > 128 else 0)]))
+    return idx
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("width", list(W.SWEEP_WIDTHS))
+def test_sweep_full_size_sampled(dtype, width):
+    """Full-size sweep inputs in the benchmark's launch shape: sampled rows
+    against the oracle, and properties that hold at any size on every row."""
+    wl = W.WORKLOADS[f"c5_{dtype}_{width}"]
+    _say(f"sweep {wl.name}")
+    x = wl.generate()
+    y = run(x, dtype, prefill_out=False)
+    idx = _sample_rows(wl.rows)
+    xs = np.ascontiguousarray(x[idx])
+    check(np.ascontiguousarray(y[idx]), xs, dtype, O.softmax(xs, dtype), label=wl.name + " sampled")
+    yd = decode(y, dtype)
+    assert not np.isnan(yd).any() and np.all(yd >= 0.0) and np.all(yd <= 1.0)
+    sums = yd.sum(axis=1)
+    # fp32: the stated row-sum tolerance.  bf16: each output carries a relative
+    # rounding error of at most 2^-9, so the sum is within 2^-9 of 1 (2x margin).
+    tol = 1e-5 if dtype == "f32" else 2.0 ** -8
+    assert np.max(np.abs(sums - 1.0)) <= tol
+
+
+# ------------------------------------------------------------ edge shapes
+
+EDGE_WIDTHS = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 257, 511, 513,
+               999, 1000, 1001, 2047, 2048, 2049, 3000, 4095, 4096, 4097, 8191, 8192, 8193]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cols", EDGE_WIDTHS)
+def test_edge_widths(dtype, cols):
+    _say(f"edge {dtype} cols={cols}")
+    x = W.random_matrix(seed=21, rows=37, cols=cols, dtype=dtype, sigma=3.0)
+    y = run(x, dtype)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"{dtype} cols={cols}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cols", [16384, 32768, 65536, 65537, 131072, 1 << 18])
+def test_wide_rows(dtype, cols):
+    _say(f"wide {dtype} cols={cols}")
+    x = W.random_matrix(seed=22, rows=6, cols=cols, dtype=dtype, sigma=2.0)
+    y = run(x, dtype)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"{dtype} cols={cols}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cols,stride", [(1000, 1024), (1000, 1003), (96, 128), (4096, 4104), (7, 8)])
+def test_row_stride_and_untouched_padding(dtype, cols, stride):
+    _say(f"stride {dtype} cols={cols} stride={stride}")
+    x = W.random_matrix(seed=23, rows=29, cols=cols, dtype=dtype, row_stride=stride)
+    y = run(x, dtype, cols=cols)
+    check(y, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"{dtype} {cols}/{stride}")
+    check_padding_untouched(y, cols, dtype, label=f"{dtype} {cols}/{stride}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cols", [64, 1000, 4096, 70000])
+def test_in_place(dtype, cols):
+    _say(f"in-place {dtype} cols={cols}")
+    x = W.random_matrix(seed=24, rows=33, cols=cols, dtype=dtype)
+    y = run(x, dtype, inplace=True)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"in-place {dtype} {cols}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_misaligned_pointer_takes_scalar_path(dtype):
+    import torch
+    _say(f"misaligned {dtype}")
+    cols = 1000
+    x = W.random_matrix(seed=25, rows=11, cols=cols + 1, dtype=dtype)
+    xd = to_device(x, dtype)[:, 1:]            # starts one element past a 16-byte boundary
+    out_full = torch.empty((11, cols + 1), dtype=xd.dtype, device="cuda")
+    out = out_full[:, 1:]
+    code = W.dtype_code(dtype)
+    kid = binding.softmax_select(xd.data_ptr(), out.data_ptr(), cols, cols + 1, code, rows=11)
+    assert binding.kernel_table()[kid].vec_elems == 1
+    binding.softmax_fwd(xd.data_ptr(), out.data_ptr(), 11, cols, cols + 1, code,
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    y = to_host(out_full, dtype)[:, 1:]
+    xs = np.ascontiguousarray(x[:, 1:])
+    check(np.ascontiguousarray(y), xs, dtype, O.softmax(xs, dtype), label="misaligned")
+
+
+def test_empty_inputs_launch_nothing():
+    import torch
+    x = torch.empty((0, 128), device="cuda")
+    binding.softmax_fwd(x.data_ptr(), x.data_ptr(), 0, 128, 128, 0, 0)
+    binding.softmax_fwd(0, 0, 5, 0, 0, 1, 0)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cols", [8, 256, 4096, 40000])
+def test_all_neg_inf_rows_give_zeros(dtype, cols):
+    _say(f"all -inf {dtype} cols={cols}")
+    x = W.random_matrix(seed=26, rows=9, cols=cols, dtype=dtype)
+    x[3, :] = W.neg_inf(dtype)
+    x[5, ::2] = W.neg_inf(dtype)
+    y = run(x, dtype)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"-inf {dtype} {cols}")
+    yd = decode(y, dtype)
+    assert np.all(yd[3] == 0.0) and not np.signbit(yd[3]).any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_extreme_values(dtype):
+    _say(f"extremes {dtype}")
+    big = {"f32": 3.0e38, "f16": 65504.0, "bf16": 3.0e38}[dtype]
+    x64 = np.random.default_rng(27).standard_normal((6, 300))
+    x64[0, 17] = big
+    x64[1, :] = -big
+    x64[2, 5] = 100.0
+    x64[3, :] = big
+    x = W.cast(x64, dtype)
+    y = run(x, dtype)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"extremes {dtype}")
+
+
+@pytest.mark.parametrize("key", ["c3", "c4", "c5_bf16_32"])
+def test_deterministic(key):
+    wl = W.WORKLOADS[key]
+    x = wl.generate(rows=min(wl.rows, 50000))
+    a = run(x, wl.dtype)
+    b = run(x, wl.dtype)
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_many_rows_past_the_grid_cap():
+    """More workgroups than one launch holds: the kernels' grid-stride loop."""
+    table = binding.kernel_table()
+    kid = next(k.kid for k in table if k.name == "row_f32_w2_v1")
+    rows = (1 << 20) + 3
+    _say(f"grid cap rows={rows}")
+    x = W.random_matrix(seed=28, rows=rows, cols=8, dtype="f32")
+    y = run(x, "f32", kernel_id=kid, prefill_out=False)
+    check(y, x, "f32", O.softmax(x, "f32"), label="grid cap")
+
+
+# ---------------------------------------------------- every table entry
+
+def _table():
+    try:
+        return binding.kernel_table()
+    except Exception:  # library missing: the fixture above fails each test loudly
+        return []
+
+
+_TABLE = _table()
+_DT = {0: "f32", 1: "f16", 2: "bf16"}
+
+
+def _widths_for(k):
+    n = k.vec_elems
+    if k.max_cols > 0:
+        m = k.max_cols
+        ws = {m, max(n, m - n), max(n, (m // 2 // n) * n + n), n}
+    else:
+        chunk = k.lanes * k.vecs_per_lane * n
+        ws = {n, 2 * chunk + 3 * n, chunk + n} if n > 1 else {1, 2 * chunk + 3, 777}
+    return sorted(ws)
+
+
+def _rows_for(k):
+    if k.variant == "packed":
+        per_block = 4 * (64 // k.lanes) * k.groups
+        return 2 * per_block + 7
+    return 45
+
+
+@pytest.mark.parametrize("kid", [k.kid for k in _TABLE], ids=[k.name for k in _TABLE])
+def test_every_kernel_in_the_table(kid):
+    k = _TABLE[kid]
+    dtype = _DT[k.dtype]
+    rows = _rows_for(k)
+    for cols in _widths_for(k):
+        _say(f"{k.name} rows={rows} cols={cols}")
+        x = W.random_matrix(seed=kid, rows=rows, cols=cols, dtype=dtype, sigma=3.0)
+        x[1, : max(1, cols // 3)] = W.neg_inf(dtype)  # a partly masked row
+        y = run(x, dtype, kernel_id=kid)
+        check(y, x, dtype, O.softmax(x, dtype), label=f"{k.name} cols={cols}")
