@@ -67,6 +67,7 @@ extern "C" {
 #define SOFTMAX_VARIANT_PACKED 0 /* L lanes of a wave per row, 64/L rows per wave (narrow rows) */
 #define SOFTMAX_VARIANT_ROW 1    /* one workgroup per row, row held in registers (single pass) */
 #define SOFTMAX_VARIANT_ONLINE 2 /* one workgroup per row, two reads + one write (any width) */
+#define SOFTMAX_VARIANT_ROW_PF 3 /* row kernel, persistent: each workgroup loops over rows and prefetches the next */
 
 /*
  * softmax_fwd -- the fused row softmax, with the library's width dispatch.

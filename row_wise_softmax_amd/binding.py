@@ -22,7 +22,7 @@ def library_path() -> str:
 # dtype codes of the C ABI
 F32, F16, BF16 = 0, 1, 2
 # kernel variants of the C ABI
-VARIANT_NAMES = {0: "packed", 1: "row", 2: "online"}
+VARIANT_NAMES = {0: "packed", 1: "row", 2: "online", 3: "row_pf"}
 
 _lib = None
 

@@ -12,6 +12,7 @@
 // register budget stream twice (online).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <stdint.h>
 #include <string.h>
 
@@ -104,24 +105,31 @@ int pow2_at_least(int64_t v) {
     return p;
 }
 
-// The width dispatch rule.  `nacc` is the row length in 16-byte accesses.
+// The width dispatch rule, set from the width sweep (bench.py --sweep, bf16
+// and fp32, widths 32 ... 16384 at about 200 MB per tensor): the fastest shape
+// at every width keeps about two 16-byte loads in flight per lane and spreads
+// a row over as many lanes as that takes.  `nacc` is the row length in
+// 16-byte accesses.
 const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype) {
     const int vec16 = 16 / elem_bytes(dtype);
     if (aligned16(in, out, cols, row_stride, dtype)) {
         const int64_t nacc = cols / vec16;
         const Entry* e = nullptr;
-        if (nacc <= 32) {
-            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, pow2_at_least(nacc), 1, 4);
-        } else if (nacc <= 64 * 16) {
-            const int v = pow2_at_least((nacc + 63) / 64);
-            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, 64, v, 1);
+        if (nacc <= 64) {
+            // several rows per wave: L lanes per row, two row groups in flight
+            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, pow2_at_least(nacc), 1, 2);
+        } else if (nacc <= 128) {
+            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, 64, 2, 1);
         } else {
-            // Register-resident if some workgroup shape of the table holds the row
-            // at 4 or more accesses per thread; else stream it twice.
-            for (int v = 4; v <= 16 && e == nullptr; v *= 2) {
-                const int w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
-                if (w <= 16) e = find(dtype, SOFTMAX_VARIANT_ROW, vec16, 64 * w, v, 1);
+            // one workgroup per row, two accesses per lane, up to 16 waves;
+            // wider rows keep 16 waves and take more accesses per lane
+            int v = 2;
+            int w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
+            while (w > 16 && v < 16) {
+                v *= 2;
+                w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
             }
+            if (w <= 16) e = find(dtype, SOFTMAX_VARIANT_ROW, vec16, 64 * w, v, 1);
             if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, vec16, 64 * 16, 4, 1);
         }
         if (e && fits(*e, in, out, cols, row_stride, dtype)) return e;
@@ -156,6 +164,33 @@ int validate(const void* in, const void* out, int64_t rows, int64_t cols, int64_
     return SOFTMAX_OK;
 }
 
+// Workgroups of entry `e` the current device holds at once (occupancy per CU
+// x CU count), cached per device and kernel.  Used to size persistent grids.
+constexpr int kMaxDevices = 64;
+constexpr int kMaxKernels = 1024;
+std::atomic<int> g_resident[kMaxDevices][kMaxKernels];  // 0 = not yet known
+
+int64_t resident_workgroups(const Entry& e, int block) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const int id = id_of(&e);
+    const bool cacheable = dev >= 0 && dev < kMaxDevices && id >= 0 && id < kMaxKernels;
+    if (cacheable) {
+        const int known = g_resident[dev][id].load(std::memory_order_relaxed);
+        if (known > 0) return known;
+    }
+    int per_cu = 0, cus = 0;
+    if (dev < 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, e.fn, block, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        return 256 * 4;  // a safe default: the kernel loops over whatever rows remain
+    }
+    const int n = per_cu * cus;
+    if (cacheable) g_resident[dev][id].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
            hipStream_t stream) {
     rws::Args a;
@@ -172,6 +207,10 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
         while (wpb > 1 && (waves + wpb - 1) / wpb < 1024) wpb /= 2;  // small jobs: more, smaller workgroups
         block = wpb * 64;
         a.nblocks = (waves + wpb - 1) / wpb;
+    } else if (e.variant == SOFTMAX_VARIANT_ROW_PF) {
+        block = e.block;
+        const int64_t res = resident_workgroups(e, block);
+        a.nblocks = rows < res ? rows : res;
     } else {
         block = e.block;
         a.nblocks = rows;

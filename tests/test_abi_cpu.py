@@ -100,7 +100,7 @@ def test_kernel_table_is_consistent(lib):
     names = [k.name for k in table]
     assert len(set(names)) == len(names)
     for k in table:
-        assert k.variant in ("packed", "row", "online")
+        assert k.variant in ("packed", "row", "row_pf", "online")
         assert k.dtype in (0, 1, 2)
         if k.variant == "online":
             assert k.max_cols == -1

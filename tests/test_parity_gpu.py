@@ -232,10 +232,14 @@ def _widths_for(k):
     return sorted(ws)
 
 
-def _rows_for(k):
+def _rows_for(k, cols):
     if k.variant == "packed":
         per_block = 4 * (64 // k.lanes) * k.groups
         return 2 * per_block + 7
+    if k.variant == "row_pf":
+        # more rows than the chip holds workgroups, so every workgroup runs
+        # its prefetch loop (at most 32 resident workgroups per CU x 256 CUs)
+        return max(45, min(16389, 20_000_000 // max(cols, 1)))
     return 45
 
 
@@ -243,8 +247,8 @@ def _rows_for(k):
 def test_every_kernel_in_the_table(kid):
     k = _TABLE[kid]
     dtype = _DT[k.dtype]
-    rows = _rows_for(k)
     for cols in _widths_for(k):
+        rows = _rows_for(k, cols)
         _say(f"{k.name} rows={rows} cols={cols}")
         x = W.random_matrix(seed=kid, rows=rows, cols=cols, dtype=dtype, sigma=3.0)
         x[1, : max(1, cols // 3)] = W.neg_inf(dtype)  # a partly masked row
