@@ -60,6 +60,11 @@ def _load():
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_void_p,
         ]
+        lib.oracle_softmax_causal.restype = ctypes.c_int
+        lib.oracle_softmax_causal.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_int64, ctypes.c_void_p,
+        ]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_bf16.restype = ctypes.c_double
@@ -90,6 +95,31 @@ def softmax(x: np.ndarray, dtype: str, cols: int | None = None) -> np.ndarray:
     rc = lib.oracle_softmax(x.ctypes.data, code, rows, cols, stride, out.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_softmax rejected its arguments (rc={rc})")
+    return out
+
+
+def softmax_causal(x: np.ndarray, dtype: str, scale: float, diag: int = 0,
+                   cols: int | None = None) -> np.ndarray:
+    """Scaled, causally masked row softmax in float64.
+
+    Row i keeps columns j <= i + diag; kept entries are multiplied by
+    ``scale`` (> 0) before the softmax, masked ones give +0.  ``x`` is held
+    as in :func:`softmax`.
+    """
+    lib = _load()
+    code = DTYPE_CODES[dtype]
+    want = np.float32 if dtype == "f32" else np.uint16
+    if x.dtype != want:
+        raise TypeError(f"oracle: {dtype} input must be held as {want.__name__}, got {x.dtype}")
+    if x.ndim != 2 or not x.flags.c_contiguous:
+        raise ValueError("oracle: input must be a 2-D C-contiguous array")
+    rows, stride = x.shape
+    cols = stride if cols is None else int(cols)
+    out = np.empty((rows, cols), dtype=np.float64)
+    rc = lib.oracle_softmax_causal(x.ctypes.data, code, rows, cols, stride, float(scale), int(diag),
+                                   out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_softmax_causal rejected its arguments (rc={rc})")
     return out
 
 

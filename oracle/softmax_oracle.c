@@ -139,3 +139,60 @@ int oracle_softmax(const void *in, int dtype, int64_t rows, int64_t cols,
     }
     return 0;
 }
+
+/*
+ * Scaled, causally masked row softmax ("Dissecting Memory Bandwidth & SRAM
+ * Tiling in Triton", section "Writing the Kernel in OpenAI Triton": scores
+ * scaled by 1/sqrt(d), entries with column > row set to -inf before the
+ * softmax).  For row i, column j is kept when j <= i + diag; for the kept
+ * columns  z_j = scale * x_ij  and
+ *     y_ij = exp(z_j - max_kept z) / sum_kept exp(z_k - max_kept z),
+ * and every masked column gets +0.  A row with no kept column, or whose kept
+ * entries are all -inf, is all +0.  `scale` must be finite and > 0.
+ * Masked inputs are never read.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_softmax_causal(const void *in, int dtype, int64_t rows, int64_t cols,
+                          int64_t row_stride, double scale, int64_t diag, double *out)
+{
+    if (rows < 0 || cols < 0 || row_stride < cols) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (!(scale > 0.0) || isinf(scale)) return -1;
+    if (rows == 0 || cols == 0) return 0;
+    if (in == NULL || out == NULL) return -1;
+
+    for (int64_t i = 0; i < rows; ++i) {
+        double *y = out + i * cols;
+        /* Number of kept columns: j = 0 .. i + diag, clipped to [0, cols]
+           (written so that no sum can overflow for any diag). */
+        int64_t kept;
+        if (diag >= cols) {
+            kept = cols;
+        } else if (diag < -i) {
+            kept = 0;
+        } else {
+            kept = i + diag + 1;
+            if (kept > cols) kept = cols;
+        }
+
+        for (int64_t j = 0; j < cols; ++j) y[j] = 0.0;
+        for (int64_t j = 0; j < kept; ++j)
+            y[j] = scale * load_element(in, dtype, i * row_stride + j);
+
+        double m = -INFINITY;
+        for (int64_t j = 0; j < kept; ++j)
+            if (y[j] > m) m = y[j];
+        if (m == -INFINITY) {
+            for (int64_t j = 0; j < kept; ++j) y[j] = 0.0;
+            continue;
+        }
+
+        double s = 0.0;
+        for (int64_t j = 0; j < kept; ++j) {
+            y[j] = exp(y[j] - m);
+            s += y[j];
+        }
+        for (int64_t j = 0; j < kept; ++j)
+            y[j] = y[j] / s;
+    }
+    return 0;
+}

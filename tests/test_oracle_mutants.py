@@ -28,6 +28,12 @@ MUTANTS = {
     "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "bf16_hidden_bit": ("(double)(128 + frac)", "(double)(frac)"),
     "multiply_by_sum": ("y[j] = y[j] / s;", "y[j] = y[j] * s;"),
+    "causal_kept_off_by_one": ("kept = i + diag + 1;", "kept = i + diag;"),
+    "causal_scale_dropped": ("y[j] = scale * load_element(in, dtype, i * row_stride + j);",
+                             "y[j] = load_element(in, dtype, i * row_stride + j);"),
+    "causal_reads_masked": ("for (int64_t j = 0; j < kept; ++j)\n            y[j] = scale",
+                            "for (int64_t j = 0; j < cols; ++j)\n            y[j] = scale"),
+    "causal_diag_sign": ("} else if (diag < -i) {", "} else if (diag < i) {"),
 }
 
 
@@ -35,7 +41,7 @@ MUTANTS = {
 def test_pins_catch_planted_mistake(name, tmp_path):
     old, new = MUTANTS[name]
     src = open(SRC).read()
-    assert old in src, f"mutation site for {name} not found"
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutant_c = tmp_path / "mutant.c"
     mutant_c.write_text(src.replace(old, new, 1))
     lib = tmp_path / "libmutant.so"
@@ -43,6 +49,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                    check=True)
     env = dict(os.environ, ROW_SOFTMAX_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                        os.path.join(ROOT, "tests", "test_oracle.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_causal.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
