@@ -18,6 +18,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu]
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
 import hashlib
 import json
 import os
@@ -114,6 +116,39 @@ class Resident:
         return o.numpy() if self.wl.dtype == "f32" else o.view(torch.int16).numpy().view(np.uint16)
 
 
+def causal_c2(steps: int, warmup: int) -> dict:
+    """c2's structure with the mask and scale fused into the kernel: raw q k^T
+    scores in, softmax(scores / 8) with columns j > i masked out.  The kernel
+    reads only the kept columns (about half) and writes every column."""
+    import torch
+    wl = W.WORKLOADS["c2"]
+    rng = np.random.default_rng(list(wl.seed))
+    q = rng.standard_normal((wl.cols, 64))
+    k = rng.standard_normal((wl.cols, 64))
+    x = W.cast(q @ k.T, "f32")
+    res = Resident(wl, x=x)
+    stream = res.stream
+
+    def launch(i):
+        binding.softmax_fwd_causal(res.ins[i].data_ptr(), res.outs[i].data_ptr(), wl.rows, wl.cols, wl.cols,
+                                   0.125, 0, res.code, stream)
+
+    ms = time_launches(launch, res.n, steps, warmup)
+    n = wl.rows
+    actual = (n * (n + 1) // 2 + n * wl.cols) * 4  # kept columns read + every column written
+    kid = binding.softmax_select(res.ins[0].data_ptr(), res.outs[0].data_ptr(), wl.cols, wl.cols, res.code,
+                                 rows=wl.rows, causal=True)
+    d = {"workload": "c2_causal_2048x2048_f32_fused_mask_scale", "rows": n, "cols": wl.cols, "dtype": "f32",
+         "kernel": binding.kernel_table()[kid].name, "buffers": res.n, "us": round(ms * 1e3, 3),
+         "gbps": round(wl.bytes / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(wl.bytes / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4),
+         "actual_bytes": actual, "actual_gbps": round(actual / (ms * 1e-3) / 1e9, 1),
+         "note": "gbps uses the metric's 2*rows*cols*4 bytes; actual_gbps the bytes moved (masked inputs are not read)"}
+    log(f"[bench] {d['workload']}: {d['us']} us  metric {d['gbps']} GB/s  actual {d['actual_gbps']} GB/s  kernel={d['kernel']}")
+    del res
+    torch.cuda.synchronize()
+    return d
+
+
 def kernel_name(res: Resident) -> str:
     kid = binding.softmax_select(res.ins[0].data_ptr(), res.outs[0].data_ptr(), res.wl.cols, res.wl.cols,
                                  res.code, rows=res.wl.rows)
@@ -134,6 +169,7 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool) -> dict:
         mms = time_launches(res.memcpy, res.n, steps, warmup)
         d["copy_kernel_gbps"] = round(wl.bytes / (cms * 1e-3) / 1e9, 1)
         d["memcpy_gbps"] = round(wl.bytes / (mms * 1e-3) / 1e9, 1)
+        d["frac_of_copy"] = round(gbps / d["copy_kernel_gbps"], 4)
     log(f"[bench] {wl.name}: {d['us']} us  {d['gbps']} GB/s  ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
         f"  kernel={d['kernel']}")
     d["_res"] = res
@@ -234,6 +270,85 @@ def sweep(steps: int, warmup: int) -> list:
     return rows_out
 
 
+# ------------------------------------------------------------ profile summaries
+
+C3_BYTES = 8192 * 4096 * 2  # input bytes of the headline workload (8192 x 4096 fp16)
+
+
+def summarize_trace(stats_csv):
+    """Write profiles/kernel_trace_bench.md from a rocprofv3 --stats kernel_stats.csv."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = ["# Kernel trace of the default benchmark run on MI355X (gfx950)", "",
+           "Command (repository root):", "",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- python3 bench.py --no-cpu",
+           "    python3 bench.py --summarize-trace gpurun_out/prof_trace/bench_kernel_stats.csv",
+           "",
+           "bench.py runs 50 warm-up + 200 timed launches per kernel and shape, over rotating buffer sets of at least 1 GiB.",
+           "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal>`:",
+           "",
+           "- `softmax_row<F32,4,2,2,false>`: c1 128x1000 fp32;",
+           "- `softmax_row<F32,4,4,2,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
+           "- `softmax_row<F32,4,4,2,true>`: c2 with the mask and 1/8 scale fused (raw scores in);",
+           "- `softmax_row<F16,8,4,2,false>`: c3 8192x4096 fp16 (the headline);",
+           "- `softmax_row<F32,4,8,2,false>`: c4 4096x4096 fp32;",
+           "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape.", "",
+           "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    path = os.path.join(PROFILE_DIR, "kernel_trace_bench.md")
+    open(path, "w").write("\n".join(out) + "\n")
+    print(open(path).read())
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """Write profiles/counters_c3_8192x4096_f16.txt from two rocprofv3 --pmc runs."""
+
+    def avg(f, counter):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in d.items()}
+
+    fe = avg(fetch_csv, "FETCH_SIZE")
+    wr = avg(write_csv, "WRITE_SIZE")
+    sm = next(k for k in fe if "softmax" in k)
+    cp = next(k for k in fe if "copy16" in k)
+    kib = C3_BYTES / 1024
+    f_scale = kib / fe[cp]
+    w_scale = kib / wr[cp]
+    fetch_b = fe[sm] * f_scale * 1024
+    write_b = wr[sm] * w_scale * 1024
+    total = fetch_b + write_b
+    alg = 2 * C3_BYTES
+    txt = f"""# HBM traffic of the softmax kernel on 8192 x 4096 fp16 (c3_8192x4096_f16), MI355X (gfx950)
+# Two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), run from the repository root:
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o c3 -- python3 bench.py --only c3 --no-cpu --steps 20 --warmup 5
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o c3 -- python3 bench.py --only c3 --no-cpu --steps 20 --warmup 5
+# then: python3 bench.py --summarize-counters gpurun_out/prof_fetch/c3_counter_collection.csv gpurun_out/prof_write/c3_counter_collection.csv
+# Counters are KiB per dispatch, averaged over each kernel's dispatches, and calibrated with
+# the plain 16-byte copy kernel (softmax_bench_copy) of the same run, which reads and writes
+# exactly {C3_BYTES} bytes: scale = known KiB / counter KiB.  FETCH_SIZE on this part
+# reads about half of the bytes actually fetched (scale ~2.0); WRITE_SIZE reads true (~1.0).
+kernel: {sm}
+source_digest: {source_digest()}
+copy_kernel_fetch_kib: {fe[cp]:.1f}
+copy_kernel_write_kib: {wr[cp]:.1f}
+fetch_scale: {f_scale:.5f}
+write_scale: {w_scale:.5f}
+softmax_fetch_kib_raw: {fe[sm]:.1f}
+softmax_write_kib_raw: {wr[sm]:.1f}
+softmax_fetch_bytes: {fetch_b:.0f}
+softmax_write_bytes: {write_b:.0f}
+hbm_bytes_per_dispatch: {total:.0f}
+algorithmic_bytes_per_dispatch: {alg}
+traffic_over_algorithmic: {total / alg:.5f}
+"""
+    path = os.path.join(PROFILE_DIR, "counters_c3_8192x4096_f16.txt")
+    open(path, "w").write(txt)
+    print(txt)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,7 +359,18 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", default=None, help="comma-separated workload keys to time (default: c1..c4)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV", default=None,
+                    help="write profiles/kernel_trace_bench.md from a rocprofv3 --stats CSV and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write profiles/counters_c3_8192x4096_f16.txt from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); rows of a softmax "
@@ -271,9 +397,11 @@ def main() -> int:
         keys = [HEADLINE] + keys
     shapes = {}
     for key in keys:
-        shapes[key] = measure_shape(key, args.steps, args.warmup, with_copy=(key == HEADLINE))
+        shapes[key] = measure_shape(key, args.steps, args.warmup, with_copy=True)
         if key != HEADLINE:
             del shapes[key]["_res"]  # free its buffers before the next shape
+    if args.only is None:
+        shapes["c2_fused"] = causal_c2(args.steps, args.warmup)
 
     head = shapes[HEADLINE]
     res = head.pop("_res")

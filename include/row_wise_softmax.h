@@ -60,8 +60,9 @@ extern "C" {
 #define SOFTMAX_ERR_BAD_SHAPE 2    /* negative dims, row_stride < cols, cols > 2^30, or a byte extent past INT64_MAX */
 #define SOFTMAX_ERR_BAD_DTYPE 3    /* dtype not one of SOFTMAX_F32 / F16 / BF16 */
 #define SOFTMAX_ERR_OVERLAP 4      /* in and out overlap without being equal */
-#define SOFTMAX_ERR_BAD_KERNEL 5   /* forced kernel id unknown, of another dtype, or unable to take this width / alignment */
+#define SOFTMAX_ERR_BAD_KERNEL 5   /* forced kernel id unknown, of another dtype or kind, or unable to take this width / alignment */
 #define SOFTMAX_ERR_HIP 6          /* the HIP runtime refused the launch */
+#define SOFTMAX_ERR_BAD_SCALE 7    /* causal entry points: scale not > 0, or scale * log2(e) not below 3e38 */
 
 /* Kernel variants of the compiled table. */
 #define SOFTMAX_VARIANT_PACKED 0 /* L lanes of a wave per row, 64/L rows per wave (narrow rows) */
@@ -89,6 +90,29 @@ int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int64_t r
                 int dtype, void *stream);
 
 /*
+ * softmax_fwd_causal -- the scaled, causally masked row softmax: row i keeps
+ * columns j <= i + diag, and
+ *
+ *     y[i, j] = exp(scale x[i, j] - M_i) / sum_{k <= i + diag} exp(scale x[i, k] - M_i)
+ *
+ * for kept j (M_i the max of scale x over the kept columns), y[i, j] = +0 for
+ * masked j; rows with no kept column, or whose kept entries are all -inf,
+ * are all +0.  This is the score scaling and causal mask applied before the
+ * softmax in "Dissecting Memory Bandwidth & SRAM Tiling in Triton", section
+ * "Writing the Kernel in OpenAI Triton" (scale 1/sqrt(head dim), mask
+ * column > row), fused into the softmax: masked inputs are never read, so a
+ * causal square reads about half of its input while still writing all of
+ * its output.  diag = 0 is that mask; diag = cols - rows aligns it to the
+ * bottom-right corner; any int64 value is accepted.
+ *   scale  > 0 with scale * log2(e) below 3e38 (else SOFTMAX_ERR_BAD_SCALE);
+ *          it is folded into the exponent as one fp32 coefficient
+ *          scale * log2(e).
+ * Other arguments, layout, ownership, aliasing and errors as softmax_fwd.
+ */
+int softmax_fwd_causal(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
+                       float scale, int64_t diag, int dtype, void *stream);
+
+/*
  * softmax_fwd_kernel -- the same operation through one forced entry of the
  * compiled kernel table (for width sweeps and tests).  Same arguments and
  * errors as softmax_fwd, plus SOFTMAX_ERR_BAD_KERNEL when `kernel_id` is out of
@@ -99,6 +123,14 @@ int softmax_fwd_kernel(int kernel_id, const void *in, void *out, int64_t rows, i
                        int64_t row_stride, int dtype, void *stream);
 
 /*
+ * softmax_fwd_causal_kernel -- softmax_fwd_causal through one forced causal
+ * table entry.  Plain entries are refused with SOFTMAX_ERR_BAD_KERNEL (and
+ * softmax_fwd_kernel refuses causal ones).
+ */
+int softmax_fwd_causal_kernel(int kernel_id, const void *in, void *out, int64_t rows, int64_t cols,
+                              int64_t row_stride, float scale, int64_t diag, int dtype, void *stream);
+
+/*
  * softmax_select -- the kernel id softmax_fwd would launch for these
  * arguments, written to *kernel_id.  Validates like softmax_fwd (rows only
  * matters for validation and launch shape); launches nothing.
@@ -106,12 +138,17 @@ int softmax_fwd_kernel(int kernel_id, const void *in, void *out, int64_t rows, i
 int softmax_select(const void *in, const void *out, int64_t rows, int64_t cols, int64_t row_stride,
                    int dtype, int *kernel_id);
 
+/* softmax_select for softmax_fwd_causal: the causal entry it would launch. */
+int softmax_select_causal(const void *in, const void *out, int64_t rows, int64_t cols, int64_t row_stride,
+                          int dtype, int *kernel_id);
+
 /* Number of entries in the compiled kernel table (ids 0 .. n-1). */
 int softmax_num_kernels(void);
 
 /*
  * softmax_kernel_info -- the parameters of table entry `kernel_id`:
- *   dtype, variant (SOFTMAX_VARIANT_*), vec_elems (elements per memory access),
+ *   dtype, variant (SOFTMAX_VARIANT_*), causal (1 for an entry of the scaled,
+ *   causally masked softmax, 0 for the plain one), vec_elems (elements per memory access),
  *   lanes (packed: lanes per row; row/online: threads per row),
  *   vecs_per_lane (accesses per lane per row, or per chunk for online),
  *   groups (packed: row groups per wave in flight; else 1),
@@ -119,7 +156,7 @@ int softmax_num_kernels(void);
  *   max_cols (widest row it takes; -1 for any).
  * Any out-pointer may be NULL.  Returns SOFTMAX_ERR_BAD_KERNEL for an unknown id.
  */
-int softmax_kernel_info(int kernel_id, int *dtype, int *variant, int *vec_elems, int *lanes,
+int softmax_kernel_info(int kernel_id, int *dtype, int *variant, int *causal, int *vec_elems, int *lanes,
                         int *vecs_per_lane, int *groups, int *block, int64_t *max_cols);
 
 /* Static, human-readable name of table entry `kernel_id` (NULL if unknown). */

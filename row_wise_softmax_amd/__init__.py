@@ -8,6 +8,7 @@ device memory and streams.
 from .binding import (  # noqa: F401
     softmax,
     softmax_fwd,
+    softmax_fwd_causal,
     softmax_fwd_kernel,
     softmax_select,
     kernel_table,

@@ -54,12 +54,18 @@ def _load():
     lib.softmax_fwd.argtypes = [vp, vp, i64, i64, i64, i32, vp]
     lib.softmax_fwd_kernel.restype = i32
     lib.softmax_fwd_kernel.argtypes = [i32, vp, vp, i64, i64, i64, i32, vp]
+    lib.softmax_fwd_causal.restype = i32
+    lib.softmax_fwd_causal.argtypes = [vp, vp, i64, i64, i64, ctypes.c_float, i64, i32, vp]
+    lib.softmax_fwd_causal_kernel.restype = i32
+    lib.softmax_fwd_causal_kernel.argtypes = [i32, vp, vp, i64, i64, i64, ctypes.c_float, i64, i32, vp]
+    lib.softmax_select_causal.restype = i32
+    lib.softmax_select_causal.argtypes = [vp, vp, i64, i64, i64, i32, ctypes.POINTER(i32)]
     lib.softmax_select.restype = i32
     lib.softmax_select.argtypes = [vp, vp, i64, i64, i64, i32, ctypes.POINTER(i32)]
     lib.softmax_num_kernels.restype = i32
     lib.softmax_num_kernels.argtypes = []
     lib.softmax_kernel_info.restype = i32
-    lib.softmax_kernel_info.argtypes = [i32] + [ctypes.POINTER(i32)] * 7 + [ctypes.POINTER(i64)]
+    lib.softmax_kernel_info.argtypes = [i32] + [ctypes.POINTER(i32)] * 8 + [ctypes.POINTER(i64)]
     lib.softmax_kernel_name.restype = ctypes.c_char_p
     lib.softmax_kernel_name.argtypes = [i32]
     lib.softmax_kernel_fits.restype = i32
@@ -98,13 +104,28 @@ def softmax_fwd_kernel(kernel_id: int, in_ptr: int, out_ptr: int, rows: int, col
            "softmax_fwd_kernel")
 
 
+def softmax_fwd_causal(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int,
+                       scale: float, diag: int, dtype: int, stream: int = 0) -> None:
+    """Raw entry point of the scaled, causally masked softmax (row i keeps j <= i + diag)."""
+    lib = _load()
+    _check(lib.softmax_fwd_causal(in_ptr, out_ptr, rows, cols, row_stride, scale, diag, dtype, stream),
+           "softmax_fwd_causal")
+
+
+def softmax_fwd_causal_kernel(kernel_id: int, in_ptr: int, out_ptr: int, rows: int, cols: int,
+                              row_stride: int, scale: float, diag: int, dtype: int, stream: int = 0) -> None:
+    lib = _load()
+    _check(lib.softmax_fwd_causal_kernel(kernel_id, in_ptr, out_ptr, rows, cols, row_stride, scale, diag,
+                                         dtype, stream), "softmax_fwd_causal_kernel")
+
+
 def softmax_select(in_ptr: int, out_ptr: int, cols: int, row_stride: int, dtype: int,
-                   rows: int = 1) -> int:
+                   rows: int = 1, causal: bool = False) -> int:
     """The kernel id the library's width dispatch picks for this call."""
     lib = _load()
     kid = ctypes.c_int(-1)
-    _check(lib.softmax_select(in_ptr, out_ptr, rows, cols, row_stride, dtype, ctypes.byref(kid)),
-           "softmax_select")
+    fn = lib.softmax_select_causal if causal else lib.softmax_select
+    _check(fn(in_ptr, out_ptr, rows, cols, row_stride, dtype, ctypes.byref(kid)), "softmax_select")
     return kid.value
 
 
@@ -120,6 +141,7 @@ class KernelInfo:
     name: str
     dtype: int
     variant: str
+    causal: bool        # entry of the scaled, causally masked softmax
     vec_elems: int      # elements per load
     lanes: int          # lanes per row (packed) or threads per row (row/online)
     vecs_per_lane: int  # loads per lane per row (or per chunk, online)
@@ -132,13 +154,13 @@ def kernel_table() -> list[KernelInfo]:
     lib = _load()
     out = []
     for kid in range(lib.softmax_num_kernels()):
-        ints = [ctypes.c_int() for _ in range(7)]
+        ints = [ctypes.c_int() for _ in range(8)]
         mc = ctypes.c_int64()
         _check(lib.softmax_kernel_info(kid, *[ctypes.byref(v) for v in ints], ctypes.byref(mc)),
                "softmax_kernel_info")
-        dt, var, ve, lanes, vpl, groups, block = (v.value for v in ints)
+        dt, var, causal, ve, lanes, vpl, groups, block = (v.value for v in ints)
         out.append(KernelInfo(kid, lib.softmax_kernel_name(kid).decode(), dt, VARIANT_NAMES[var],
-                              ve, lanes, vpl, groups, block, mc.value))
+                              bool(causal), ve, lanes, vpl, groups, block, mc.value))
     return out
 
 
@@ -175,11 +197,15 @@ def _as_rows(t):
     return t.numel() // max(cols, 1), cols, cols
 
 
-def softmax(x, out=None, kernel_id: int | None = None):
+def softmax(x, out=None, kernel_id: int | None = None, causal: bool = False, scale: float = 1.0,
+            diag: int = 0):
     """Row softmax over the last dimension of a CUDA (HIP) tensor.
 
     ``out`` (optional) must match ``x`` in shape, dtype and strides; it may be
-    ``x`` itself (in place).  The call is asynchronous on torch's current stream.
+    ``x`` itself (in place).  With ``causal=True`` row i keeps columns
+    j <= i + diag and the kept entries are multiplied by ``scale`` first (rows
+    count over all leading dimensions).  The call is asynchronous on torch's
+    current stream.
     """
     import torch
     if not x.is_cuda:
@@ -191,7 +217,13 @@ def softmax(x, out=None, kernel_id: int | None = None):
     if out.shape != x.shape or out.dtype != x.dtype or out.stride() != x.stride() or out.device != x.device:
         raise ValueError("softmax: out must match the input's shape, dtype, strides and device")
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    if kernel_id is None:
+    if causal:
+        if kernel_id is None:
+            softmax_fwd_causal(x.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag, code, stream)
+        else:
+            softmax_fwd_causal_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag,
+                                      code, stream)
+    elif kernel_id is None:
         softmax_fwd(x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
     else:
         softmax_fwd_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)

@@ -16,6 +16,7 @@ namespace rws {
 struct Entry {
     int dtype;    // SOFTMAX_F32 / F16 / BF16
     int variant;  // SOFTMAX_VARIANT_*
+    bool causal;  // scaled, causally masked softmax (softmax_fwd_causal)
     int vec;      // elements per access
     int lanes;    // packed: lanes per row; row/online: threads per row
     int vpl;      // accesses per lane per row (online: per chunk)

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -26,6 +27,7 @@ using rws::Entry;
 
 constexpr int64_t kMaxGrid = int64_t(1) << 20;  // workgroups per launch; kernels loop past it
 constexpr int64_t kMaxCols = int64_t(1) << 30;  // keeps every in-row index, chunk offset included, in int
+constexpr double kLog2eD = 1.4426950408889634074;
 
 int elem_bytes(int dtype) { return dtype == SOFTMAX_F32 ? 4 : 2; }
 
@@ -80,12 +82,13 @@ bool fits(const Entry& e, const void* in, const void* out, int64_t cols, int64_t
     return mc < 0 || cols <= mc;
 }
 
-const Entry* find(int dtype, int variant, int vec, int lanes, int vpl, int groups) {
+const Entry* find(int dtype, int variant, bool causal, int vec, int lanes, int vpl, int groups) {
     int n;
     const Entry* t = table_of(dtype, &n);
     for (int i = 0; i < n; ++i) {
         const Entry& e = t[i];
-        if (e.variant == variant && e.vec == vec && e.lanes == lanes && e.vpl == vpl && e.groups == groups)
+        if (e.variant == variant && e.causal == causal && e.vec == vec && e.lanes == lanes && e.vpl == vpl &&
+            e.groups == groups)
             return &e;
     }
     return nullptr;
@@ -109,17 +112,18 @@ int pow2_at_least(int64_t v) {
 // and fp32, widths 32 ... 16384 at about 200 MB per tensor): the fastest shape
 // at every width keeps about two 16-byte loads in flight per lane and spreads
 // a row over as many lanes as that takes.  `nacc` is the row length in
-// 16-byte accesses.
-const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype) {
+// 16-byte accesses.  The causal table holds the same picks.
+const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype,
+                          bool causal) {
     const int vec16 = 16 / elem_bytes(dtype);
     if (aligned16(in, out, cols, row_stride, dtype)) {
         const int64_t nacc = cols / vec16;
         const Entry* e = nullptr;
         if (nacc <= 64) {
             // several rows per wave: L lanes per row, two row groups in flight
-            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, pow2_at_least(nacc), 1, 2);
+            e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, pow2_at_least(nacc), 1, 2);
         } else if (nacc <= 128) {
-            e = find(dtype, SOFTMAX_VARIANT_PACKED, vec16, 64, 2, 1);
+            e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1);
         } else {
             // one workgroup per row, two accesses per lane, up to 16 waves;
             // wider rows keep 16 waves and take more accesses per lane
@@ -129,14 +133,14 @@ const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t
                 v *= 2;
                 w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
             }
-            if (w <= 16) e = find(dtype, SOFTMAX_VARIANT_ROW, vec16, 64 * w, v, 1);
-            if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, vec16, 64 * 16, 4, 1);
+            if (w <= 16) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * w, v, 1);
+            if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, 4, 1);
         }
         if (e && fits(*e, in, out, cols, row_stride, dtype)) return e;
     }
     // Any alignment: scalar accesses, streamed twice.
     const int w = cols <= 64 * 8 ? 1 : (cols <= 4 * 64 * 8 * 4 ? 4 : 16);
-    return find(dtype, SOFTMAX_VARIANT_ONLINE, 1, 64 * w, 8, 1);
+    return find(dtype, SOFTMAX_VARIANT_ONLINE, causal, 1, 64 * w, 8, 1);
 }
 
 // Shared validation.  Returns SOFTMAX_OK, or an error; *empty is set when
@@ -162,6 +166,16 @@ int validate(const void* in, const void* out, int64_t rows, int64_t cols, int64_
         if (a < b + uint64_t(extent) && b < a + uint64_t(extent)) return SOFTMAX_ERR_OVERLAP;
     }
     return SOFTMAX_OK;
+}
+
+// The exponent coefficient scale * log2(e), rounded once to fp32; scale must
+// be finite and > 0 (the max of scale * x is then scale * max x).
+bool coef_of(float scale, float* coef) {
+    if (!(scale > 0.0f) || isinf(scale)) return false;
+    const double c = double(scale) * kLog2eD;
+    if (!(c <= double(3.0e38f))) return false;
+    *coef = float(c);
+    return *coef > 0.0f;
 }
 
 // Workgroups of entry `e` the current device holds at once (occupancy per CU
@@ -191,14 +205,17 @@ int64_t resident_workgroups(const Entry& e, int block) {
     return n;
 }
 
-int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
-           hipStream_t stream) {
+int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, float coef,
+           int64_t diag, hipStream_t stream) {
     rws::Args a;
     a.in = in;
     a.out = out;
     a.rows = rows;
     a.stride = row_stride / e.vec;
+    a.diag = diag;
     a.nacc = int(cols / e.vec);
+    a.cols = int(cols);
+    a.coef = coef;
     int block;
     if (e.variant == SOFTMAX_VARIANT_PACKED) {
         const int64_t rows_per_wave = int64_t(64 / e.lanes) * e.groups;
@@ -225,52 +242,89 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     return SOFTMAX_OK;
 }
 
+int fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, bool causal,
+        float scale, int64_t diag, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    float coef = float(kLog2eD);
+    if (causal && !coef_of(scale, &coef)) return SOFTMAX_ERR_BAD_SCALE;
+    if (empty) return SOFTMAX_OK;
+    const Entry* e = select_entry(in, out, cols, row_stride, dtype, causal);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    return launch(*e, in, out, rows, cols, row_stride, coef, diag, static_cast<hipStream_t>(stream));
+}
+
+int fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
+               int dtype, bool causal, float scale, int64_t diag, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    float coef = float(kLog2eD);
+    if (causal && !coef_of(scale, &coef)) return SOFTMAX_ERR_BAD_SCALE;
+    const Entry* e = entry_by_id(kernel_id);
+    if (e == nullptr || e->causal != causal) return SOFTMAX_ERR_BAD_KERNEL;
+    if (empty) return e->dtype == dtype ? SOFTMAX_OK : SOFTMAX_ERR_BAD_KERNEL;
+    if (!fits(*e, in, out, cols, row_stride, dtype)) return SOFTMAX_ERR_BAD_KERNEL;
+    return launch(*e, in, out, rows, cols, row_stride, coef, diag, static_cast<hipStream_t>(stream));
+}
+
+int select_id(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+              bool causal, int* kernel_id) {
+    if (kernel_id == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    const Entry* e =
+        select_entry(in, out, cols > 0 ? cols : 1, row_stride > 0 ? row_stride : 1, dtype, causal);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    *kernel_id = id_of(e);
+    return SOFTMAX_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
                 void* stream) {
-    bool empty;
-    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
-    if (st != SOFTMAX_OK || empty) return st;
-    const Entry* e = select_entry(in, out, cols, row_stride, dtype);
-    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
-    return launch(*e, in, out, rows, cols, row_stride, static_cast<hipStream_t>(stream));
+    return fwd(in, out, rows, cols, row_stride, dtype, false, 1.0f, 0, stream);
 }
 
-int softmax_fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols,
-                       int64_t row_stride, int dtype, void* stream) {
-    bool empty;
-    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
-    if (st != SOFTMAX_OK) return st;
-    const Entry* e = entry_by_id(kernel_id);
-    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
-    if (empty) return e->dtype == dtype ? SOFTMAX_OK : SOFTMAX_ERR_BAD_KERNEL;
-    if (!fits(*e, in, out, cols, row_stride, dtype)) return SOFTMAX_ERR_BAD_KERNEL;
-    return launch(*e, in, out, rows, cols, row_stride, static_cast<hipStream_t>(stream));
+int softmax_fwd_causal(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, float scale,
+                       int64_t diag, int dtype, void* stream) {
+    return fwd(in, out, rows, cols, row_stride, dtype, true, scale, diag, stream);
+}
+
+int softmax_fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
+                       int dtype, void* stream) {
+    return fwd_kernel(kernel_id, in, out, rows, cols, row_stride, dtype, false, 1.0f, 0, stream);
+}
+
+int softmax_fwd_causal_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols,
+                              int64_t row_stride, float scale, int64_t diag, int dtype, void* stream) {
+    return fwd_kernel(kernel_id, in, out, rows, cols, row_stride, dtype, true, scale, diag, stream);
 }
 
 int softmax_select(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
                    int* kernel_id) {
-    if (kernel_id == nullptr) return SOFTMAX_ERR_NULL_POINTER;
-    bool empty;
-    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
-    if (st != SOFTMAX_OK) return st;
-    const Entry* e = select_entry(in, out, cols > 0 ? cols : 1, row_stride > 0 ? row_stride : 1, dtype);
-    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
-    *kernel_id = id_of(e);
-    return SOFTMAX_OK;
+    return select_id(in, out, rows, cols, row_stride, dtype, false, kernel_id);
+}
+
+int softmax_select_causal(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
+                          int dtype, int* kernel_id) {
+    return select_id(in, out, rows, cols, row_stride, dtype, true, kernel_id);
 }
 
 int softmax_num_kernels(void) { return total_kernels(); }
 
-int softmax_kernel_info(int kernel_id, int* dtype, int* variant, int* vec_elems, int* lanes, int* vecs_per_lane,
-                        int* groups, int* block, int64_t* max_cols) {
+int softmax_kernel_info(int kernel_id, int* dtype, int* variant, int* causal, int* vec_elems, int* lanes,
+                        int* vecs_per_lane, int* groups, int* block, int64_t* max_cols) {
     const Entry* e = entry_by_id(kernel_id);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
     if (dtype) *dtype = e->dtype;
     if (variant) *variant = e->variant;
+    if (causal) *causal = e->causal ? 1 : 0;
     if (vec_elems) *vec_elems = e->vec;
     if (lanes) *lanes = e->lanes;
     if (vecs_per_lane) *vecs_per_lane = e->vpl;
@@ -299,13 +353,14 @@ const char* softmax_status_string(int status) {
         case SOFTMAX_ERR_BAD_SHAPE: return "bad shape (negative dims, row_stride < cols, cols > 2^30 or extent overflow)";
         case SOFTMAX_ERR_BAD_DTYPE: return "bad dtype (expected 0 = fp32, 1 = fp16, 2 = bf16)";
         case SOFTMAX_ERR_OVERLAP: return "input and output overlap without being equal";
-        case SOFTMAX_ERR_BAD_KERNEL: return "kernel id unknown or unable to take this dtype, width, stride or alignment";
+        case SOFTMAX_ERR_BAD_KERNEL: return "kernel id unknown, of the other kind (plain or causal), or unable to take this dtype, width, stride or alignment";
         case SOFTMAX_ERR_HIP: return "HIP runtime refused the launch";
+        case SOFTMAX_ERR_BAD_SCALE: return "bad scale (must be > 0 with scale * log2(e) below 3e38)";
         default: return "unknown status";
     }
 }
 
-const char* softmax_version(void) { return "row_wise_softmax_amd 0.1.0 (gfx950)"; }
+const char* softmax_version(void) { return "row_wise_softmax_amd 0.2.0 (gfx950)"; }
 
 int softmax_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (bytes < 0 || bytes % 16) return SOFTMAX_ERR_BAD_SHAPE;
@@ -320,7 +375,8 @@ int softmax_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) 
     if (grid > kMaxGrid) grid = kMaxGrid;
     const rws::u32x4* s = static_cast<const rws::u32x4*>(src);
     rws::u32x4* d = static_cast<rws::u32x4*>(dst);
-    void* args[] = {&s, &d, const_cast<int64_t*>(&n)};
+    int64_t nn = n;
+    void* args[] = {&s, &d, &nn};
     hipError_t rc = hipLaunchKernel((const void*)&rws::copy16<kU>, dim3(unsigned(grid)), dim3(256), args, 0,
                                     static_cast<hipStream_t>(stream));
     if (rc != hipSuccess) {

@@ -28,10 +28,12 @@
 //                normalises and writes.
 //
 // Arithmetic (all fp32).  In the single-pass kernels the exponentials are
-// 2^(x*log2(e) - a) with one FMA and v_exp_f32, where a = m * log2(e) rounded
-// to fp32 is the row's "frame".  Every exponential of a row uses the same
-// frame, so the rounding of a cancels in the ratio; only the FMA's own
-// rounding of each argument remains.  A row whose entries are all -inf gets
+// 2^(x*c - a) with one FMA and v_exp_f32, where c = scale * log2(e) (scale 1
+// for the plain softmax) and a = m * c rounded to fp32 is the row's "frame".
+// Every exponential of a row uses the same frame, so the rounding of a
+// cancels in the ratio; only the FMA's own rounding of each argument remains.
+// Rows with a very large max are first rebased (rebase_large_max) so that
+// the rounding of a stays below 1/4.  A row whose entries are all -inf gets
 // frame 0, so every exponential is exp2(-inf) = +0, the sum is 0, the
 // reciprocal is taken as 0 and every output is +0.  The reciprocal of the sum
 // is v_rcp_f32 (about 1 ulp; the sum is at least 1 whenever the row has a
@@ -205,74 +207,83 @@ __device__ inline float group_reduce(float v) {
 }
 
 // Merge of two (max, sum) pairs, each sum taken relative to its own max:
-//   m = max(m1, m2),  s = s1 * e^(m1 - m) + s2 * e^(m2 - m);
-// a max of -inf marks an empty pair (sum 0).
-__device__ inline float exp_diff(float d) { return __builtin_amdgcn_exp2f(d * kLog2e); }
+//   m = max(m1, m2),  s = s1 * e^(c (m1 - m)) + s2 * e^(c (m2 - m)),
+// with c = scale * log2 e applied through exp2; a max of -inf marks an empty
+// pair (sum 0).
+__device__ inline float exp_diff(float d, float coef) { return __builtin_amdgcn_exp2f(d * coef); }
 
-__device__ inline void merge_pair(float& m, float& s, float m2, float s2) {
+__device__ inline void merge_pair(float& m, float& s, float m2, float s2, float coef) {
     float mn = fmaxf(m, m2);
     if (mn == -INFINITY) return;  // both empty
-    s = s * exp_diff(m - mn) + s2 * exp_diff(m2 - mn);
+    s = s * exp_diff(m - mn, coef) + s2 * exp_diff(m2 - mn, coef);
     m = mn;
 }
 
 template <int Ctrl>
-__device__ inline void pair_step_dpp(float& m, float& s) {
-    merge_pair(m, s, dpp<Ctrl>(m), dpp<Ctrl>(s));
+__device__ inline void pair_step_dpp(float& m, float& s, float coef) {
+    merge_pair(m, s, dpp<Ctrl>(m), dpp<Ctrl>(s), coef);
 }
 
 // All-reduce of (max, sum) pairs over a whole wave.
-__device__ inline void wave_reduce_pair(float& m, float& s) {
-    pair_step_dpp<kDppXor1>(m, s);
-    pair_step_dpp<kDppXor2>(m, s);
-    pair_step_dpp<kDppHalfMirror>(m, s);
-    pair_step_dpp<kDppMirror>(m, s);
-    merge_pair(m, s, swap16(m), swap16(s));
+__device__ inline void wave_reduce_pair(float& m, float& s, float coef) {
+    pair_step_dpp<kDppXor1>(m, s, coef);
+    pair_step_dpp<kDppXor2>(m, s, coef);
+    pair_step_dpp<kDppHalfMirror>(m, s, coef);
+    pair_step_dpp<kDppMirror>(m, s, coef);
+    merge_pair(m, s, swap16(m), swap16(s), coef);
     float m_lo = as_f(__builtin_amdgcn_readlane(as_i(m), 0));
     float s_lo = as_f(__builtin_amdgcn_readlane(as_i(s), 0));
     float m_hi = as_f(__builtin_amdgcn_readlane(as_i(m), 32));
     float s_hi = as_f(__builtin_amdgcn_readlane(as_i(s), 32));
-    merge_pair(m_lo, s_lo, m_hi, s_hi);
+    merge_pair(m_lo, s_lo, m_hi, s_hi, coef);
     m = m_lo;
     s = s_lo;
 }
 
-// The row's frame from its max: m * log2 e, or 0 for an all -inf row.
-__device__ inline float frame_of(float m) { return m == -INFINITY ? 0.0f : m * kLog2e; }
+// The row's frame from its max: m * c (c = scale * log2 e), or 0 for an all
+// -inf row.
+__device__ inline float frame_of(float m, float coef) { return m == -INFINITY ? 0.0f : m * coef; }
 
-// The one-FMA form needs m * log2 e finite in fp32, i.e. |m| below about
-// 2.36e38 (reachable in fp32 and bf16 only).
-__device__ inline bool frame_fits(float m) { return fabsf(m) <= 2.0e38f || m == -INFINITY; }
-
-__device__ inline float exp_in_frame(float x, float frame) {
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -frame));
+// exp2(fma(x, c, -frame)) with frame = fl(m c): for x = m the argument is the
+// rounding error of fl(m c), at most ulp(m c) / 2.  It is common to the whole
+// row and cancels in the ratio, but it must stay small: a large one both
+// overflows exp2 and inflates every other argument's own rounding.  Up to
+// |m c| = 2^22 it is at most 0.25.
+constexpr float kFrameLimit = 4194304.0f;  // 2^22
+__device__ inline bool frame_small(float m, float coef) {
+    return m == -INFINITY || fabsf(m * coef) <= kFrameLimit;
 }
 
-// A row whose max m has |m| > 2e38: every other fp32 value of the row is at
-// least ulp(2e38) = 2^104 below m, so its exponential is exactly 0 in fp32 and
-// the softmax is 1/count on the entries equal to m.  Rewriting the row as
-// 0 where x == m and -inf elsewhere (m := 0) gives exactly that through the
-// ordinary path.  The test is a ballot, so common rows pay one scalar branch.
+__device__ inline float exp_in_frame(float x, float coef, float frame) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(x, coef, -frame));
+}
+
+// Rows whose max has |m c| > 2^22 (for scale 1, |m| above about 2.9e6) are
+// rebased in registers, x := x - m and m := 0, before the one-FMA path.  The
+// subtraction is exact for every x within a factor of two of m (the entries
+// whose exponentials matter), x = m becomes exactly 0, and x - m may overflow
+// to -inf only where e^(c (x - m)) is 0 anyway.  The test is a ballot, so
+// ordinary rows pay one scalar branch.
 template <int n>
-__device__ inline void tame_huge_max(float* x, float& m) {
-    if (__builtin_amdgcn_ballot_w64(!frame_fits(m)) != 0) {
-        if (!frame_fits(m)) {
+__device__ inline void rebase_large_max(float* x, float& m, float coef) {
+    if (__builtin_amdgcn_ballot_w64(!frame_small(m, coef)) != 0) {
+        if (!frame_small(m, coef)) {
 #pragma unroll
-            for (int i = 0; i < n; ++i) x[i] = x[i] == m ? 0.0f : -INFINITY;
+            for (int i = 0; i < n; ++i) x[i] = x[i] - m;
             m = 0.0f;
         }
     }
 }
 
-// Replace x[0..n) by its exponentials relative to the row max m (|m| <= 2e38
-// or -inf); returns their sum.
+// Replace x[0..n) by its exponentials relative to the row max m; returns
+// their sum.  Requires frame_small(m, coef) (see rebase_large_max).
 template <int n>
-__device__ inline float exp_and_sum(float* x, float m) {
-    const float fr = frame_of(m);
+__device__ inline float exp_and_sum(float* x, float m, float coef) {
+    const float fr = frame_of(m, coef);
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-        x[i] = exp_in_frame(x[i], fr);
+        x[i] = exp_in_frame(x[i], coef, fr);
         s += x[i];
     }
     return s;
@@ -289,15 +300,62 @@ struct Args {
     int64_t rows;
     int64_t stride;   // row stride in accesses (elements / access width)
     int64_t nblocks;  // logical workgroups; the grid may be smaller and loop
+    int64_t diag;     // causal kernels: row i keeps columns j <= i + diag
     int nacc;         // accesses per row (cols / access width)
+    int cols;         // elements per row
+    float coef;       // scale * log2(e); log2(e) for the plain softmax
 };
+
+// Columns row `row` keeps: all of them, or j <= row + diag for the causal
+// (scaled, masked) softmax of "Dissecting Memory Bandwidth & SRAM Tiling in
+// Triton", section "Writing the Kernel in OpenAI Triton".  No sum can overflow.
+template <bool Causal>
+__device__ inline int kept_cols(int64_t row, const Args& a) {
+    if constexpr (!Causal) {
+        return a.cols;
+    } else {
+        if (a.diag >= a.cols) return a.cols;
+        if (a.diag < -row) return 0;
+        const int64_t k = row + a.diag + 1;
+        return k > a.cols ? a.cols : int(k);
+    }
+}
+
+// Load access `idx` of a row into f, or -inf where the row has nothing to
+// give: past its end, or (causal) past its kept columns.  A causal access
+// wholly past the kept columns is not read at all; the one that straddles
+// them is read and its masked elements set to -inf.
+template <class E, int N, bool Causal, bool Keep = false>
+__device__ inline void load_access(const typename Access<E, N>::raw* p, int idx, int nacc, int kept, float* f) {
+    if constexpr (!Causal) {
+        if (idx < nacc) {
+            load_elems<E, N, Keep>(p, f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < N; ++e) f[e] = -INFINITY;
+        }
+    } else {
+        const int first = idx * N;
+        if (first < kept) {
+            load_elems<E, N, Keep>(p, f);
+            if (first + N > kept) {
+#pragma unroll
+                for (int e = 0; e < N; ++e)
+                    if (first + e >= kept) f[e] = -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < N; ++e) f[e] = -INFINITY;
+        }
+    }
+}
 
 // ------------------------------------------------------------ packed kernel
 //
 // Lane l of a group of L lanes owns accesses l, l + L, l + 2L, ... of its row,
 // so one load instruction of a wave reads 64 consecutive 16-byte chunks: the
 // rows of a group are adjacent when the row stride equals the width.
-template <class E, int N, int L, int V, int G>
+template <class E, int N, int L, int V, int G, bool Causal>
 __global__ void __launch_bounds__(256) softmax_packed(Args a) {
     typedef typename Access<E, N>::raw raw;
     constexpr int kRowsPerGroup = kWave / L;
@@ -316,16 +374,11 @@ __global__ void __launch_bounds__(256) softmax_packed(Args a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t row = row0 + g * kRowsPerGroup;
+            const bool live = row < a.rows;
+            const int kept = live ? kept_cols<Causal>(row, a) : 0;
             const raw* p = in + row * a.stride + l;
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                if (row < a.rows && v * L + l < a.nacc) {
-                    load_elems<E, N>(p + v * L, x[g][v]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < N; ++e) x[g][v][e] = -INFINITY;
-                }
-            }
+            for (int v = 0; v < V; ++v) load_access<E, N, Causal>(p + v * L, v * L + l, live ? a.nacc : 0, kept, x[g][v]);
         }
         float mx[G], r[G];
 #pragma unroll
@@ -339,8 +392,8 @@ __global__ void __launch_bounds__(256) softmax_packed(Args a) {
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            tame_huge_max<V * N>(&x[g][0][0], mx[g]);
-            const float s = exp_and_sum<V * N>(&x[g][0][0], mx[g]);
+            rebase_large_max<V * N>(&x[g][0][0], mx[g], a.coef);
+            const float s = exp_and_sum<V * N>(&x[g][0][0], mx[g], a.coef);
             r[g] = recip_sum(group_reduce<L, OpSum>(s));
         }
 #pragma unroll
@@ -366,18 +419,12 @@ __global__ void __launch_bounds__(256) softmax_packed(Args a) {
 // store.  Two barriers per row: after the per-wave maxima reach LDS and after
 // the per-wave sums do (separate slots, so no third barrier guards reuse).
 
-template <class E, int N, int W, int V>
-__device__ inline void load_row(const typename Access<E, N>::raw* p, int t, int nacc, float (&x)[V][N]) {
+template <class E, int N, int W, int V, bool Causal>
+__device__ inline void load_row(const typename Access<E, N>::raw* p, int t, int nacc, int kept,
+                                float (&x)[V][N]) {
     constexpr int kThreads = W * kWave;
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-        if (v * kThreads + t < nacc) {
-            load_elems<E, N>(p + v * kThreads, x[v]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < N; ++e) x[v][e] = -INFINITY;
-        }
-    }
+    for (int v = 0; v < V; ++v) load_access<E, N, Causal>(p + v * kThreads, v * kThreads + t, nacc, kept, x[v]);
 }
 
 // Max, exponentials, sum and the normalised store of one row held in x.
@@ -386,7 +433,7 @@ __device__ inline void load_row(const typename Access<E, N>::raw* p, int t, int 
 // red_sum before the next call's first barrier, so the slots can be reused
 // without a third barrier.
 template <class E, int N, int W, int V>
-__device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* q, int t, int nacc,
+__device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* q, int t, int nacc, float coef,
                                   float* red_max, float* red_sum) {
     constexpr int kThreads = W * kWave;
     const int lane = t & (kWave - 1);
@@ -405,8 +452,8 @@ __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* 
         for (int w = 1; w < W; ++w) m = fmaxf(m, red_max[w]);
     }
 
-    tame_huge_max<V * N>(&x[0][0], m);
-    float s = exp_and_sum<V * N>(&x[0][0], m);
+    rebase_large_max<V * N>(&x[0][0], m, coef);
+    float s = exp_and_sum<V * N>(&x[0][0], m, coef);
     s = group_reduce<kWave, OpSum>(s);
     if (W > 1) {
         if (lane == 0) red_sum[wave] = s;
@@ -427,7 +474,7 @@ __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* 
     }
 }
 
-template <class E, int N, int W, int V>
+template <class E, int N, int W, int V, bool Causal>
 __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
     typedef typename Access<E, N>::raw raw;
     __shared__ float red_max[W];
@@ -437,8 +484,8 @@ __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
     const int t = threadIdx.x;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         float x[V][N];
-        load_row<E, N, W, V>(in + row * a.stride + t, t, a.nacc, x);
-        finish_row<E, N, W, V>(x, out + row * a.stride + t, t, a.nacc, red_max, red_sum);
+        load_row<E, N, W, V, Causal>(in + row * a.stride + t, t, a.nacc, kept_cols<Causal>(row, a), x);
+        finish_row<E, N, W, V>(x, out + row * a.stride + t, t, a.nacc, a.coef, red_max, red_sum);
     }
 }
 
@@ -449,7 +496,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
 // before the current row is reduced, so its HBM reads overlap the current
 // row's reductions, exponentials and stores.  The grid is sized to the
 // number of workgroups the chip holds at once.
-template <class E, int N, int W, int V>
+template <class E, int N, int W, int V, bool Causal>
 __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
     typedef typename Access<E, N>::raw raw;
     __shared__ float red_max[W];
@@ -460,7 +507,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
     int64_t row = blockIdx.x;
     if (row >= a.rows) return;  // uniform per workgroup: no barrier is skipped by part of it
     float nx[V][N];
-    load_row<E, N, W, V>(in + row * a.stride + t, t, a.nacc, nx);
+    load_row<E, N, W, V, Causal>(in + row * a.stride + t, t, a.nacc, kept_cols<Causal>(row, a), nx);
     for (; row < a.rows; row += gridDim.x) {
         float x[V][N];
 #pragma unroll
@@ -468,8 +515,9 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
 #pragma unroll
             for (int e = 0; e < N; ++e) x[v][e] = nx[v][e];
         const int64_t next = row + gridDim.x;
-        if (next < a.rows) load_row<E, N, W, V>(in + next * a.stride + t, t, a.nacc, nx);
-        finish_row<E, N, W, V>(x, out + row * a.stride + t, t, a.nacc, red_max, red_sum);
+        if (next < a.rows)
+            load_row<E, N, W, V, Causal>(in + next * a.stride + t, t, a.nacc, kept_cols<Causal>(next, a), nx);
+        finish_row<E, N, W, V>(x, out + row * a.stride + t, t, a.nacc, a.coef, red_max, red_sum);
     }
 }
 
@@ -481,12 +529,13 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
 // adds the chunk's exponentials.  The per-lane (max, sum) pairs are merged
 // across the wave and then across waves through LDS.  Pass 2 re-reads the
 // row and writes e^(x - m) / sum.  Traffic: two reads and one write per
-// element (the second read may hit L2 or the Infinity Cache).
+// element (the second read may hit L2 or the Infinity Cache); a causal row
+// reads only its kept columns, twice.
 //
-// Exponentials here are 2^((x - m) log2 e), two operations: each lane's sum is
+// Exponentials here are 2^((x - m) c), two operations: each lane's sum is
 // relative to that lane's own max, and the subtraction keeps the terms of
 // different lanes and both passes consistent without a shared frame.
-template <class E, int N, int W, int V>
+template <class E, int N, int W, int V, bool Causal>
 __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
     typedef typename Access<E, N>::raw raw;
     constexpr int kThreads = W * kWave;
@@ -498,22 +547,20 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
+    const float coef = a.coef;
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const raw* p = in + row * a.stride + t;
+        const int kept = kept_cols<Causal>(row, a);
+        // accesses that hold at least one kept column
+        const int nread = Causal ? (kept + N - 1) / N : a.nacc;
         float lm = -INFINITY;  // lane running max; -inf: nothing finite seen yet
-        float ls = 0.0f;       // lane sum of e^(x - lm)
-        for (int c = 0; c < a.nacc; c += kChunk) {
+        float ls = 0.0f;       // lane sum of e^(c (x - lm))
+        for (int c = 0; c < nread; c += kChunk) {
             float x[V][N];
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                if (c + v * kThreads + t < a.nacc) {
-                    load_elems<E, N, true>(p + c + v * kThreads, x[v]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < N; ++e) x[v][e] = -INFINITY;
-                }
-            }
+            for (int v = 0; v < V; ++v)
+                load_access<E, N, Causal, true>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, kept, x[v]);
             float cm = x[0][0];
 #pragma unroll
             for (int v = 0; v < V; ++v)
@@ -521,17 +568,17 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
                 for (int e = 0; e < N; ++e) cm = fmaxf(cm, x[v][e]);
             if (cm == -INFINITY) continue;  // nothing finite in this chunk for this lane
             if (cm > lm) {
-                ls *= exp_diff(lm - cm);  // lm = -inf: 0 * 0
+                ls *= exp_diff(lm - cm, coef);  // lm = -inf: 0 * 0
                 lm = cm;
             }
             float s = 0.0f;
 #pragma unroll
             for (int v = 0; v < V; ++v)
 #pragma unroll
-                for (int e = 0; e < N; ++e) s += exp_diff(x[v][e] - lm);
+                for (int e = 0; e < N; ++e) s += exp_diff(x[v][e] - lm, coef);
             ls += s;
         }
-        wave_reduce_pair(lm, ls);
+        wave_reduce_pair(lm, ls, coef);
         if (lane == 0) {
             red_m[wave] = lm;
             red_s[wave] = ls;
@@ -540,7 +587,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
         lm = red_m[0];
         ls = red_s[0];
 #pragma unroll
-        for (int w = 1; w < W; ++w) merge_pair(lm, ls, red_m[w], red_s[w]);
+        for (int w = 1; w < W; ++w) merge_pair(lm, ls, red_m[w], red_s[w], coef);
         const float m = lm == -INFINITY ? 0.0f : lm;  // all -inf row: every term exp(-inf) = 0
         const float r = recip_sum(ls);
 
@@ -549,12 +596,12 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
             float x[V][N];
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                if (c + v * kThreads + t < a.nacc) load_elems<E, N>(p + c + v * kThreads, x[v]);
+                load_access<E, N, Causal>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, kept, x[v]);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 if (c + v * kThreads + t < a.nacc) {
 #pragma unroll
-                    for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m) * r;
+                    for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m, coef) * r;
                     store_elems<E, N>(q + c + v * kThreads, x[v]);
                 }
             }

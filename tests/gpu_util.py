@@ -49,8 +49,12 @@ def sentinel(dtype: str):
 
 
 def run(x: np.ndarray, dtype: str, cols: int | None = None, kernel_id: int | None = None,
-        inplace: bool = False, prefill_out: bool = True):
-    """Run the library on host array x (shape rows x row_stride); return the raw output (host)."""
+        inplace: bool = False, prefill_out: bool = True, causal: bool = False, scale: float = 1.0,
+        diag: int = 0):
+    """Run the library on host array x (shape rows x row_stride); return the raw output (host).
+
+    causal=True calls the scaled, causally masked entry points (row i keeps
+    columns j <= i + diag, kept entries multiplied by scale)."""
     import torch
     rows, stride = x.shape
     cols = stride if cols is None else cols
@@ -63,7 +67,12 @@ def run(x: np.ndarray, dtype: str, cols: int | None = None, kernel_id: int | Non
         out = torch.empty_like(xd)
     stream = torch.cuda.current_stream().cuda_stream
     code = W.dtype_code(dtype)
-    if kernel_id is None:
+    if causal and kernel_id is None:
+        binding.softmax_fwd_causal(xd.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag, code, stream)
+    elif causal:
+        binding.softmax_fwd_causal_kernel(kernel_id, xd.data_ptr(), out.data_ptr(), rows, cols, stride, scale,
+                                          diag, code, stream)
+    elif kernel_id is None:
         binding.softmax_fwd(xd.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
     else:
         binding.softmax_fwd_kernel(kernel_id, xd.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
@@ -71,12 +80,25 @@ def run(x: np.ndarray, dtype: str, cols: int | None = None, kernel_id: int | Non
     return to_host(out, dtype)
 
 
+def causal_mask(rows: int, cols: int, diag: int) -> np.ndarray:
+    """True where row i keeps column j (j <= i + diag)."""
+    i = np.arange(rows, dtype=np.int64)[:, None]
+    j = np.arange(cols, dtype=np.int64)[None, :]
+    return j - i <= diag
+
+
 def check(y_raw: np.ndarray, x: np.ndarray, dtype: str, ref: np.ndarray, cols: int | None = None,
-          label: str = "") -> float:
-    """Compare the raw GPU output with the oracle's float64 result; returns max abs error."""
+          label: str = "", keep: np.ndarray | None = None) -> float:
+    """Compare the raw GPU output with the oracle's float64 result; returns max abs error.
+
+    ``keep`` (causal calls) marks the kept columns: masked ones count as -inf
+    inputs (exact 0 expected), and row sums are taken over rows that keep a
+    finite entry."""
     cols = x.shape[1] if cols is None else cols
     y = decode(np.ascontiguousarray(y_raw[:, :cols]), dtype)
     xin = decode(np.ascontiguousarray(x[:, :cols]), dtype)
+    if keep is not None:
+        xin = np.where(keep, xin, -np.inf)
     finite_rows = np.isfinite(xin).any(axis=1)
     assert not np.isnan(y).any(), f"{label}: NaN in output"
     assert np.isfinite(y[finite_rows]).all(), f"{label}: Inf in output"

@@ -29,6 +29,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
     for want in ("softmax_fwd", "softmax_fwd_kernel", "softmax_select", "softmax_num_kernels",
+                 "softmax_fwd_causal", "softmax_fwd_causal_kernel", "softmax_select_causal",
                  "softmax_kernel_info", "softmax_kernel_name", "softmax_kernel_fits",
                  "softmax_status_string", "softmax_version", "softmax_bench_copy"):
         assert want in names
@@ -47,8 +48,8 @@ def test_library_is_built_for_gfx950():
 
 def test_version_and_status_strings(lib):
     assert "gfx950" in binding.version()
-    for st in range(7):
-        assert lib.softmax_status_string(st)
+    for st in range(8):
+        assert lib.softmax_status_string(st) != b"unknown status"
     assert lib.softmax_status_string(99) == b"unknown status"
 
 
@@ -56,8 +57,9 @@ def _fwd(lib, in_ptr, out_ptr, rows, cols, stride, dtype):
     return lib.softmax_fwd(in_ptr, out_ptr, rows, cols, stride, dtype, None)
 
 
-# Host addresses only: every case below is rejected (or is empty) before the
-# library touches the device, so no address is ever dereferenced.
+# Host addresses only: every case in this file is rejected (or is empty)
+# before the library touches the device, so no address is ever dereferenced
+# and no kernel is launched.
 A, B = 0x100000, 0x900000
 
 
@@ -81,17 +83,38 @@ def test_argument_errors_before_any_launch(lib, args, status):
     assert _fwd(lib, *args) == status
 
 
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan"), 3e38])
+def test_causal_bad_scale(lib, scale):
+    assert lib.softmax_fwd_causal(A, B, 4, 8, 8, scale, 0, 0, None) == 7
+
+
+def test_causal_argument_errors(lib):
+    assert lib.softmax_fwd_causal(A, B, 4, 8, 7, 1.0, 0, 0, None) == 2      # row_stride < cols
+    assert lib.softmax_fwd_causal(0, B, 4, 8, 8, 1.0, 0, 0, None) == 1      # null
+    assert lib.softmax_fwd_causal(A, B, 4, 8, 8, 1.0, 0, 9, None) == 3      # dtype
+    assert lib.softmax_fwd_causal(A, A + 4, 4, 8, 8, 1.0, 0, 0, None) == 4  # overlap
+    assert lib.softmax_fwd_causal(A, B, 0, 8, 8, 1.0, 0, 0, None) == 0      # empty: nothing launched
+
+
+def test_plain_and_causal_entries_are_not_interchangeable(lib):
+    table = binding.kernel_table()
+    plain = next(k for k in table if k.dtype == 0 and not k.causal and k.variant == "online")
+    causal = next(k for k in table if k.dtype == 0 and k.causal and k.variant == "online")
+    assert lib.softmax_fwd_kernel(causal.kid, A, B, 4, 8, 8, 0, None) == 5
+    assert lib.softmax_fwd_causal_kernel(plain.kid, A, B, 4, 8, 8, 1.0, 0, 0, None) == 5
+
+
 def test_forced_kernel_errors(lib):
     n = lib.softmax_num_kernels()
     assert n > 100
     assert lib.softmax_fwd_kernel(-1, A, B, 4, 8, 8, 0, None) == 5
     assert lib.softmax_fwd_kernel(n, A, B, 4, 8, 8, 0, None) == 5
     table = binding.kernel_table()
-    f16 = next(k for k in table if k.dtype == 1)
+    f16 = next(k for k in table if k.dtype == 1 and not k.causal)
     assert lib.softmax_fwd_kernel(f16.kid, A, B, 4, 8, 8, 0, None) == 5  # wrong dtype
-    narrow = next(k for k in table if k.dtype == 0 and k.max_cols == 4)
+    narrow = next(k for k in table if k.dtype == 0 and k.max_cols == 4 and not k.causal)
     assert lib.softmax_fwd_kernel(narrow.kid, A, B, 4, 8, 8, 0, None) == 5  # too wide
-    vec = next(k for k in table if k.dtype == 0 and k.vec_elems == 4)
+    vec = next(k for k in table if k.dtype == 0 and k.vec_elems == 4 and not k.causal)
     assert lib.softmax_fwd_kernel(vec.kid, A + 4, B, 4, 8, 8, 0, None) == 5  # misaligned
 
 
@@ -101,6 +124,7 @@ def test_kernel_table_is_consistent(lib):
     assert len(set(names)) == len(names)
     for k in table:
         assert k.variant in ("packed", "row", "row_pf", "online")
+        assert k.name.startswith("causal_") == k.causal
         assert k.dtype in (0, 1, 2)
         if k.variant == "online":
             assert k.max_cols == -1
@@ -108,24 +132,28 @@ def test_kernel_table_is_consistent(lib):
             assert k.max_cols == k.lanes * k.vecs_per_lane * k.vec_elems
         if k.vec_elems > 1:
             assert k.vec_elems * (4 if k.dtype == 0 else 2) == 16
-    # every dtype has the scalar (any-alignment) path
+    # every dtype has the scalar (any-alignment) path, plain and causal
     for dt in (0, 1, 2):
-        assert any(k.dtype == dt and k.vec_elems == 1 for k in table)
+        for c in (False, True):
+            assert any(k.dtype == dt and k.vec_elems == 1 and k.causal == c for k in table)
 
 
 @pytest.mark.parametrize("dtype", [0, 1, 2])
 @pytest.mark.parametrize("cols", [1, 3, 8, 32, 64, 100, 256, 1000, 1001, 2048, 3000, 4096, 8192,
                                   16384, 32768, 65536, 131072, 1 << 18])
-def test_dispatch_always_picks_a_fitting_kernel(lib, dtype, cols):
-    kid = binding.softmax_select(A, B, cols, cols, dtype, rows=4)
+@pytest.mark.parametrize("causal", [False, True])
+def test_dispatch_always_picks_a_fitting_kernel(lib, dtype, cols, causal):
+    kid = binding.softmax_select(A, B, cols, cols, dtype, rows=4, causal=causal)
     assert binding.kernel_fits(kid, A, B, cols, cols, dtype)
     info = binding.kernel_table()[kid]
+    assert info.causal == causal
     esz = 4 if dtype == 0 else 2
     if (cols * esz) % 16 == 0:
         assert info.vec_elems * esz == 16, "aligned rows must take 16-byte accesses"
     # misaligned pointers fall back to the scalar path
-    kid2 = binding.softmax_select(A + 2, B + 2, cols, cols, dtype, rows=4)
+    kid2 = binding.softmax_select(A + 2, B + 2, cols, cols, dtype, rows=4, causal=causal)
     assert binding.kernel_table()[kid2].vec_elems == 1
+    assert binding.kernel_table()[kid2].causal == causal
 
 
 def test_bench_copy_argument_errors(lib):

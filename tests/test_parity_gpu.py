@@ -14,7 +14,7 @@ from oracle import oracle as O
 from row_wise_softmax_amd import binding
 from row_wise_softmax_amd import workloads as W
 
-from gpu_util import TOL, check, check_padding_untouched, decode, run, to_device, to_host
+from gpu_util import TOL, causal_mask, check, check_padding_untouched, decode, run, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -252,5 +252,57 @@ def test_every_kernel_in_the_table(kid):
         _say(f"{k.name} rows={rows} cols={cols}")
         x = W.random_matrix(seed=kid, rows=rows, cols=cols, dtype=dtype, sigma=3.0)
         x[1, : max(1, cols // 3)] = W.neg_inf(dtype)  # a partly masked row
-        y = run(x, dtype, kernel_id=kid)
-        check(y, x, dtype, O.softmax(x, dtype), label=f"{k.name} cols={cols}")
+        if k.causal:
+            # a diagonal that leaves some rows empty, some partial, some full
+            diag = cols // 2 - rows // 2
+            y = run(x, dtype, kernel_id=kid, causal=True, scale=0.375, diag=diag)
+            check(y, x, dtype, O.softmax_causal(x, dtype, 0.375, diag), label=f"{k.name} cols={cols}",
+                  keep=causal_mask(rows, cols, diag))
+        else:
+            y = run(x, dtype, kernel_id=kid)
+            check(y, x, dtype, O.softmax(x, dtype), label=f"{k.name} cols={cols}")
+
+
+# ------------------------------------------- magnitudes x kernel families
+
+_MAGNITUDES = [1e3, 1e5, 3e6, 1e7, 1e9, 3e9, 1e12, 1e20, 1e30, 1e37, 3e38]
+_FAMILIES = ["packed_{d}_l64_v2_g1", "row_{d}_w4_v2", "rowpf_{d}_w4_v2", "online_{d}_vec_w4_v2",
+             "online_{d}_scalar_w4_v8"]
+_CAUSAL_FAMILIES = ["causal_packed_{d}_l64_v2_g1", "causal_row_{d}_w4_v2", "causal_online_{d}_vec_w16_v4",
+                    "causal_online_{d}_scalar_w4_v8"]
+
+
+def _magnitude_rows(dtype, cols=512, seed=51):
+    """Rows whose max spans 1e3 .. 3e38 (clipped to the type), both signs,
+    entries a few units in the last place apart, some mixed with ordinary values."""
+    top = {"f32": 3.3e38, "bf16": 3.3e38, "f16": 6.0e4}[dtype]
+    rng = np.random.default_rng(seed)
+    rows = []
+    for mag in _MAGNITUDES:
+        mag = min(mag, top)
+        for sign in (1.0, -1.0):
+            base = np.float64(np.float32(sign * mag))
+            ulp = float(np.spacing(np.float32(abs(base)))) * (2 ** 16 if dtype != "f32" else 1)
+            rows.append(base + rng.integers(-40, 1, size=cols) * ulp)   # a cluster just below the max
+            mixed = rng.standard_normal(cols) * 3.0
+            mixed[rng.integers(0, cols, size=3)] = base
+            rows.append(mixed)                                          # ordinary values and a few huge ones
+    x = W.cast(np.clip(np.array(rows), -top, top), dtype)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("family", _FAMILIES + _CAUSAL_FAMILIES)
+def test_magnitudes_every_family(dtype, family):
+    name = family.format(d=dtype)
+    k = next((k for k in _TABLE if k.name == name), None)
+    assert k is not None, f"no table entry {name}"
+    x = _magnitude_rows(dtype)
+    rows, cols = x.shape
+    _say(f"magnitudes {name} rows={rows}")
+    if k.causal:
+        y = run(x, dtype, kernel_id=k.kid, causal=True, scale=0.75, diag=cols)
+        check(y, x, dtype, O.softmax_causal(x, dtype, 0.75, cols), label=name)
+    else:
+        y = run(x, dtype, kernel_id=k.kid)
+        check(y, x, dtype, O.softmax(x, dtype), label=name)
