@@ -109,9 +109,10 @@ int pow2_at_least(int64_t v) {
 }
 
 // The width dispatch rule, set from the width sweep (bench.py --sweep, bf16
-// and fp32, widths 32 ... 16384 at about 200 MB per tensor): the fastest shape
-// at every width keeps about two 16-byte loads in flight per lane and spreads
-// a row over as many lanes as that takes.  `nacc` is the row length in
+// and fp32, widths 32 ... 16384 at about 200 MB per tensor): up to 1024
+// 16-byte accesses per row the fastest shape keeps about two loads in flight
+// per lane and spreads the row over as many lanes as that takes; wider rows
+// do best on four waves with more loads each.  `nacc` is the row length in
 // 16-byte accesses.  The causal table holds the same picks.
 const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype,
                           bool causal) {
@@ -124,16 +125,18 @@ const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t
             e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, pow2_at_least(nacc), 1, 2);
         } else if (nacc <= 128) {
             e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1);
+        } else if (nacc <= 1024) {
+            // one workgroup per row, two accesses per lane, up to 8 waves
+            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
         } else {
-            // one workgroup per row, two accesses per lane, up to 16 waves;
-            // wider rows keep 16 waves and take more accesses per lane
-            int v = 2;
-            int w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
-            while (w > 16 && v < 16) {
-                v *= 2;
-                w = pow2_at_least((nacc + 64 * v - 1) / (64 * v));
+            // wider rows: four waves with more accesses each (8192 fp32 and
+            // 16384 bf16 columns ran 4-5% faster this way than spread over
+            // 16 waves); where the table has no such shape, 8 or 16 waves
+            const int v4 = pow2_at_least((nacc + 255) / 256);
+            for (int w = 4; w <= 16 && e == nullptr; w *= 2) {
+                const int v = v4 * 4 / w;
+                if (v >= 1) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * w, v, 1);
             }
-            if (w <= 16) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * w, v, 1);
             if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, 4, 1);
         }
         if (e && fits(*e, in, out, cols, row_stride, dtype)) return e;
