@@ -155,7 +155,7 @@ def kernel_name(res: Resident) -> str:
     return binding.kernel_table()[kid].name
 
 
-def measure_shape(key: str, steps: int, warmup: int, with_copy: bool) -> dict:
+def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfused: bool = False) -> dict:
     wl = W.WORKLOADS[key]
     log(f"[bench] {wl.name}: generating and uploading")
     res = Resident(wl)
@@ -164,6 +164,16 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool) -> dict:
     d = {"workload": wl.name, "rows": wl.rows, "cols": wl.cols, "dtype": wl.dtype,
          "kernel": kernel_name(res), "buffers": res.n, "us": round(ms * 1e3, 3),
          "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
+    if with_unfused:
+        import torch
+        nbytes = binding.unfused_workspace_bytes(wl.rows, wl.cols, res.code)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ums = time_launches(lambda i: binding.unfused_5op(res.ins[i].data_ptr(), res.outs[i].data_ptr(), wl.rows,
+                                                           wl.cols, wl.cols, res.code, ws.data_ptr(), nbytes,
+                                                           res.stream), res.n, steps, warmup)
+        d["unfused_5op_us"] = round(ums * 1e3, 3)
+        d["fused_speedup_over_unfused"] = round(ums / ms, 3)
+        del ws
     if with_copy:
         cms = time_launches(res.copy, res.n, steps, warmup)
         mms = time_launches(res.memcpy, res.n, steps, warmup)
@@ -171,7 +181,8 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool) -> dict:
         d["memcpy_gbps"] = round(wl.bytes / (mms * 1e-3) / 1e9, 1)
         d["frac_of_copy"] = round(gbps / d["copy_kernel_gbps"], 4)
     log(f"[bench] {wl.name}: {d['us']} us  {d['gbps']} GB/s  ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
-        f"  kernel={d['kernel']}")
+        f"  kernel={d['kernel']}" + (f"  unfused 5-op {d['unfused_5op_us']} us ({d['fused_speedup_over_unfused']}x)"
+                                     if "unfused_5op_us" in d else ""))
     d["_res"] = res
     return d
 
@@ -399,7 +410,7 @@ def main() -> int:
         keys = [HEADLINE] + keys
     shapes = {}
     for key in keys:
-        shapes[key] = measure_shape(key, args.steps, args.warmup, with_copy=True)
+        shapes[key] = measure_shape(key, args.steps, args.warmup, with_copy=True, with_unfused=key in ("c3", "c4"))
         if key != HEADLINE:
             del shapes[key]["_res"]  # free its buffers before the next shape
     if args.only is None:

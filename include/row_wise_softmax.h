@@ -183,6 +183,33 @@ const char *softmax_version(void);
  */
 int softmax_bench_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
+/*
+ * ---- Measurement baseline: the unfused five-operation softmax ----
+ *
+ * The same softmax computed as five separate kernels, each a round trip
+ * through HBM: m = rowmax(x); z = x - m; num = exp(z); s = rowsum(num);
+ * y = num / s -- the naive form of "GPU Kernels - Implementing and optimizing
+ * Softmax" (section "Baseline & Triton Softmax kernel"), whose traffic
+ * "Kernel Fusion" (section "Where the time goes in an elementwise chain")
+ * counts as five reads and three writes of the tensor.  It exists so the
+ * benchmark can measure what fusion saves on this machine; it is not a path
+ * of softmax_fwd.  z and num are stored in the element type, m and s in fp32.
+ *
+ * softmax_unfused_workspace_bytes -- bytes of device workspace the baseline
+ * needs for rows x cols of `dtype` (z, num, m, s), or -1 for bad arguments.
+ *
+ * softmax_unfused_5op -- runs the five kernels on `stream`.  Same layout and
+ * aliasing rules as softmax_fwd (in == out allowed); `workspace` is caller-
+ * owned device memory of at least the size above, 256-byte aligned and
+ * disjoint from in and out.  Requires 16-byte-aligned in/out, and row_stride
+ * and cols that are whole 16-byte accesses (else SOFTMAX_ERR_BAD_SHAPE, as for
+ * a short workspace).  Rows with no finite entry give NaN, as the five
+ * separate operations do.
+ */
+int64_t softmax_unfused_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+int softmax_unfused_5op(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                        void *workspace, int64_t workspace_size, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

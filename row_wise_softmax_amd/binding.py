@@ -76,6 +76,10 @@ def _load():
     lib.softmax_version.argtypes = []
     lib.softmax_bench_copy.restype = i32
     lib.softmax_bench_copy.argtypes = [vp, vp, i64, vp]
+    lib.softmax_unfused_workspace_bytes.restype = i64
+    lib.softmax_unfused_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.softmax_unfused_5op.restype = i32
+    lib.softmax_unfused_5op.argtypes = [vp, vp, i64, i64, i64, i32, vp, i64, vp]
     _lib = lib
     return lib
 
@@ -133,6 +137,18 @@ def bench_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None
     """Plain 16-byte-vector device copy (the achievable-bandwidth reference)."""
     lib = _load()
     _check(lib.softmax_bench_copy(src_ptr, dst_ptr, nbytes, stream), "softmax_bench_copy")
+
+
+def unfused_workspace_bytes(rows: int, cols: int, dtype: int) -> int:
+    return int(_load().softmax_unfused_workspace_bytes(rows, cols, dtype))
+
+
+def unfused_5op(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int, dtype: int,
+                workspace_ptr: int, workspace_size: int, stream: int = 0) -> None:
+    """The unfused five-kernel softmax (measurement baseline); needs a caller workspace."""
+    lib = _load()
+    _check(lib.softmax_unfused_5op(in_ptr, out_ptr, rows, cols, row_stride, dtype, workspace_ptr,
+                                   workspace_size, stream), "softmax_unfused_5op")
 
 
 @dataclass(frozen=True)

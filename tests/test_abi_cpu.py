@@ -162,3 +162,20 @@ def test_bench_copy_argument_errors(lib):
     assert lib.softmax_bench_copy(0, B, 16, None) == 1
     assert lib.softmax_bench_copy(A, A + 16, 64, None) == 4
     assert lib.softmax_bench_copy(A, B, 0, None) == 0
+
+
+def test_unfused_baseline_argument_errors(lib):
+    ws = binding.unfused_workspace_bytes(4, 8, 0)
+    assert ws > 2 * 4 * 8 * 4
+    assert binding.unfused_workspace_bytes(-1, 8, 0) == -1
+    assert binding.unfused_workspace_bytes(4, 8, 9) == -1
+    W = 0x4000000  # host address, 256-byte aligned, never dereferenced
+    assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 0, W, ws - 1, None) == 2      # short workspace
+    assert lib.softmax_unfused_5op(A + 4, B, 4, 8, 8, 0, W, ws, None) == 2      # misaligned input
+    assert lib.softmax_unfused_5op(A, B, 4, 7, 7, 0, W, ws, None) == 2          # not whole 16-byte accesses
+    assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 0, W + 16, ws, None) == 2     # workspace not 256-aligned
+    assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 0, 0, ws, None) == 1          # null workspace
+    assert lib.softmax_unfused_5op(A, A + 16, 4, 8, 8, 0, W, ws, None) == 4     # in/out overlap
+    assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 0, A, ws, None) == 4          # workspace overlaps input
+    assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 5, W, ws, None) == 3          # dtype
+    assert lib.softmax_unfused_5op(A, B, 0, 8, 8, 0, W, ws, None) == 0          # empty

@@ -1,0 +1,54 @@
+"""GPU parity of the unfused five-kernel baseline against the CPU oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from row_wise_softmax_amd import binding
+from row_wise_softmax_amd import workloads as W
+
+from gpu_util import check, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    binding._load()
+
+
+def _run_unfused(x, dtype, inplace=False):
+    import torch
+    rows, cols = x.shape
+    code = W.dtype_code(dtype)
+    xd = to_device(x, dtype)
+    out = xd if inplace else torch.empty_like(xd)
+    nbytes = binding.unfused_workspace_bytes(rows, cols, code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    binding.unfused_5op(xd.data_ptr(), out.data_ptr(), rows, cols, cols, code, ws.data_ptr(), nbytes,
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return to_host(out, dtype)
+
+
+@pytest.mark.parametrize("key,rows", [("c3", 2048), ("c4", 1024), ("c1", 128), ("c2", 512)])
+def test_unfused_matches_the_oracle(key, rows):
+    wl = W.WORKLOADS[key]
+    x = wl.generate(rows=rows)
+    print(f"[gpu-case] unfused {wl.name} rows={rows}", file=sys.stderr, flush=True)
+    y = _run_unfused(x, wl.dtype)
+    check(y, x, wl.dtype, O.softmax(x, wl.dtype), label=f"unfused {key}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cols", [8, 256, 1000, 4096, 16384])
+def test_unfused_widths(dtype, cols):
+    x = W.random_matrix(seed=61, rows=33, cols=cols, dtype=dtype, sigma=2.0)
+    if (cols * (4 if dtype == "f32" else 2)) % 16:
+        pytest.skip("the baseline takes whole 16-byte accesses only")
+    y = _run_unfused(x, dtype, inplace=(cols == 256))
+    check(y, x, dtype, O.softmax(x, dtype), label=f"unfused {dtype} {cols}")
