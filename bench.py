@@ -149,6 +149,32 @@ def causal_c2(steps: int, warmup: int) -> dict:
     return d
 
 
+def split_shapes(steps: int, warmup: int) -> dict:
+    """Few, wide rows: softmax_fwd (one workgroup per row) vs the split-row path."""
+    import torch
+    out = {}
+    for key in ("wide_f32", "wide_bf16"):
+        wl = W.WORKLOADS[key]
+        res = Resident(wl)
+        nbytes = binding.split_workspace_bytes(wl.rows, wl.cols, res.code)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        one = time_launches(res.softmax, res.n, steps, warmup)
+        spl = time_launches(lambda i: binding.softmax_fwd_split(res.ins[i].data_ptr(), res.outs[i].data_ptr(), wl.rows,
+                                                                 wl.cols, wl.cols, res.code, ws.data_ptr(), nbytes, 1,
+                                                                 res.stream), res.n, steps, warmup)
+        d = {"workload": wl.name, "rows": wl.rows, "cols": wl.cols, "dtype": wl.dtype,
+             "single_pass_kernel": kernel_name(res), "single_pass_us": round(one * 1e3, 3),
+             "single_pass_gbps": round(wl.bytes / (one * 1e-3) / 1e9, 1),
+             "split_us": round(spl * 1e3, 3), "split_gbps": round(wl.bytes / (spl * 1e-3) / 1e9, 1),
+             "note": "gbps by the metric's 2*rows*cols*size bytes; the split path moves up to 1.5x that"}
+        log(f"[bench] {wl.name}: softmax_fwd {d['single_pass_us']} us ({d['single_pass_gbps']} GB/s)"
+            f"  split {d['split_us']} us ({d['split_gbps']} GB/s)")
+        out[key] = d
+        del res, ws
+    torch.cuda.synchronize()
+    return out
+
+
 def kernel_name(res: Resident) -> str:
     kid = binding.softmax_select(res.ins[0].data_ptr(), res.outs[0].data_ptr(), res.wl.cols, res.wl.cols,
                                  res.code, rows=res.wl.rows)
@@ -415,6 +441,7 @@ def main() -> int:
             del shapes[key]["_res"]  # free its buffers before the next shape
     if args.only is None:
         shapes["c2_fused"] = causal_c2(args.steps, args.warmup)
+        shapes.update(split_shapes(args.steps, args.warmup))
 
     head = shapes[HEADLINE]
     res = head.pop("_res")

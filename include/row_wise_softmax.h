@@ -21,9 +21,9 @@
  * (the single stride of "Kernel Fusion", section "A fused softmax in Triton").
  * Elements between `cols` and `row_stride` are never read or written.
  *
- * Ownership: the caller owns both device buffers.  The library allocates no
- * device memory, keeps no pointer after returning, never synchronises the host
- * and never pre-fills `out` (it writes every out[i, j < cols] exactly once;
+ * Ownership: the caller owns both device buffers (and any workspace).  The
+ * library allocates no device memory, keeps no pointer after returning, never
+ * synchronises the host and never pre-fills `out` (it writes every out[i, j < cols] exactly once;
  * "I Wrote My First GPU Kernel", section "The Honest Part", on the cost of
  * zero-filling an output the kernel overwrites anyway).
  *
@@ -182,6 +182,42 @@ const char *softmax_version(void);
  * misaligned), OVERLAP, HIP.
  */
 int softmax_bench_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/*
+ * ---- Split-row softmax: few, wide rows ----
+ *
+ * With one workgroup per row, a matrix of few wide rows (say 8 x 1,048,576)
+ * occupies a few of the 256 compute units.  The split path cuts every row
+ * into tiles, one workgroup each: a first kernel writes each tile's (max, sum)
+ * pair to a workspace, a second merges a row's pairs with the online-softmax
+ * rule ("Dissecting Memory Bandwidth & SRAM Tiling in Triton", section "The
+ * Mathematical Remedy: Online Softmax Tiling") -- the same fixed merge order
+ * in every workgroup of the row -- and re-reads its tile to write it
+ * normalised.  This is the two-pass answer to a reduction that spans
+ * workgroups ("Kernel Fusion", section "What fusion cannot fix").  Traffic is
+ * two reads and one write per element; the re-read may hit L2 or the
+ * Infinity Cache.  Results are those of softmax_fwd up to rounding.
+ *
+ * softmax_split_workspace_bytes -- device workspace bytes softmax_fwd_split
+ * needs for rows x cols of `dtype` (8 bytes per tile), or -1 for bad
+ * arguments.
+ *
+ * softmax_fwd_split -- softmax_fwd with permission to use the split path.
+ *   workspace       caller-owned device memory of at least the size above,
+ *                   256-byte aligned, disjoint from in and out; its contents
+ *                   are scratch (overwritten, never read before written).
+ *   force           0: split when rows < 1024 and a row spans two or more
+ *                   tiles, otherwise run softmax_fwd's single-pass kernels
+ *                   (the workspace is then unused and may be NULL); 1: always
+ *                   split.  Other values: SOFTMAX_ERR_BAD_KERNEL.
+ * Other arguments, layout, aliasing (in == out allowed) and errors as
+ * softmax_fwd; a short or misaligned workspace is SOFTMAX_ERR_BAD_SHAPE, a
+ * NULL one (when the split path runs) SOFTMAX_ERR_NULL_POINTER, one that
+ * overlaps in or out SOFTMAX_ERR_OVERLAP.
+ */
+int64_t softmax_split_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+int softmax_fwd_split(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                      void *workspace, int64_t workspace_size, int force, void *stream);
 
 /*
  * ---- Measurement baseline: the unfused five-operation softmax ----

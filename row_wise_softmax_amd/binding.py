@@ -76,6 +76,10 @@ def _load():
     lib.softmax_version.argtypes = []
     lib.softmax_bench_copy.restype = i32
     lib.softmax_bench_copy.argtypes = [vp, vp, i64, vp]
+    lib.softmax_split_workspace_bytes.restype = i64
+    lib.softmax_split_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.softmax_fwd_split.restype = i32
+    lib.softmax_fwd_split.argtypes = [vp, vp, i64, i64, i64, i32, vp, i64, i32, vp]
     lib.softmax_unfused_workspace_bytes.restype = i64
     lib.softmax_unfused_workspace_bytes.argtypes = [i64, i64, i32]
     lib.softmax_unfused_5op.restype = i32
@@ -137,6 +141,18 @@ def bench_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None
     """Plain 16-byte-vector device copy (the achievable-bandwidth reference)."""
     lib = _load()
     _check(lib.softmax_bench_copy(src_ptr, dst_ptr, nbytes, stream), "softmax_bench_copy")
+
+
+def split_workspace_bytes(rows: int, cols: int, dtype: int) -> int:
+    return int(_load().softmax_split_workspace_bytes(rows, cols, dtype))
+
+
+def softmax_fwd_split(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int, dtype: int,
+                      workspace_ptr: int, workspace_size: int, force: int = 0, stream: int = 0) -> None:
+    """Softmax allowed to split few, wide rows over several workgroups (caller workspace)."""
+    lib = _load()
+    _check(lib.softmax_fwd_split(in_ptr, out_ptr, rows, cols, row_stride, dtype, workspace_ptr, workspace_size,
+                                 force, stream), "softmax_fwd_split")
 
 
 def unfused_workspace_bytes(rows: int, cols: int, dtype: int) -> int:

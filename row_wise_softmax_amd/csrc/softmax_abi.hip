@@ -285,9 +285,106 @@ int select_id(const void* in, const void* out, int64_t rows, int64_t cols, int64
     return SOFTMAX_OK;
 }
 
+// ---- split-row path: tiles of one workgroup each, two kernels, a workspace
+
+constexpr int kSplitW = 4;
+constexpr int kSplitVecV = 4;     // 16-byte accesses per thread per tile
+constexpr int kSplitScalarV = 8;  // elements per thread per tile (any alignment)
+constexpr int64_t kSplitMaxRows = 1024;  // below this many rows, split when asked to choose
+
+struct SplitPair {
+    const void* stats;
+    const void* norm;
+    int vec;
+    int tile;  // accesses per tile
+};
+
+template <class E>
+SplitPair split_kernels(bool vec) {
+    constexpr int kN = 16 / E::kBytes;
+    if (vec)
+        return {(const void*)&rws::softmax_split_stats<E, kN, kSplitW, kSplitVecV>,
+                (const void*)&rws::softmax_split_norm<E, kN, kSplitW, kSplitVecV>, kN, kSplitW * 64 * kSplitVecV};
+    return {(const void*)&rws::softmax_split_stats<E, 1, kSplitW, kSplitScalarV>,
+            (const void*)&rws::softmax_split_norm<E, 1, kSplitW, kSplitScalarV>, 1, kSplitW * 64 * kSplitScalarV};
+}
+
+SplitPair split_for(int dtype, bool vec) {
+    switch (dtype) {
+        case SOFTMAX_F32: return split_kernels<rws::F32>(vec);
+        case SOFTMAX_F16: return split_kernels<rws::F16>(vec);
+        default: return split_kernels<rws::BF16>(vec);
+    }
+}
+
+// Tiles per row of the split path (the scalar path's tiles are the smallest,
+// so the workspace is sized for them).
+int64_t split_tiles(int64_t cols, const SplitPair& k) {
+    const int64_t nacc = cols / k.vec;
+    return (nacc + k.tile - 1) / k.tile;
+}
+
+int64_t split_workspace(int64_t rows, int64_t cols, int dtype) {
+    const int64_t tiles = split_tiles(cols, split_for(dtype, false));
+    return ((rows * tiles * 8 + 255) / 256) * 256;
+}
+
+int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, float* part,
+                 hipStream_t stream) {
+    const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
+    rws::SplitArgs a;
+    a.in = in;
+    a.out = out;
+    a.part = part;
+    a.rows = rows;
+    a.stride = row_stride / k.vec;
+    a.nacc = int(cols / k.vec);
+    a.tiles = int(split_tiles(cols, k));
+    a.work = rows * a.tiles;
+    a.coef = float(kLog2eD);
+    const int64_t grid = a.work < kMaxGrid ? a.work : kMaxGrid;
+    void* args[] = {&a};
+    for (const void* fn : {k.stats, k.norm}) {
+        if (hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kSplitW * 64), args, 0, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return SOFTMAX_ERR_HIP;
+        }
+    }
+    return SOFTMAX_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t softmax_split_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    if (rows < 0 || cols < 0 || cols > kMaxCols) return -1;
+    if (dtype != SOFTMAX_F32 && dtype != SOFTMAX_F16 && dtype != SOFTMAX_BF16) return -1;
+    if (rows > INT64_MAX / 8 / (cols / 2048 + 2)) return -1;
+    return split_workspace(rows, cols, dtype);
+}
+
+int softmax_fwd_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                      void* workspace, int64_t workspace_size, int force, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK || empty) return st;
+    if (force != 0 && force != 1) return SOFTMAX_ERR_BAD_KERNEL;
+    const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
+    const bool split = force == 1 || (rows < kSplitMaxRows && split_tiles(cols, k) >= 2);
+    if (!split) return fwd(in, out, rows, cols, row_stride, dtype, false, 1.0f, 0, stream);
+    if (workspace == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    const int64_t need = split_workspace(rows, cols, dtype);
+    if (uintptr_t(workspace) % 256 || workspace_size < need) return SOFTMAX_ERR_BAD_SHAPE;
+    const int64_t esz = elem_bytes(dtype);
+    const int64_t extent = ((rows - 1) * row_stride + cols) * esz;
+    const uintptr_t a = uintptr_t(in), b = uintptr_t(out), w = uintptr_t(workspace);
+    if ((w < a + uint64_t(extent) && a < w + uint64_t(need)) || (w < b + uint64_t(extent) && b < w + uint64_t(need)))
+        return SOFTMAX_ERR_OVERLAP;
+    return launch_split(in, out, rows, cols, row_stride, dtype, static_cast<float*>(workspace),
+                        static_cast<hipStream_t>(stream));
+}
+
 
 int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
                 void* stream) {

@@ -610,6 +610,135 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
     }
 }
 
+// ---------------------------------------------------------- split-row kernels
+//
+// For few, wide rows: one workgroup per row leaves most of the chip idle, so
+// each row is cut into tiles of W*64*V accesses and every tile gets its own
+// workgroup -- the "two passes" answer to a reduction that spans blocks ("Kernel
+// Fusion", section "What fusion cannot fix"), with the tiles' partial results
+// combined by the online-softmax merge ("Dissecting Memory Bandwidth & SRAM
+// Tiling in Triton", section "The Mathematical Remedy: Online Softmax
+// Tiling").  Kernel 1 writes each tile's (max, sum) to a workspace; kernel 2
+// has every workgroup of a row merge that row's pairs in one fixed order (so
+// all of them reach the same bits), re-read its tile and write it normalised.
+// Traffic: two reads and one write per element; kernel 1 reads with the
+// default cache policy so that kernel 2's re-read can hit L2 or the Infinity
+// Cache.  No workgroup waits for another, so the grid may be any size.
+struct SplitArgs {
+    const void* in;
+    void* out;
+    float* part;     // 2 floats (max, sum) per (row, tile), row-major
+    int64_t rows;
+    int64_t stride;  // row stride in accesses
+    int64_t work;    // rows * tiles
+    int nacc;        // accesses per row
+    int tiles;       // tiles per row
+    float coef;      // log2(e)
+};
+
+template <class E, int N, int W, int V>
+__global__ void __launch_bounds__(W * kWave) softmax_split_stats(SplitArgs a) {
+    typedef typename Access<E, N>::raw raw;
+    constexpr int kThreads = W * kWave;
+    constexpr int kTile = kThreads * V;
+    __shared__ float red_m[W];
+    __shared__ float red_s[W];
+    const raw* in = static_cast<const raw*>(a.in);
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    for (int64_t b = blockIdx.x; b < a.work; b += gridDim.x) {
+        const int64_t row = b / a.tiles;
+        const int base = int(b - row * a.tiles) * kTile;
+        const raw* p = in + row * a.stride + base + t;
+        float x[V][N];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            load_access<E, N, false, true>(p + v * kThreads, base + v * kThreads + t, a.nacc, 0, x[v]);
+        float m = x[0][0];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int e = 0; e < N; ++e) m = fmaxf(m, x[v][e]);
+        m = group_reduce<kWave, OpMax>(m);
+        if (lane == 0) red_m[wave] = m;
+        __syncthreads();
+        m = red_m[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) m = fmaxf(m, red_m[w]);
+        float s = 0.0f;
+        if (m != -INFINITY) {  // uniform: m is the workgroup's
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int e = 0; e < N; ++e) s += exp_diff(x[v][e] - m, a.coef);
+        }
+        s = group_reduce<kWave, OpSum>(s);
+        if (lane == 0) red_s[wave] = s;
+        __syncthreads();
+        if (t == 0) {
+            s = red_s[0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) s += red_s[w];
+            f32x2 pr = {m, s};
+            *reinterpret_cast<f32x2*>(a.part + 2 * b) = pr;
+        }
+        __syncthreads();  // red_m / red_s are rewritten for the next tile
+    }
+}
+
+template <class E, int N, int W, int V>
+__global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
+    typedef typename Access<E, N>::raw raw;
+    constexpr int kThreads = W * kWave;
+    constexpr int kTile = kThreads * V;
+    __shared__ float red_m[W];
+    __shared__ float red_s[W];
+    const raw* in = static_cast<const raw*>(a.in);
+    raw* out = static_cast<raw*>(a.out);
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    for (int64_t b = blockIdx.x; b < a.work; b += gridDim.x) {
+        const int64_t row = b / a.tiles;
+        const int base = int(b - row * a.tiles) * kTile;
+        const raw* p = in + row * a.stride + base + t;
+        float x[V][N];
+#pragma unroll
+        for (int v = 0; v < V; ++v) load_access<E, N, false>(p + v * kThreads, base + v * kThreads + t, a.nacc, 0, x[v]);
+        // Merge the row's tile pairs: thread t takes tiles t, t + 64W, ... in
+        // order, then the wave and workgroup reductions run in a fixed order.
+        float m = -INFINITY, s = 0.0f;
+        const float* part = a.part + 2 * row * a.tiles;
+        for (int j = t; j < a.tiles; j += kThreads) {
+            const f32x2 pr = *reinterpret_cast<const f32x2*>(part + 2 * j);
+            merge_pair(m, s, pr.x, pr.y, a.coef);
+        }
+        wave_reduce_pair(m, s, a.coef);
+        if (lane == 0) {
+            red_m[wave] = m;
+            red_s[wave] = s;
+        }
+        __syncthreads();
+        m = red_m[0];
+        s = red_s[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+        const float mu = m == -INFINITY ? 0.0f : m;  // all -inf row: every term exp(-inf) = 0
+        const float r = recip_sum(s);
+        raw* q = out + row * a.stride + base + t;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (base + v * kThreads + t < a.nacc) {
+#pragma unroll
+                for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - mu, a.coef) * r;
+                store_elems<E, N>(q + v * kThreads, x[v]);
+            }
+        }
+        __syncthreads();  // red_m / red_s are rewritten for the next tile
+    }
+}
+
 // ------------------------------------------------------------- copy kernel
 //
 // Plain 16-byte copy with the same non-temporal hints, U accesses per thread in

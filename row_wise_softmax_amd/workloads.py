@@ -17,7 +17,9 @@ distributions are never stated, so the distributions here are a stated recipe):
   section "Where the time goes in an elementwise chain");
 * ``c5``  the width sweep of "GPU Kernels - Implementing and optimizing
   Softmax" (widths 32 ... 16384, about 200 MB per tensor), bf16 and fp32,
-  x ~ N(0, 2^2), rows = floor(200e6 / (cols * element size)).
+  x ~ N(0, 2^2), rows = floor(200e6 / (cols * element size));
+* ``wide_*`` few, wide rows for the split-row path (8 x 2^20 fp32 and
+  32 x 2^18 bf16, x ~ N(0, 2^2)); not a configuration of the pages.
 
 Recipe: numpy ``default_rng`` (PCG64) draws in float64, in slices of about
 2^20 elements whose streams are the children of ``SeedSequence(seed)``, then a
@@ -181,6 +183,9 @@ def _build_registry() -> dict:
         "c3": Workload("c3_8192x4096_f16", 8192, 4096, "f16", "normal", (3,), {"sigma": 1.0}),
         "c4": Workload("c4_4096x4096_f32", 4096, 4096, "f32", "uniform", (4,), {"lo": -10.0, "hi": 10.0}),
     }
+    # few, wide rows (the split-row path): vocabulary-sized logits rows
+    reg["wide_f32"] = Workload("few_wide_8x1048576_f32", 8, 1 << 20, "f32", "normal", (6, 1), {"sigma": 2.0})
+    reg["wide_bf16"] = Workload("few_wide_32x262144_bf16", 32, 1 << 18, "bf16", "normal", (6, 2), {"sigma": 2.0})
     for dt in ("bf16", "f32"):
         for w in SWEEP_WIDTHS:
             key = f"c5_{dt}_{w}"

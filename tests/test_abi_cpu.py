@@ -179,3 +179,20 @@ def test_unfused_baseline_argument_errors(lib):
     assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 0, A, ws, None) == 4          # workspace overlaps input
     assert lib.softmax_unfused_5op(A, B, 4, 8, 8, 5, W, ws, None) == 3          # dtype
     assert lib.softmax_unfused_5op(A, B, 0, 8, 8, 0, W, ws, None) == 0          # empty
+
+
+def test_split_argument_errors(lib):
+    ws = binding.split_workspace_bytes(4, 1 << 16, 0)
+    assert ws >= 4 * ((1 << 16) // 2048) * 8 and ws % 256 == 0
+    assert binding.split_workspace_bytes(-1, 8, 0) == -1
+    assert binding.split_workspace_bytes(4, 8, 7) == -1
+    Wk = 0x40000000  # host address, 256-byte aligned, never dereferenced
+    n = 1 << 16
+    # force = 1 (split): every case below is rejected before any launch
+    assert lib.softmax_fwd_split(A, A + 4 * n * 4 + 256, 4, n, n, 0, 0, ws, 1, None) == 1        # null workspace
+    assert lib.softmax_fwd_split(A, A + 4 * n * 4 + 256, 4, n, n, 0, Wk, ws - 256, 1, None) == 2  # short
+    assert lib.softmax_fwd_split(A, A + 4 * n * 4 + 256, 4, n, n, 0, Wk + 8, ws, 1, None) == 2   # misaligned
+    assert lib.softmax_fwd_split(A, A + 4 * n * 4 + 256, 4, n, n, 0, A, ws, 1, None) == 4        # overlaps input
+    assert lib.softmax_fwd_split(A, A + 4 * n * 4 + 256, 4, n, n, 0, Wk, ws, 2, None) == 5       # bad force
+    assert lib.softmax_fwd_split(A, A + 16, 4, n, n, 0, Wk, ws, 1, None) == 4                    # in/out overlap
+    assert lib.softmax_fwd_split(A, B, 0, n, n, 0, 0, 0, 1, None) == 0                           # empty

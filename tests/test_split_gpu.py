@@ -1,0 +1,94 @@
+"""GPU parity of the split-row softmax (few, wide rows) against the CPU oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from row_wise_softmax_amd import binding
+from row_wise_softmax_amd import workloads as W
+
+from gpu_util import check, check_padding_untouched, decode, sentinel, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    binding._load()
+
+
+def _run_split(x, dtype, cols=None, force=1, inplace=False, offset=0):
+    """Run softmax_fwd_split on host array x (rows x row_stride); offset shifts both
+    pointers by that many elements (to reach the any-alignment path)."""
+    import torch
+    rows, stride = x.shape
+    cols = stride if cols is None else cols
+    code = W.dtype_code(dtype)
+    full = np.concatenate([np.zeros(offset, dtype=x.dtype), x.ravel()])
+    xd = to_device(full, dtype)
+    if inplace:
+        out = xd
+    else:
+        out = to_device(np.full_like(full, sentinel(dtype)), dtype)
+    nbytes = binding.split_workspace_bytes(rows, cols, code)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    esz = 4 if dtype == "f32" else 2
+    binding.softmax_fwd_split(xd.data_ptr() + offset * esz, out.data_ptr() + offset * esz, rows, cols, stride,
+                              code, ws.data_ptr(), nbytes, force, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return to_host(out, dtype)[offset:].reshape(rows, stride)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(1, 4096), (3, 5000), (8, 1 << 16), (2, 1 << 20), (17, 100000), (1000, 3000)])
+@pytest.mark.parametrize("force", [1, 0])
+def test_split_matches_the_oracle(dtype, rows, cols, force):
+    print(f"[gpu-case] split {dtype} rows={rows} cols={cols} force={force}", file=sys.stderr, flush=True)
+    x = W.random_matrix(seed=71, rows=rows, cols=cols, dtype=dtype, sigma=3.0)
+    y = _run_split(x, dtype, force=force)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"split {dtype} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_any_alignment_and_stride(dtype):
+    rows, cols, stride = 5, 70001, 70011
+    x = W.random_matrix(seed=72, rows=rows, cols=cols, dtype=dtype, row_stride=stride)
+    y = _run_split(x, dtype, cols=cols, offset=1)
+    check(y, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label="split scalar")
+    check_padding_untouched(y, cols, dtype, label="split scalar")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_split_in_place(dtype):
+    x = W.random_matrix(seed=73, rows=4, cols=1 << 17, dtype=dtype)
+    y = _run_split(x, dtype, inplace=True)
+    check(y, x, dtype, O.softmax(x, dtype), label="split in place")
+
+
+def test_split_masked_and_extreme_rows():
+    rows, cols = 6, 50000
+    x64 = np.random.default_rng(74).standard_normal((rows, cols)) * 2
+    x64[0, :] = -np.inf                 # whole row -inf -> zeros
+    x64[1, :cols // 2] = -np.inf        # first half masked (whole tiles of -inf)
+    x64[2, 12345] = 3.0e38              # a huge entry in one tile
+    x64[3, :] = -3.0e38
+    x64[4, 40000] = 1e9
+    x = W.cast(x64, "f32")
+    y = _run_split(x, "f32")
+    check(y, x, "f32", O.softmax(x, "f32"), label="split extremes")
+    yd = decode(y, "f32")
+    assert np.all(yd[0] == 0.0)
+
+
+def test_split_equals_single_pass_when_not_split():
+    """force = 0 with many rows runs the single-pass kernels: same bits as softmax_fwd."""
+    import torch
+    from gpu_util import run
+    x = W.random_matrix(seed=75, rows=2048, cols=1024, dtype="f32")
+    a = _run_split(x, "f32", force=0)
+    b = run(x, "f32")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
