@@ -65,6 +65,11 @@ def _load():
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_double, ctypes.c_int64, ctypes.c_void_p,
         ]
+        lib.oracle_attention_fwd.restype = ctypes.c_int
+        lib.oracle_attention_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+        ]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_bf16.restype = ctypes.c_double
@@ -120,6 +125,32 @@ def softmax_causal(x: np.ndarray, dtype: str, scale: float, diag: int = 0,
                                    out.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_softmax_causal rejected its arguments (rc={rc})")
+    return out
+
+
+def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str, scale: float,
+                  causal: bool) -> np.ndarray:
+    """O = softmax(scale * Q K^T, causal mask) V in float64.
+
+    q is [batch, heads, nq, d], k and v are [batch, heads, nk, d], held as in
+    :func:`softmax` (float32, or uint16 bits for f16 / bf16).  With ``causal``
+    query i keeps keys j <= i + (nk - nq); a query with no kept key gives 0.
+    """
+    lib = _load()
+    code = DTYPE_CODES[dtype]
+    want = np.float32 if dtype == "f32" else np.uint16
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != want or t.ndim != 4 or not t.flags.c_contiguous:
+            raise ValueError(f"oracle: {name} must be a C-contiguous 4-D {want.__name__} array")
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    if k.shape != (b, h, nk, d) or v.shape != (b, h, nk, d):
+        raise ValueError("oracle: k and v must be [batch, heads, nk, d] matching q")
+    out = np.empty((b, h, nq, d), dtype=np.float64)
+    rc = lib.oracle_attention_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, code, b, h, nq, nk, d,
+                                  float(scale), int(bool(causal)), out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attention_fwd rejected its arguments (rc={rc})")
     return out
 
 

@@ -41,6 +41,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_F32 0
@@ -194,5 +195,70 @@ int oracle_softmax_causal(const void *in, int dtype, int64_t rows, int64_t cols,
         for (int64_t j = 0; j < kept; ++j)
             y[j] = y[j] / s;
     }
+    return 0;
+}
+
+/*
+ * Attention forward with the softmax in the middle ("Dissecting Memory
+ * Bandwidth & SRAM Tiling in Triton", section "Memory Hierarchy: Why Standard
+ * Attention Collapses": O = softmax(Q K^T / sqrt(d)) V, and section "Writing
+ * the Kernel in OpenAI Triton": the causal mask).  Computed the plain way, in
+ * double: for every batch b, head h and query i,
+ *     s_j = scale * sum_d q[i][d] k[j][d]           for every kept key j,
+ *     p_j = exp(s_j - max s) / sum exp(s - max s),
+ *     o[i][d] = sum_j p_j v[j][d].
+ * With `causal`, key j is kept for query i when j <= i + (nk - nq) (the mask
+ * aligned to the last query, as for a query block appended to a key cache);
+ * a query with no kept key gets o = 0.  q is [b][h][nq][d], k and v are
+ * [b][h][nk][d], out is [b][h][nq][d] doubles, all dense.  dtype is that of
+ * q, k and v (ORACLE_F16 or ORACLE_BF16 for the MFMA path; ORACLE_F32 works
+ * too).  Returns 0, or -1 on a bad argument.
+ */
+int oracle_attention_fwd(const void *q, const void *k, const void *v, int dtype,
+                         int64_t batch, int64_t heads, int64_t nq, int64_t nk, int64_t d,
+                         double scale, int causal, double *out)
+{
+    if (batch < 0 || heads < 0 || nq < 0 || nk < 0 || d <= 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (!(scale > 0.0) || isinf(scale)) return -1;
+    if (batch == 0 || heads == 0 || nq == 0) return 0;
+    if (q == NULL || k == NULL || v == NULL || out == NULL) return -1;
+
+    double *s = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+    if (s == NULL) return -1;
+    for (int64_t bh = 0; bh < batch * heads; ++bh) {
+        const int64_t qb = bh * nq * d, kb = bh * nk * d;
+        for (int64_t i = 0; i < nq; ++i) {
+            double *o = out + qb + i * d;
+            for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+            int64_t kept = nk;
+            if (causal) {
+                kept = i + (nk - nq) + 1;
+                if (kept < 0) kept = 0;
+                if (kept > nk) kept = nk;
+            }
+            if (kept == 0) continue;
+
+            double m = -INFINITY;
+            for (int64_t j = 0; j < kept; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += load_element(q, dtype, qb + i * d + c) * load_element(k, dtype, kb + j * d + c);
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            double sum = 0.0;
+            for (int64_t j = 0; j < kept; ++j) {
+                s[j] = exp(s[j] - m);
+                sum += s[j];
+            }
+            for (int64_t j = 0; j < kept; ++j) {
+                const double p = s[j] / sum;
+                for (int64_t c = 0; c < d; ++c)
+                    o[c] += p * load_element(v, dtype, kb + j * d + c);
+            }
+        }
+    }
+    free(s);
     return 0;
 }

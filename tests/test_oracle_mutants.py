@@ -34,6 +34,12 @@ MUTANTS = {
     "causal_reads_masked": ("for (int64_t j = 0; j < kept; ++j)\n            y[j] = scale",
                             "for (int64_t j = 0; j < cols; ++j)\n            y[j] = scale"),
     "causal_diag_sign": ("} else if (diag < -i) {", "} else if (diag < i) {"),
+    "attn_scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "attn_causal_offset": ("kept = i + (nk - nq) + 1;", "kept = i + 1;"),
+    "attn_k_from_q_base": ("* load_element(k, dtype, kb + j * d + c);", "* load_element(k, dtype, qb + j * d + c);"),
+    "attn_v_transposed": ("o[c] += p * load_element(v, dtype, kb + j * d + c);",
+                          "o[c] += p * load_element(v, dtype, kb + c * nk + j);"),
+    "attn_unnormalised": ("const double p = s[j] / sum;", "const double p = s[j];"),
 }
 
 
@@ -50,6 +56,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     env = dict(os.environ, ROW_SOFTMAX_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_causal.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_causal.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_attention.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
