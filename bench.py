@@ -175,6 +175,37 @@ def split_shapes(steps: int, warmup: int) -> dict:
     return out
 
 
+def attention_shapes(steps: int, warmup: int) -> dict:
+    """Fused attention forward (MFMA) on the shapes of the attention page's
+    table: batch 4, 32 heads, head dim 128, causal, seeded N(0, 1) inputs."""
+    import torch
+    out = {}
+    for dt, n in (("f16", 1024), ("f16", 4096), ("bf16", 4096)):
+        b, h, d = 4, 32, 128
+        g = torch.Generator(device="cpu").manual_seed(7)
+        tdt = torch_dtype(dt)
+        qkv = [torch.randn((b, h, n, d), generator=g).to(tdt).to("cuda") for _ in range(3)]
+        o = torch.empty_like(qkv[0])
+        stream = torch.cuda.current_stream().cuda_stream
+        code = W.dtype_code(dt)
+
+        def launch(i):
+            binding.attention_fwd(qkv[0].data_ptr(), qkv[1].data_ptr(), qkv[2].data_ptr(), o.data_ptr(), b, h, n, n, d,
+                                  1.0 / d ** 0.5, True, code, stream)
+
+        reps = max(3, min(steps, 20))
+        ms = time_launches(launch, 1, reps, max(1, min(warmup, 3)))
+        flops = 4.0 * b * h * d * (n * (n + 1) / 2)  # two products over the kept (causal) keys
+        tf = flops / (ms * 1e-3) / 1e12
+        key = f"attention_{dt}_b{b}_h{h}_n{n}_d{d}_causal"
+        out[key] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / 2500.0, 4),
+                    "note": "flops = 4*b*h*d*n(n+1)/2 (kept keys only); peak = 2.5 PFLOP/s dense fp16/bf16 MFMA"}
+        log(f"[bench] {key}: {out[key]['us']} us  {out[key]['tflops']} TFLOP/s ({100 * out[key]['frac_of_mfma_peak']:.1f}% of MFMA peak)")
+        del qkv, o
+    torch.cuda.synchronize()
+    return out
+
+
 def kernel_name(res: Resident) -> str:
     kid = binding.softmax_select(res.ins[0].data_ptr(), res.outs[0].data_ptr(), res.wl.cols, res.wl.cols,
                                  res.code, rows=res.wl.rows)
@@ -442,6 +473,7 @@ def main() -> int:
     if args.only is None:
         shapes["c2_fused"] = causal_c2(args.steps, args.warmup)
         shapes.update(split_shapes(args.steps, args.warmup))
+        shapes.update(attention_shapes(args.steps, args.warmup))
 
     head = shapes[HEADLINE]
     res = head.pop("_res")

@@ -220,6 +220,33 @@ int softmax_fwd_split(const void *in, void *out, int64_t rows, int64_t cols, int
                       void *workspace, int64_t workspace_size, int force, void *stream);
 
 /*
+ * ---- Fused attention forward on the matrix cores ----
+ *
+ * attention_fwd -- O = softmax(scale * Q K^T) V per batch and head, with the
+ * softmax fused between the two products so the nq x nk scores never reach
+ * memory: the attention of "Dissecting Memory Bandwidth & SRAM Tiling in
+ * Triton" (sections "Memory Hierarchy: Why Standard Attention Collapses" and
+ * "Writing the Kernel in OpenAI Triton"), whose online softmax is this
+ * library's merge rule applied per key block.  Both products run on
+ * v_mfma_f32_16x16x32_{f16,bf16}; softmax statistics and the accumulator are
+ * fp32.
+ *   q, o        [batch][heads][nq][head_dim], dense, 16-byte aligned
+ *   k, v        [batch][heads][nk][head_dim], dense, 16-byte aligned
+ *   head_dim    64 or 128
+ *   scale       > 0 with scale * log2(e) below 3e38 (typically 1/sqrt(head_dim))
+ *   causal      0, or 1: query i keeps keys j <= i + (nk - nq) (the mask aligned
+ *               to the last query); a query with no kept key gets o = 0
+ *   dtype       SOFTMAX_F16 or SOFTMAX_BF16 (q, k, v and o share it)
+ * o must not overlap q, k or v; k and v may be NULL when nk == 0.
+ * batch * heads <= 65535, nq <= 2^30.
+ * Errors: BAD_DTYPE, BAD_SHAPE (negative sizes, head_dim, misalignment, too
+ * large), BAD_SCALE, NULL_POINTER, OVERLAP, HIP.  batch, heads or nq == 0
+ * launches nothing.  Same asynchrony and ownership rules as softmax_fwd.
+ */
+int attention_fwd(const void *q, const void *k, const void *v, void *o, int64_t batch, int64_t heads,
+                  int64_t nq, int64_t nk, int64_t head_dim, float scale, int causal, int dtype, void *stream);
+
+/*
  * ---- Measurement baseline: the unfused five-operation softmax ----
  *
  * The same softmax computed as five separate kernels, each a round trip

@@ -80,6 +80,8 @@ def _load():
     lib.softmax_split_workspace_bytes.argtypes = [i64, i64, i32]
     lib.softmax_fwd_split.restype = i32
     lib.softmax_fwd_split.argtypes = [vp, vp, i64, i64, i64, i32, vp, i64, i32, vp]
+    lib.attention_fwd.restype = i32
+    lib.attention_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp]
     lib.softmax_unfused_workspace_bytes.restype = i64
     lib.softmax_unfused_workspace_bytes.argtypes = [i64, i64, i32]
     lib.softmax_unfused_5op.restype = i32
@@ -153,6 +155,35 @@ def softmax_fwd_split(in_ptr: int, out_ptr: int, rows: int, cols: int, row_strid
     lib = _load()
     _check(lib.softmax_fwd_split(in_ptr, out_ptr, rows, cols, row_stride, dtype, workspace_ptr, workspace_size,
                                  force, stream), "softmax_fwd_split")
+
+
+def attention_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, batch: int, heads: int, nq: int, nk: int,
+                  head_dim: int, scale: float, causal: bool, dtype: int, stream: int = 0) -> None:
+    """Raw entry point of the fused attention forward (dense [batch, heads, n, head_dim] layouts)."""
+    lib = _load()
+    _check(lib.attention_fwd(q_ptr, k_ptr, v_ptr, o_ptr, batch, heads, nq, nk, head_dim, scale, int(bool(causal)),
+                             dtype, stream), "attention_fwd")
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = False, out=None):
+    """softmax(scale q k^T) v for contiguous [batch, heads, n, head_dim] fp16 / bf16 CUDA tensors."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("attention: q, k, v must be [batch, heads, n, head_dim]")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("attention: q, k, v must be contiguous GPU tensors of one dtype")
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    if tuple(k.shape) != (b, h, nk, d) or tuple(v.shape) != (b, h, nk, d):
+        raise ValueError("attention: k and v must be [batch, heads, nk, head_dim] matching q")
+    code = _torch_dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    scale = 1.0 / float(d) ** 0.5 if scale is None else float(scale)
+    attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), b, h, nq, nk, d, scale, causal, code,
+                  torch.cuda.current_stream(q.device).cuda_stream)
+    return out
 
 
 def unfused_workspace_bytes(rows: int, cols: int, dtype: int) -> int:

@@ -22,7 +22,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "librow_wise_softmax.so")
 
 ARCH = "gfx950"
-SOURCES = ["softmax_abi.hip", "table_f32.hip", "table_f16.hip", "table_bf16.hip", "unfused.hip"]
+SOURCES = ["softmax_abi.hip", "table_f32.hip", "table_f16.hip", "table_bf16.hip", "unfused.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -196,3 +196,17 @@ def test_split_argument_errors(lib):
     assert lib.softmax_fwd_split(A, A + 4 * n * 4 + 256, 4, n, n, 0, Wk, ws, 2, None) == 5       # bad force
     assert lib.softmax_fwd_split(A, A + 16, 4, n, n, 0, Wk, ws, 1, None) == 4                    # in/out overlap
     assert lib.softmax_fwd_split(A, B, 0, n, n, 0, 0, 0, 1, None) == 0                           # empty
+
+
+def test_attention_argument_errors(lib):
+    a = lambda *args: lib.attention_fwd(*args, None)  # noqa: E731
+    Q, K, V, O = 0x100000, 0x200000, 0x300000, 0x400000
+    assert a(Q, K, V, O, 1, 1, 64, 64, 64, 0.125, 1, 0) == 3       # fp32 not supported
+    assert a(Q, K, V, O, 1, 1, 64, 64, 96, 0.125, 1, 1) == 2       # head_dim
+    assert a(Q, K, V, O, 1, 1, 64, 64, 64, 0.0, 1, 1) == 7         # scale
+    assert a(Q, K, V, O, 1, 1, 64, 64, 64, 0.125, 2, 1) == 2       # causal flag
+    assert a(0, K, V, O, 1, 1, 64, 64, 64, 0.125, 1, 1) == 1       # null
+    assert a(Q + 2, K, V, O, 1, 1, 64, 64, 64, 0.125, 1, 1) == 2   # misaligned
+    assert a(Q, K, V, Q + 64, 1, 1, 64, 64, 64, 0.125, 1, 1) == 4  # o overlaps q
+    assert a(Q, K, V, O, 300, 300, 64, 64, 64, 0.125, 1, 1) == 2   # batch * heads > 65535
+    assert a(Q, K, V, O, 0, 1, 64, 64, 64, 0.125, 1, 1) == 0       # empty

@@ -1,0 +1,87 @@
+"""GPU parity of the fused attention forward (MFMA) against the CPU oracle.
+
+Tolerance, from the arithmetic: P is rounded to the input type before the
+second product (relative error <= 2^-(m+1) per weight, and the weights sum to
+one) and O is rounded on the way out (<= 2^-(m+1) |O| <= 2^-(m+1) max|V|),
+with m the mantissa width (11 for fp16, 8 for bf16); the fp32 products and
+sums add far less.  So |O_gpu - O_oracle| <= 2^-m max|V|; the tests allow 4x.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from row_wise_softmax_amd import binding
+from row_wise_softmax_amd import workloads as W
+
+from gpu_util import decode, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+MANT = {"f16": 11, "bf16": 8}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    binding._load()
+
+
+def _qkv(b, h, nq, nk, d, dtype, seed):
+    rng = np.random.default_rng([seed, b, h, nq, nk, d])
+    q = W.cast(rng.standard_normal((b, h, nq, d)), dtype)
+    k = W.cast(rng.standard_normal((b, h, nk, d)), dtype)
+    v = W.cast(rng.standard_normal((b, h, nk, d)), dtype)
+    return q, k, v
+
+
+def _run(q, k, v, dtype, scale, causal):
+    import torch
+    b, h, nq, d = q.shape
+    nk = k.shape[2]
+    qd, kd, vd = (to_device(np.ascontiguousarray(t), dtype) for t in (q, k, v))
+    od = torch.full_like(qd, float("nan"))
+    binding.attention_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), od.data_ptr(), b, h, nq, nk, d, scale,
+                          causal, W.dtype_code(dtype), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return decode(to_host(od, dtype), dtype)
+
+
+SHAPES = [(1, 1, 64, 64, 64), (2, 3, 100, 100, 64), (1, 2, 128, 256, 128), (1, 1, 77, 33, 128),
+          (2, 2, 200, 200, 128), (1, 4, 1, 130, 64), (1, 1, 130, 1, 64), (1, 2, 64, 0, 64), (3, 1, 257, 300, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{b}x{h}x{nq}x{nk}x{d}" for b, h, nq, nk, d in SHAPES])
+def test_attention_matches_the_oracle(dtype, causal, shape):
+    b, h, nq, nk, d = shape
+    print(f"[gpu-case] attention {dtype} causal={causal} {shape}", file=sys.stderr, flush=True)
+    q, k, v = _qkv(b, h, nq, nk, d, dtype, seed=91)
+    scale = 1.0 / np.sqrt(d)
+    got = _run(q, k, v, dtype, scale, causal)
+    want = O.attention_fwd(q, k, v, dtype, scale, causal)
+    vmax = float(np.max(np.abs(decode(v, dtype)))) if v.size else 1.0
+    tol = 4 * 2.0 ** -MANT[dtype] * max(vmax, 1.0)
+    assert not np.isnan(got).any()
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert err <= tol, f"max abs error {err:.3e} > {tol:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_attention_large_scale_and_peaked_rows(dtype):
+    """A large scale makes every row nearly one-hot: the online max must track it."""
+    q, k, v = _qkv(1, 2, 150, 150, 64, dtype, seed=92)
+    got = _run(q, k, v, dtype, 2.0, True)
+    want = O.attention_fwd(q, k, v, dtype, 2.0, True)
+    tol = 4 * 2.0 ** -MANT[dtype] * float(np.max(np.abs(decode(v, dtype))))
+    assert float(np.max(np.abs(got - want))) <= tol
+
+
+def test_attention_first_causal_row_copies_v0():
+    q, k, v = _qkv(2, 2, 64, 64, 128, "f16", seed=93)
+    got = _run(q, k, v, "f16", 0.125, True)
+    assert np.array_equal(got[:, :, 0], decode(v, "f16")[:, :, 0])
