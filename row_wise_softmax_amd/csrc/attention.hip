@@ -12,12 +12,11 @@
 // products run on the matrix cores: v_mfma_f32_16x16x32_{f16,bf16}.
 //
 // Work split: one workgroup of 4 waves per (batch*head, block of 64 queries);
-// each wave owns 16 query rows and keeps their Q fragments in registers.  Per
+// each wave owns 16 queries and keeps their Q fragments in registers.  Per
 // block of 64 keys the workgroup stages K (row-major) and V (transposed) in
-// LDS; each wave computes its 16 x 64 score tile with MFMA, updates m and l
-// in fp32 (exponentials as 2^(x log2 e) on v_exp_f32), writes P in the input
-// type to a wave-private LDS tile, reads it back in the MFMA A-operand layout
-// and accumulates O += P V.
+// LDS; each wave computes its 64 x 16 transposed score tile with MFMA,
+// updates m and l in fp32 (exponentials as 2^(x log2 e) on v_exp_f32),
+// rounds P to the input type in registers and accumulates O^T += V^T P^T.
 //
 // MFMA operand layout used (16 x 16 x 32): lane L supplies row (or column)
 // L % 16 and eight consecutive k slots 8 (L / 16) .. 8 (L / 16) + 7; the
@@ -47,6 +46,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBM = 64;  // queries per workgroup (16 per wave)
 constexpr int kBN = 64;  // keys per block
 constexpr int kThreads = 256;
+static_assert(kBN * 64 / 8 % kThreads == 0 && (kBN / 2) * (64 / 8) % kThreads == 0, "K/V staging splits evenly");
 constexpr double kLog2eD = 1.4426950408889634074;
 
 struct AttnArgs {
@@ -72,146 +72,207 @@ __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ inline u32x4 lds16(const unsigned short* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Exchange with lane ^ 32 (ds_bpermute: byte address of the source lane).
+__device__ inline float xor32(float v) {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, v)));
+}
+
+// All-reduce over the four lanes L, L ^ 16, L ^ 32, L ^ 48 (same L % 16).
+template <class Op>
+__device__ inline float across_groups(float v) {
+    v = Op::apply(v, rws::swap16(v));
+    return Op::apply(v, xor32(v));
+}
+
+__device__ inline unsigned pack2(unsigned short lo, unsigned short hi) { return unsigned(lo) | (unsigned(hi) << 16); }
+
+// Scores are computed transposed, S^T = K Q^T, so that lane L owns query
+// c = L % 16 of its wave and holds keys 4g .. 4g + 3 (g = L / 16) of every
+// 16-key tile: the softmax statistics of a query are per-lane scalars (shared
+// by the four lanes of one query), and the exponentials are already the B
+// operand of O^T = V^T P^T -- slot j of a 32-key step takes key 4g + j of its
+// first tile (j < 4) or 16 + 4g + (j - 4) of its second, and V^T is read from
+// LDS in the same slot order.  While a block is computed, the next block's K
+// and V are already on their way from HBM into registers.
 template <class E, int D, bool Causal>
 __global__ void __launch_bounds__(kThreads) attention_fwd_kernel(AttnArgs a) {
-    constexpr int kKS = D / 32;      // MFMA k-steps over the head dimension
-    constexpr int kKP = D + 8;       // padded K row in LDS (halves)
-    constexpr int kVP = kBN + 8;     // padded V^T row (keys)
-    constexpr int kPP = kBN + 8;     // padded P row (keys)
-    constexpr int kDT = D / 16;      // 16-wide output tiles per wave
+    constexpr int kKS = D / 32;               // MFMA k-steps over the head dimension
+    constexpr int kKP = D + 8;                // padded K row in LDS (halves)
+    constexpr int kVP = kBN + 8;              // padded V^T row (keys)
+    constexpr int kDT = D / 16;               // 16-row output tiles (of O^T) per wave
+    constexpr int kLoadsK = kBN * D / 8 / kThreads;        // 16-byte K pieces per thread per block
+    constexpr int kLoadsV = (kBN / 2) * (D / 8) / kThreads;  // (key pair, 8 dims) V items per thread
     __shared__ __attribute__((aligned(16))) unsigned short sK[kBN * kKP];
     __shared__ __attribute__((aligned(16))) unsigned short sVt[D * kVP];
-    __shared__ __attribute__((aligned(16))) unsigned short sP[4][16 * kPP];
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int w = t / kWave;
-    const int g = lane >> 4;  // lane group: k slots 8g .. 8g + 7, result rows 4g .. 4g + 3
-    const int c = lane & 15;  // operand row / column, result column
+    const int g = lane >> 4;
+    const int c = lane & 15;
     const int64_t bh = blockIdx.y;
     const int64_t m0 = int64_t(blockIdx.x) * kBM;
+    const int64_t qi = m0 + 16 * w + c;  // this lane's query
     const unsigned short* qb = static_cast<const unsigned short*>(a.q) + bh * a.nq * D;
     const unsigned short* kb = static_cast<const unsigned short*>(a.k) + bh * a.nk * D;
     const unsigned short* vb = static_cast<const unsigned short*>(a.v) + bh * a.nk * D;
     unsigned short* ob = static_cast<unsigned short*>(a.o) + bh * a.nq * D;
 
-    // Q fragments of this wave's 16 rows (A operand): row m0 + 16w + c.
+    // Q fragments (B operand of S^T): column qi, head-dim slots 32s + 8g .. + 7.
     u32x4 qf[kKS];
-    {
-        const int64_t row = m0 + 16 * w + c;
 #pragma unroll
-        for (int s = 0; s < kKS; ++s) {
-            if (row < a.nq) qf[s] = rws::ld<true>(reinterpret_cast<const u32x4*>(qb + row * D + 32 * s + 8 * g));
-            else qf[s] = u32x4{0, 0, 0, 0};
-        }
+    for (int s = 0; s < kKS; ++s) {
+        if (qi < a.nq) qf[s] = rws::ld<true>(reinterpret_cast<const u32x4*>(qb + qi * D + 32 * s + 8 * g));
+        else qf[s] = u32x4{0, 0, 0, 0};
     }
 
-    float mrow[4], lrow[4];
+    float m = -INFINITY;  // running max of this lane's query (log2 domain)
+    float l = 0.0f;       // this lane's partial normaliser (its keys only)
     f32x4 oacc[kDT];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        mrow[r] = -INFINITY;
-        lrow[r] = 0.0f;
-    }
 #pragma unroll
     for (int u = 0; u < kDT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Keys any query of this block may see.
-    int64_t kend = a.nk;
+    int64_t kend = a.nk;  // keys any query of this workgroup may see
     if (Causal) {
         const int64_t last = m0 + kBM - 1 + a.offset + 1;
         kend = last < kend ? last : kend;
     }
 
-    for (int64_t n0 = 0; n0 < kend; n0 += kBN) {
-        __syncthreads();  // every wave is done with the previous block's sK / sVt
-        // Stage K (row-major) and V (transposed) for keys n0 .. n0 + 63.
-        for (int idx = t; idx < kBN * D / 8; idx += kThreads) {
+    // K / V staging registers.  K: thread t moves 16-byte pieces t + 256 i
+    // (row-major, coalesced).  V: item t + 256 i is a pair of consecutive keys
+    // (2 (item % 32), + 1) and 8 head dims (8 (item / 32) ..); the pair is
+    // written to V^T as one dword per head dim, so a wave's 32-bit LDS writes
+    // cover 32 consecutive dwords of one V^T row per half-wave, the two halves
+    // 8 rows (32 banks) apart: no bank conflicts.
+    u32x4 kreg[kLoadsK], vreg[kLoadsV][2];
+    auto fetch = [&](int64_t n0) {
+#pragma unroll
+        for (int i = 0; i < kLoadsK; ++i) {
+            const int idx = t + i * kThreads;
             const int key = idx / (D / 8);
             const int dc = (idx % (D / 8)) * 8;
-            u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (n0 + key < a.nk) {
-                kv = rws::ld<false>(reinterpret_cast<const u32x4*>(kb + (n0 + key) * D + dc));
-                vv = rws::ld<false>(reinterpret_cast<const u32x4*>(vb + (n0 + key) * D + dc));
+            if (n0 + key < a.nk) kreg[i] = rws::ld<false>(reinterpret_cast<const u32x4*>(kb + (n0 + key) * D + dc));
+            else kreg[i] = u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadsV; ++i) {
+            const int item = t + i * kThreads;
+            const int key = 2 * (item % (kBN / 2));
+            const int dc = (item / (kBN / 2)) * 8;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (n0 + key + h < a.nk)
+                    vreg[i][h] = rws::ld<false>(reinterpret_cast<const u32x4*>(vb + (n0 + key + h) * D + dc));
+                else
+                    vreg[i][h] = u32x4{0, 0, 0, 0};
             }
-            *reinterpret_cast<u32x4*>(sK + key * kKP + dc) = kv;
+        }
+    };
+    if (kend > 0) fetch(0);
+
+    for (int64_t n0 = 0; n0 < kend; n0 += kBN) {
+        __syncthreads();  // every wave is done reading the previous block from LDS
+#pragma unroll
+        for (int i = 0; i < kLoadsK; ++i) {
+            const int idx = t + i * kThreads;
+            const int key = idx / (D / 8);
+            const int dc = (idx % (D / 8)) * 8;
+            *reinterpret_cast<u32x4*>(sK + key * kKP + dc) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadsV; ++i) {
+            const int item = t + i * kThreads;
+            const int key = 2 * (item % (kBN / 2));
+            const int dc = (item / (kBN / 2)) * 8;
+            unsigned* col = reinterpret_cast<unsigned*>(sVt + dc * kVP + key);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sVt[(dc + 2 * e) * kVP + key] = (unsigned short)(vv[e] & 0xffffu);
-                sVt[(dc + 2 * e + 1) * kVP + key] = (unsigned short)(vv[e] >> 16);
+                const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
+                col[(2 * e) * (kVP / 2)] = (a0 & 0xffffu) | (a1 << 16);            // head dim dc + 2e
+                col[(2 * e + 1) * (kVP / 2)] = (a0 >> 16) | (a1 & 0xffff0000u);    // head dim dc + 2e + 1
             }
         }
         __syncthreads();
+        if (n0 + kBN < kend) fetch(n0 + kBN);  // in flight while this block is computed
 
-        // Scores of this wave's 16 rows against the 64 keys (four 16 x 16 tiles).
+        // S^T tiles: keys 16nt + 4g + r (r = 0..3) against query qi.
         f32x4 sacc[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < kKS; ++s) sacc[nt] = mfma<E>(qf[s], lds16(sK + (16 * nt + c) * kKP + 32 * s + 8 * g), sacc[nt]);
+            for (int s = 0; s < kKS; ++s)
+                sacc[nt] = mfma<E>(lds16(sK + (16 * nt + c) * kKP + 32 * s + 8 * g), qf[s], sacc[nt]);
         }
 
-        // Scale into the log2 domain, mask, and update the running statistics.
+        // Scale into the log2 domain; mask only blocks that need it (uniform branch).
+        const bool full = n0 + kBN <= a.nk && (!Causal || n0 + kBN - 1 <= m0 + a.offset);
+        float bm = -INFINITY;
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t qi = m0 + 16 * w + 4 * g + r;
-            float bm = -INFINITY;
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int64_t kj = n0 + 16 * nt + c;
-                float x = sacc[nt][r] * a.coef;
-                if (kj >= a.nk || (Causal && kj > qi + a.offset)) x = -INFINITY;
-                sacc[nt][r] = x;
-                bm = fmaxf(bm, x);
-            }
-            bm = rws::group_reduce<16, rws::OpMax>(bm);  // the 16 lanes holding this row
-            const float mnew = fmaxf(mrow[r], bm);
-            const float msafe = mnew == -INFINITY ? 0.0f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrow[r] - msafe);  // 0 while the row had nothing
-            float ps = 0.0f;
+                for (int r = 0; r < 4; ++r) {
+                    sacc[nt][r] *= a.coef;
+                    bm = fmaxf(bm, sacc[nt][r]);
+                }
+        } else {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const float p = __builtin_amdgcn_exp2f(sacc[nt][r] - msafe);
-                sacc[nt][r] = p;
-                ps += p;
-            }
-            lrow[r] = lrow[r] * alpha + ps;  // per-lane partial; summed over the row's lanes at the end
-            mrow[r] = mnew;
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int u = 0; u < kDT; ++u) oacc[u][r] *= alpha;
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t kj = n0 + 16 * nt + 4 * g + r;
+                    float x = sacc[nt][r] * a.coef;
+                    if (kj >= a.nk || (Causal && kj > qi + a.offset)) x = -INFINITY;
+                    sacc[nt][r] = x;
+                    bm = fmaxf(bm, x);
+                }
         }
-
-        // P in the input type, to this wave's LDS tile (row-major).
-        unsigned short* pw = sP[w];
+        bm = across_groups<rws::OpMax>(bm);
+        const float mnew = fmaxf(m, bm);
+        const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);  // 0 while the query had no key
+        m = mnew;
+        float ps = 0.0f;
+        unsigned short ph[4][4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float pv = sacc[nt][r];
-                pw[(4 * g + r) * kPP + 16 * nt + c] = rws::narrow_half<E>(pv);
+                const float p = __builtin_amdgcn_exp2f(sacc[nt][r] - msafe);
+                ps += p;
+                ph[nt][r] = rws::narrow_half<E>(p);
             }
-        __syncthreads();  // P writes visible before the A-operand reads
+        l = l * alpha + ps;
+#pragma unroll
+        for (int u = 0; u < kDT; ++u) oacc[u] *= alpha;
 
-        // O += P V over the block's 64 keys (two k-steps of 32).
+        // O^T += V^T P^T over the block's two 32-key steps.
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const u32x4 pa = lds16(pw + c * kPP + 32 * s + 8 * g);
+            const u32x4 pb = {pack2(ph[2 * s][0], ph[2 * s][1]), pack2(ph[2 * s][2], ph[2 * s][3]),
+                              pack2(ph[2 * s + 1][0], ph[2 * s + 1][1]), pack2(ph[2 * s + 1][2], ph[2 * s + 1][3])};
 #pragma unroll
-            for (int u = 0; u < kDT; ++u)
-                oacc[u] = mfma<E>(pa, lds16(sVt + (16 * u + c) * kVP + 32 * s + 8 * g), oacc[u]);
+            for (int u = 0; u < kDT; ++u) {
+                const unsigned short* vrow = sVt + (16 * u + c) * kVP + 32 * s + 4 * g;
+                const rws::u32x2 lo = *reinterpret_cast<const rws::u32x2*>(vrow);
+                const rws::u32x2 hi = *reinterpret_cast<const rws::u32x2*>(vrow + 16);
+                const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+                oacc[u] = mfma<E>(va, pb, oacc[u]);
+            }
         }
     }
 
-    // Normalise and store: result rows 4g + r, column 16u + c.
+    // Normalise and store: lane holds O[qi][16u + 4g + r], r = 0..3 (8 bytes).
+    l = across_groups<rws::OpSum>(l);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (qi < a.nq) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float l = rws::group_reduce<16, rws::OpSum>(lrow[r]);
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        const int64_t qi = m0 + 16 * w + 4 * g + r;
-        if (qi < a.nq) {
-#pragma unroll
-            for (int u = 0; u < kDT; ++u) ob[qi * D + 16 * u + c] = rws::narrow_half<E>(oacc[u][r] * inv);
+        for (int u = 0; u < kDT; ++u) {
+            const rws::u32x2 pk = {pack2(rws::narrow_half<E>(oacc[u][0] * inv), rws::narrow_half<E>(oacc[u][1] * inv)),
+                                   pack2(rws::narrow_half<E>(oacc[u][2] * inv), rws::narrow_half<E>(oacc[u][3] * inv))};
+            rws::st<true>(reinterpret_cast<rws::u32x2*>(ob + qi * D + 16 * u + 4 * g), pk);
         }
     }
 }
