@@ -51,7 +51,8 @@ def _run(q, k, v, dtype, scale, causal):
 
 
 SHAPES = [(1, 1, 64, 64, 64), (2, 3, 100, 100, 64), (1, 2, 128, 256, 128), (1, 1, 77, 33, 128),
-          (2, 2, 200, 200, 128), (1, 4, 1, 130, 64), (1, 1, 130, 1, 64), (1, 2, 64, 0, 64), (3, 1, 257, 300, 64)]
+          (2, 2, 200, 200, 128), (1, 4, 1, 130, 64), (1, 1, 130, 1, 64), (1, 2, 64, 0, 64), (3, 1, 257, 300, 64),
+          (2, 5, 300, 300, 64), (1, 8, 512, 512, 128), (1, 2, 640, 520, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -85,3 +86,27 @@ def test_attention_first_causal_row_copies_v0():
     q, k, v = _qkv(2, 2, 64, 64, 128, "f16", seed=93)
     got = _run(q, k, v, "f16", 0.125, True)
     assert np.array_equal(got[:, :, 0], decode(v, "f16")[:, :, 0])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("direction", [1.0, -1.0])
+def test_attention_scores_that_ramp_across_blocks(dtype, direction):
+    """Scores that grow (or shrink) steadily with the key index: the running max
+    moves a little in every key block, sometimes by less than the kernel lets
+    the exponent offset lag, sometimes by more, so both the kept and the
+    rescaled offsets are exercised against the oracle."""
+    b, h, n, d = 1, 2, 520, 64
+    rng = np.random.default_rng(94)
+    q = np.zeros((b, h, n, d))
+    q[..., 0] = 1.0
+    q[..., 1:] = 0.05 * rng.standard_normal((b, h, n, d - 1))
+    k = 0.05 * rng.standard_normal((b, h, n, d))
+    k[..., 0] = direction * 0.26 * np.arange(n)  # log2-domain slope ~ 3 per 64 keys at scale 1/8
+    v = rng.standard_normal((b, h, n, d))
+    q, k, v = (W.cast(t, dtype) for t in (q, k, v))
+    for causal in (False, True):
+        got = _run(q, k, v, dtype, 0.125, causal)
+        want = O.attention_fwd(q, k, v, dtype, 0.125, causal)
+        tol = 4 * 2.0 ** -MANT[dtype] * float(np.max(np.abs(decode(v, dtype))))
+        err = float(np.max(np.abs(got - want)))
+        assert err <= tol, f"causal={causal}: max abs error {err:.3e} > {tol:.3e}"
