@@ -244,14 +244,19 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfus
     return d
 
 
+# Sources the fused softmax kernels are built from (attention and the unfused
+# baseline are separate kernels and do not change the softmax's traffic).
+SOFTMAX_SOURCES = ("kernel_table.hpp", "softmax_abi.hip", "softmax_kernels.hpp", "table_bf16.hip",
+                   "table_entries.inc", "table_f16.hip", "table_f32.hip")
+
+
 def source_digest() -> str:
-    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    """Hash of the softmax kernel sources, to tell whether stored counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "row_wise_softmax_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".inc")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in SOFTMAX_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -361,10 +366,29 @@ def summarize_trace(stats_csv):
            "- `softmax_row<F32,4,4,2,true>`: c2 with the mask and 1/8 scale fused (raw scores in);",
            "- `softmax_row<F16,8,4,2,false>`: c3 8192x4096 fp16 (the headline);",
            "- `softmax_row<F32,4,8,2,false>`: c4 4096x4096 fp32;",
-           "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape.", "",
+           "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape;",
+           "- `unfused_reduce` / `unfused_elementwise`: the five-kernel unfused softmax on c3 and c4 (max, sub, exp, sum, div);",
+           "- `softmax_online` (single pass) and `softmax_split_stats` + `softmax_split_norm` (split rows):"
+           " 8 x 1048576 fp32 and 32 x 262144 bf16;",
+           "- `attention_fwd_kernel<E,128,true>`: causal attention forward, batch 4, 32 heads, head dim 128"
+           " (fp16 at 1024 and 4096 keys, bf16 at 4096; split by launch grid below).", "",
            "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if os.path.exists(trace_csv):
+        groups = {}
+        for r in csv.DictReader(open(trace_csv)):
+            if "attention_fwd_kernel" in r["Kernel_Name"]:
+                dt = "bf16" if "BF16" in r["Kernel_Name"] else "f16"
+                key = (dt, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+                groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        if groups:
+            out += ["", "Attention dispatches by launch grid (workgroups = 32 heads x 4 batch x queries / 128):", "",
+                    "| dtype | workgroups | keys | calls | average ns | min ns |", "|---|---|---|---|---|---|"]
+            for (dt, wg), ds in sorted(groups.items()):
+                heads, per_block = 4 * 32, 128  # batch x heads, queries per workgroup
+                out.append(f"| {dt} | {wg} | {wg // heads * per_block} | {len(ds)} | {sum(ds) / len(ds):.0f} | {min(ds)} |")
     path = os.path.join(PROFILE_DIR, "kernel_trace_bench.md")
     open(path, "w").write("\n".join(out) + "\n")
     print(open(path).read())
