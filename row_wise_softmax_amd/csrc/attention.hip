@@ -9,7 +9,7 @@
 // accumulator rescaled whenever the max grows (same page, section "The
 // Mathematical Remedy: Online Softmax Tiling", and the kernel of section
 // "Writing the Kernel in OpenAI Triton").  This is a contraction, so both
-// products run on the matrix cores: v_mfma_f32_16x16x32_{f16,bf16}.
+// products run on the matrix cores: v_mfma_f32_32x32x16_{f16,bf16}.
 //
 // Work split: one workgroup of 4 waves per (batch*head, block of 128
 // queries); each wave owns 32 queries and keeps their Q fragments in
@@ -57,6 +57,8 @@ constexpr double kLog2eD = 1.4426950408889634074;
 // it by more than this (log2 domain), so P <= 2^kSlack: the rescale of the
 // accumulators is skipped for most blocks and P stays far inside fp16 range.
 constexpr float kSlack = 8.0f;
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource flags word (raw, untyped 32-bit data)
+constexpr int kWaitVm0 = 0x0F70;        // s_waitcnt vmcnt(0), other counters untouched
 
 struct AttnArgs {
     const void* q;
@@ -96,35 +98,63 @@ __device__ inline unsigned pack2f(float lo, float hi) {
     return rws::narrow_dword<E>(f);
 }
 
-// V^T keeps the 16 keys of each group in the order 0-3, 8-11, 4-7, 12-15
-// (bits 2 and 3 of the key swapped), so that the eight keys one lane feeds to
-// a 16-key MFMA step are 16 contiguous bytes.  Key pairs stay adjacent:
-// this maps the pair index p = key / 2 (bits 1 and 2 swapped).
-__device__ inline int vt_pair(int p) { return (p & ~6) | ((p & 2) << 1) | ((p & 4) >> 1); }
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane j receives,
+// as its element e, element j % 4 of the 8 bytes addressed by lane
+// 4e + j / 4 of the group.  So if lane s of the group addresses the four
+// consecutive head dims 4 (s % 4) .. of key row s / 4, lane j receives head
+// dim j of key rows 0, 1, 2, 3: one V^T operand column from row-major V.
+__device__ inline rws::u32x2 lds_tr(const unsigned short* p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(rws::u32x2, r);
+}
 
 // Scores are computed transposed, S^T = K Q^T, so that lane L owns query
 // c = L % 32 of its wave and holds keys 8 (r / 4) + 4 h + r % 4 (h = L / 32,
 // r = 0..15) of every 32-key tile: the softmax statistics of a query are
 // per-lane scalars (shared by lanes L and L ^ 32), and accumulators 8q .. 8q + 7
 // of a tile are already the B operand of the O^T = V^T P^T step over its keys
-// 16q .. 16q + 15.  While a block is computed, the next block's K and V are
-// already on their way from HBM into registers.
+// 16q .. 16q + 15.  The matching V^T operand is read from row-major V with
+// two transposing LDS reads.
+//
+// The wave works through 32-key tiles in a software pipeline: while the
+// vector ALUs turn tile t's scores into P, the matrix cores already compute
+// tile t + 1's scores, then P V of tile t runs, then tile t + 1's max is
+// taken.  K is therefore needed one 64-key block ahead of V.  K and V go from
+// HBM straight into LDS (buffer loads with the lds flag, no registers): K into
+// three rotating buffers, V into two, so that the next blocks land while the
+// current ones are read, with one barrier per block.  Rows are not padded:
+// each row's 16-byte chunks are stored XOR-swizzled so that every LDS read of
+// a wave touches distinct banks.
 template <class E, int D, bool Causal>
 __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) {
-    constexpr int kKS = D / 16;                              // MFMA k-steps over the head dimension
-    constexpr int kKP = D + 8;                               // padded K row in LDS (halves)
-    constexpr int kVP = kBN + 8;                             // padded V^T row (keys)
-    constexpr int kDT = D / 32;                              // 32-row output tiles (of O^T) per wave
-    constexpr int kLoadsK = kBN * D / 8 / kThreads;          // 16-byte K pieces per thread per block
-    constexpr int kLoadsV = (kBN / 2) * (D / 8) / kThreads;  // (key pair, 8 dims) V items per thread
-    __shared__ __attribute__((aligned(16))) unsigned short sK[kBN * kKP];
-    __shared__ __attribute__((aligned(16))) unsigned short sVt[D * kVP];
+    constexpr int kKS = D / 16;                                    // MFMA k-steps over the head dimension
+    constexpr int kC = D / 8;                                      // 16-byte chunks per K or V row
+    constexpr int kDT = D / 32;                                    // 32-row output tiles (of O^T) per wave
+    constexpr int kDma = kBN * D * 2 / 1024 / (kThreads / kWave);  // 1 KB pieces per wave per block
+    // Separate arrays, each named statically below: loads from one are then
+    // known not to alias the pieces in flight into another, and the compiler
+    // does not make them wait for those.
+    __shared__ __attribute__((aligned(16))) unsigned short sK0[kBN * D];
+    __shared__ __attribute__((aligned(16))) unsigned short sK1[kBN * D];
+    __shared__ __attribute__((aligned(16))) unsigned short sK2[kBN * D];
+    __shared__ __attribute__((aligned(16))) unsigned short sV0[kBN * D];
+    __shared__ __attribute__((aligned(16))) unsigned short sV1[kBN * D];
+    // Chunk cc of K row r sits at position cc ^ ksw(r): a K read takes one
+    // chunk of 16 consecutive rows.  A V read takes two chunks of 4
+    // consecutive rows (and another two per half-wave), so V rows are
+    // swizzled by whole 4-chunk groups.  A 128-byte row (D = 64) spans half
+    // the banks, so pairs of rows share a pattern.
+    auto ksw = [](int r) { return (D == 64 ? r >> 1 : r) & (kC - 1); };
+    auto vsw = [](int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); };
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
-    const int w = t / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(t / kWave);
     const int h = lane >> 5;
     const int c = lane & 31;
+    const int swz = ksw(c);  // = ksw(32 half + c) for both tile halves
 
     // Workgroups of one (batch, head) share K and V: give each XCD (and its
     // L2) a contiguous run of them.  Causal query blocks run longest-first.
@@ -137,9 +167,14 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
     const int64_t mw = m0 + 32 * w;  // first query of this wave
     const int64_t qi = mw + c;       // this lane's query
     const unsigned short* qb = static_cast<const unsigned short*>(a.q) + bh * a.nq * D;
-    const unsigned short* kb = static_cast<const unsigned short*>(a.k) + bh * a.nk * D;
-    const unsigned short* vb = static_cast<const unsigned short*>(a.v) + bh * a.nk * D;
     unsigned short* ob = static_cast<unsigned short*>(a.o) + bh * a.nq * D;
+    // K and V of this (batch, head) as buffer resources: reads past the last
+    // key return zeros (the host guarantees nk * D * 2 < 2^31).
+    const uint32_t kvbytes = uint32_t(a.nk * D * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(static_cast<const unsigned short*>(a.k) + bh * a.nk * D), 0, kvbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(static_cast<const unsigned short*>(a.v) + bh * a.nk * D), 0, kvbytes, kRsrcWord3);
 
     // Q fragments (B operand of S^T): column qi, head-dim slots 16s + 8h .. + 7.
     u32x4 qf[kKS];
@@ -159,101 +194,64 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
 
     // Keys any query of this workgroup (of this wave) may see.
     const int64_t qlast = (m0 + kBM < a.nq ? m0 + kBM : a.nq) - 1;
-    int64_t kend = a.nk, wend = a.nk;
+    int64_t kend = a.nk, wend = mw < a.nq ? a.nk : 0;  // a wave wholly past the last query sees nothing
     if (Causal) {
         kend = qlast + a.offset + 1 < kend ? qlast + a.offset + 1 : kend;
         wend = mw + 31 + a.offset + 1 < wend ? mw + 31 + a.offset + 1 : wend;
+        wend = wend < kend ? wend : kend;  // never past the staged blocks
     }
-    const bool wave_idle = mw >= a.nq;  // every query of this wave is past the end
+    const int64_t nblk = kend > 0 ? (kend + kBN - 1) / kBN : 0;
 
-    // K / V staging registers.  K: thread t moves 16-byte pieces t + 256 i
-    // (row-major, coalesced).  V: item t + 256 i is a pair of consecutive keys
-    // (2 (item % 32), + 1) and 8 head dims (8 (item / 32) ..); the pair is
-    // written to V^T as one dword per head dim, so a wave's 32-bit LDS writes
-    // cover 32 distinct dwords of one V^T row per half-wave, the two halves
-    // 8 rows (32 banks) apart.
-    u32x4 kreg[kLoadsK], vreg[kLoadsV][2];
-    auto fetch = [&](int64_t n0) {
+    // One 64-key block of K or V into LDS: each wave moves kDma 1 KB pieces;
+    // lane L of a piece fills position L % kC of row (piece rows) + L / kC, so
+    // it fetches the chunk that the swizzle puts there.  Rows past the last
+    // key read as zeros.
+    auto dma = [&](__amdgpu_buffer_rsrc_t rs, int64_t n0, unsigned short* dst, auto sw) {
 #pragma unroll
-        for (int i = 0; i < kLoadsK; ++i) {
-            const int idx = t + i * kThreads;
-            const int key = idx / (D / 8);
-            const int dc = (idx % (D / 8)) * 8;
-            if (n0 + key < a.nk) kreg[i] = rws::ld<false>(reinterpret_cast<const u32x4*>(kb + (n0 + key) * D + dc));
-            else kreg[i] = u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < kLoadsV; ++i) {
-            const int item = t + i * kThreads;
-            const int key = 2 * (item % (kBN / 2));
-            const int dc = (item / (kBN / 2)) * 8;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                if (n0 + key + e < a.nk)
-                    vreg[i][e] = rws::ld<false>(reinterpret_cast<const u32x4*>(vb + (n0 + key + e) * D + dc));
-                else
-                    vreg[i][e] = u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < kDma; ++i) {
+            const int piece = w * kDma + i;  // wave-uniform
+            const int row = piece * (512 / D) + lane / kC;
+            const int chunk = (lane % kC) ^ sw(row);
+            const uint32_t off = uint32_t(((n0 + row) * D + chunk * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + piece * 512),
+                                                     16, off, 0, 0, 0);
         }
     };
-    if (kend > 0) fetch(0);
+    // V rows past the last key must hold zeros, not stale LDS (P is 0 there,
+    // and 0 * NaN would not be): clear them in the one block that has such
+    // rows, before its pieces are requested (those rows then read as zeros too).
+    auto clear_v_tail = [&](int64_t n0, unsigned short* dst) {
+        const int64_t valid = a.nk - n0;
+        if (valid >= kBN) return;
+        for (int idx = t; idx < kBN * kC; idx += kThreads)
+            if (idx / kC >= valid) *reinterpret_cast<u32x4*>(dst + idx * 8) = u32x4{0, 0, 0, 0};
+    };
 
-    for (int64_t n0 = 0; n0 < kend; n0 += kBN) {
-        __syncthreads();  // every wave is done reading the previous block from LDS
+    // S^T of one 32-key tile (keys 32 half + 8(r/4) + 4h + r%4 of a staged block).
+    auto scores = [&](const unsigned short* blk, int half) {
+        f32x16 acc;
 #pragma unroll
-        for (int i = 0; i < kLoadsK; ++i) {
-            const int idx = t + i * kThreads;
-            const int key = idx / (D / 8);
-            const int dc = (idx % (D / 8)) * 8;
-            *reinterpret_cast<u32x4*>(sK + key * kKP + dc) = kreg[i];
-        }
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kLoadsV; ++i) {
-            const int item = t + i * kThreads;
-            const int pair = item % (kBN / 2);
-            const int dc = (item / (kBN / 2)) * 8;
-            unsigned* col = reinterpret_cast<unsigned*>(sVt + dc * kVP) + (pair & ~7) + vt_pair(pair & 7);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
-                col[(2 * e) * (kVP / 2)] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);      // head dim dc + 2e
-                col[(2 * e + 1) * (kVP / 2)] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // head dim dc + 2e + 1
-            }
-        }
-        __syncthreads();
-        if (n0 + kBN < kend) fetch(n0 + kBN);  // in flight while this block is computed
-        if (wave_idle || n0 >= wend) continue;  // nothing of this block is visible to this wave
-
-        // S^T tiles: keys n0 + 32nt + 8(r/4) + 4h + r%4 against query qi.
-        f32x16 sacc[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[nt][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < kKS; ++s)
-                sacc[nt] = mfma<E>(lds16(sK + (32 * nt + c) * kKP + 16 * s + 8 * h), qf[s], sacc[nt]);
-        }
-
-        // Mask only blocks that need it (wave-uniform branch); block max in raw score units.
-        const bool full = n0 + kBN <= a.nk && (!Causal || n0 + kBN - 1 <= mw + a.offset);
-        float bm = -INFINITY;
+        for (int s = 0; s < kKS; ++s)
+            acc = mfma<E>(lds16(blk + (32 * half + c) * D + ((2 * s + h) ^ swz) * 8), qf[s], acc);
+        return acc;
+    };
+    // Mask a tile starting at key k0, then move the exponent offset if its max
+    // would make P exceed 2^kSlack (the accumulators are rescaled to match).
+    auto prepare = [&](f32x16& sc, int64_t k0) {
+        const bool full = k0 + 32 <= a.nk && (!Causal || k0 + 31 <= mw + a.offset);  // wave-uniform
         if (!full) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t kj = n0 + 32 * nt + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (kj >= a.nk || (Causal && kj > qi + a.offset)) sacc[nt][r] = -INFINITY;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int64_t kj = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (kj >= a.nk || (Causal && kj > qi + a.offset)) sc[r] = -INFINITY;
+            }
         }
+        float bm = sc[0];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) bm = fmaxf(bm, sacc[nt][r]);
-        bm = fmaxf(bm, xor32(bm)) * a.coef;  // the query's block max, log2 domain
-
-        // Move the exponent offset only when P would exceed 2^kSlack.
+        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sc[r]);
+        bm = fmaxf(bm, xor32(bm)) * a.coef;  // the query's tile max, log2 domain
         if (__builtin_amdgcn_ballot_w64(bm > m + kSlack)) {
             const float mnew = fmaxf(m, bm);
             const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);  // m = -inf: 0
@@ -262,26 +260,88 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
 #pragma unroll
             for (int u = 0; u < kDT; ++u) oacc[u] *= alpha;
         }
+    };
+    // V^T operand for output tile u and the 8 key slots of this lane in a
+    // 16-key step starting at key kb of the block: slots e < 4 are keys
+    // kb + 4h + e, slots e >= 4 keys kb + 8 + 4h + (e - 4).  Lane s of each
+    // 16-lane group addresses key row (s / 4) of those four and head dims
+    // 32u + 16 (group % 2) + 4 (s % 4) .. + 3.
+    const int grp = lane >> 4, sl = lane & 15;
+    auto v_operand = [&](const unsigned short* blk, int kb, int u) {
+        const int dim = 32 * u + 16 * (grp & 1) + 4 * (sl & 3);
+        const int r0 = kb + 4 * h + (sl >> 2), r1 = r0 + 8;
+        const rws::u32x2 lo = lds_tr(blk + r0 * D + (((dim >> 3) ^ vsw(r0)) << 3) + (dim & 7));
+        const rws::u32x2 hi = lds_tr(blk + r1 * D + (((dim >> 3) ^ vsw(r1)) << 3) + (dim & 7));
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
+    // P = 2^(s coef - m) rounded to the input type; O^T += V^T P^T over the
+    // tile's two 16-key steps.
+    auto consume = [&](const f32x16& sc, const unsigned short* vblk, int half) {
         const float moff = m == -INFINITY ? 0.0f : m;  // no visible key yet: every score is -inf
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.coef, -moff));
+            l += p[r];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const u32x4 pb = {pack2f<E>(p[8 * q], p[8 * q + 1]), pack2f<E>(p[8 * q + 2], p[8 * q + 3]),
+                              pack2f<E>(p[8 * q + 4], p[8 * q + 5]), pack2f<E>(p[8 * q + 6], p[8 * q + 7])};
+#pragma unroll
+            for (int u = 0; u < kDT; ++u) oacc[u] = mfma<E>(v_operand(vblk, 32 * half + 16 * q, u), pb, oacc[u]);
+        }
+    };
 
-        // P = 2^(s coef - m), rounded to the input type; O^T += V^T P^T per 16 keys.
+    f32x16 scur;
+    if (nblk > 0) {
+        clear_v_tail(0, sV0);
+        dma(krs, 0, sK0, ksw);
+        if (nblk > 1) dma(krs, kBN, sK1, ksw);
+        dma(vrs, 0, sV0, vsw);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's pieces have landed
+        __syncthreads();
+        if (wend > 0) {
+            scur = scores(sK0, 0);
+            prepare(scur, 0);
+        }
+    }
+    // Block jb: K block jb in kcur, jb + 1 in knext, jb + 2 goes to kfar; V
+    // block jb in vcur, jb + 1 goes to vnext.
+    auto block = [&](int64_t jb, const unsigned short* kcur, const unsigned short* knext, unsigned short* kfar,
+                     const unsigned short* vcur, unsigned short* vnext) {
+        const int64_t n0 = jb * kBN;
+        if (jb > 0) {
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);  // K block jb + 1 and V block jb have landed
+            __syncthreads();  // ... for every wave; all are done with K block jb - 1 and V block jb - 1
+        }
+        if (jb + 2 < nblk) dma(krs, n0 + 2 * kBN, kfar, ksw);  // in flight while this block is computed
+        if (jb + 1 < nblk) {
+            clear_v_tail(n0 + kBN, vnext);
+            dma(vrs, n0 + kBN, vnext, vsw);
+        }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nt][r], a.coef, -moff));
-                l += p[r];
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const u32x4 pb = {pack2f<E>(p[8 * q], p[8 * q + 1]), pack2f<E>(p[8 * q + 2], p[8 * q + 3]),
-                                  pack2f<E>(p[8 * q + 4], p[8 * q + 5]), pack2f<E>(p[8 * q + 6], p[8 * q + 7])};
-#pragma unroll
-                for (int u = 0; u < kDT; ++u)
-                    oacc[u] = mfma<E>(lds16(sVt + (32 * u + c) * kVP + 32 * nt + 16 * q + 8 * h), pb, oacc[u]);
+        for (int half = 0; half < 2; ++half) {
+            const int64_t k0 = n0 + 32 * half;  // this tile's first key
+            if (k0 < wend) {                    // wave-uniform: some key of the tile is visible
+                // Next tile's scores (always from staged LDS; discarded past the last tile).
+                f32x16 snext = half == 0 ? scores(kcur, 1) : scores(knext, 0);
+                consume(scur, vcur, half);
+                if (k0 + 32 < wend) {
+                    prepare(snext, k0 + 32);
+                    scur = snext;
+                }
             }
         }
+    };
+    // Six-block cycle: the K buffer index cycles with period 3, the V one with 2.
+    for (int64_t jb = 0; jb < nblk; jb += 6) {
+        block(jb, sK0, sK1, sK2, sV0, sV1);
+        if (jb + 1 < nblk) block(jb + 1, sK1, sK2, sK0, sV1, sV0);
+        if (jb + 2 < nblk) block(jb + 2, sK2, sK0, sK1, sV0, sV1);
+        if (jb + 3 < nblk) block(jb + 3, sK0, sK1, sK2, sV1, sV0);
+        if (jb + 4 < nblk) block(jb + 4, sK1, sK2, sK0, sV0, sV1);
+        if (jb + 5 < nblk) block(jb + 5, sK2, sK0, sK1, sV1, sV0);
     }
 
     // Normalise and store: lane holds O[qi][32u + 8j + 4h + r], r = 0..3 (8 bytes).
@@ -322,6 +382,7 @@ extern "C" int attention_fwd(const void* q, const void* k, const void* v, void* 
     if (heads > 65535 / (batch > 0 ? batch : 1) || bh > 65535) return SOFTMAX_ERR_BAD_SHAPE;
     if (nq > (int64_t(1) << 30) || nq > (int64_t(1) << 40) / head_dim / bh || nk > (int64_t(1) << 40) / head_dim / bh)
         return SOFTMAX_ERR_BAD_SHAPE;
+    if (nk * head_dim * 2 >= (int64_t(1) << 31)) return SOFTMAX_ERR_BAD_SHAPE;  // K/V of one head < 2 GiB
     const int64_t nqb = (nq + kBM - 1) / kBM;
     if (nqb > INT32_MAX / bh) return SOFTMAX_ERR_BAD_SHAPE;  // one workgroup per (batch*head, 128 queries)
     for (const void* p : {q, k, v, static_cast<const void*>(o)})
