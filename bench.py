@@ -62,10 +62,31 @@ def n_buffers(pair_bytes: int) -> int:
     return max(2, -(-ROTATE_BYTES // pair_bytes))
 
 
-def time_launches(launch, n_buf: int, steps: int, warmup: int) -> float:
-    """Mean ms per launch over `steps` launches, cycling buffer index 0..n_buf-1."""
+SPIN_S = 0.3  # untimed launches before each measurement, for steady clocks
+
+
+def spin_up(launch, n_buf: int, seconds: float) -> None:
+    """Launch repeatedly for `seconds` (untimed): from idle the GPU needs a few
+    hundred milliseconds of load to reach its steady clocks, and a few
+    milliseconds of warm-up measure the ramp instead of the kernel (3% on the
+    fp16 softmax, up to 25% on attention)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            launch(i % n_buf)
+            i += 1
+        torch.cuda.synchronize()
+
+
+def time_launches(launch, n_buf: int, steps: int, warmup: int, spin_s: float = SPIN_S) -> float:
+    """Mean ms per launch over `steps` launches, cycling buffer index 0..n_buf-1,
+    after a spin-up of `spin_s` seconds and `warmup` untimed launches."""
     import torch
     stream = torch.cuda.current_stream()
+    if spin_s > 0:
+        spin_up(launch, n_buf, spin_s)
     for i in range(warmup):
         launch(i % n_buf)
     torch.cuda.synchronize()
@@ -361,6 +382,7 @@ def sweep(steps: int, warmup: int) -> list:
             res = Resident(wl)
             chosen = kernel_name(res)
             results = []
+            spin_up(res.softmax, res.n, SPIN_S)  # once per width; the kernels then follow each other closely
             for k in table:
                 if k.causal:
                     continue  # the sweep times the plain softmax
@@ -369,7 +391,7 @@ def sweep(steps: int, warmup: int) -> list:
                     continue
                 if k.max_cols > 0 and k.max_cols >= 4 * wl.cols:  # far too wide: wastes most lanes
                     continue
-                ms = time_launches(lambda i, kid=k.kid: res.softmax(i, kid), res.n, steps, warmup)
+                ms = time_launches(lambda i, kid=k.kid: res.softmax(i, kid), res.n, steps, warmup, spin_s=0.02)
                 results.append((wl.bytes / (ms * 1e-3) / 1e9, k.name, ms * 1e3))
             results.sort(reverse=True)
             best = results[0]

@@ -69,6 +69,8 @@ struct AttnArgs {
     int64_t nk;
     int64_t offset;  // causal: query i keeps keys j <= i + offset (offset = nk - nq)
     int nqb;         // query blocks per (batch, head)
+    int nbh;         // batch * heads
+    int grp;         // (batch, head) pairs per scheduling group
     int nwg;         // workgroups in the grid
     float coef;      // scale * log2(e)
 };
@@ -157,12 +159,18 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
     const int swz = ksw(c);  // = ksw(32 half + c) for both tile halves
 
     // Workgroups of one (batch, head) share K and V: give each XCD (and its
-    // L2) a contiguous run of them.  Causal query blocks run longest-first.
+    // L2) a contiguous run j of them, in groups of `grp` (batch, head) pairs,
+    // about as many workgroups as an XCD holds at once.  Within a group the
+    // causal query blocks run longest-first across all its pairs, so the
+    // short ones fill in behind the long ones.
     const int i = blockIdx.x;
     const int full_rounds = a.nwg / kXcds * kXcds;
     const int j = i < full_rounds ? (i % kXcds) * (a.nwg / kXcds) + i / kXcds : i;
-    const int64_t bh = j / a.nqb;
-    const int qblk = Causal ? a.nqb - 1 - j % a.nqb : j % a.nqb;
+    const int gsz = a.grp * a.nqb;  // workgroups per group
+    const int g = j / gsz, r = j % gsz;
+    const int gb = a.nbh - g * a.grp < a.grp ? a.nbh - g * a.grp : a.grp;  // pairs in this group
+    const int64_t bh = int64_t(g) * a.grp + r % gb;
+    const int qblk = Causal ? a.nqb - 1 - r / gb : r / gb;
     const int64_t m0 = int64_t(qblk) * kBM;
     const int64_t mw = m0 + 32 * w;  // first query of this wave
     const int64_t qi = mw + c;       // this lane's query
@@ -201,6 +209,8 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
         wend = wend < kend ? wend : kend;  // never past the staged blocks
     }
     const int64_t nblk = kend > 0 ? (kend + kBN - 1) / kBN : 0;
+    // Keys this lane's query keeps: j < kmax.
+    const int64_t kmax = Causal && qi + a.offset + 1 < a.nk ? qi + a.offset + 1 : a.nk;
 
     // One 64-key block of K or V into LDS: each wave moves kDma 1 KB pieces;
     // lane L of a piece fills position L % kC of row (piece rows) + L / kC, so
@@ -228,13 +238,16 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
     };
 
     // S^T of one 32-key tile (keys 32 half + 8(r/4) + 4h + r%4 of a staged block).
+    // The lane's K read offset of every k-step, computed once.
+    int koff[kKS];
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) koff[s] = c * D + ((2 * s + h) ^ swz) * 8;
     auto scores = [&](const unsigned short* blk, int half) {
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < kKS; ++s)
-            acc = mfma<E>(lds16(blk + (32 * half + c) * D + ((2 * s + h) ^ swz) * 8), qf[s], acc);
+        for (int s = 0; s < kKS; ++s) acc = mfma<E>(lds16(blk + 32 * half * D + koff[s]), qf[s], acc);
         return acc;
     };
     // Mask a tile starting at key k0, then move the exponent offset if its max
@@ -242,11 +255,15 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
     auto prepare = [&](f32x16& sc, int64_t k0) {
         const bool full = k0 + 32 <= a.nk && (!Causal || k0 + 31 <= mw + a.offset);  // wave-uniform
         if (!full) {
+            // A real branch (the barrier keeps the compiler from flattening it
+            // into selects that every tile would pay for).  Accumulator r
+            // holds key k0 + 4h + 8(r/4) + r%4, kept iff that is < kmax.
+            __builtin_amdgcn_sched_barrier(0);
+            const int64_t room = kmax - k0 - 4 * h;
+            const int lim = room < 0 ? 0 : room > 32 ? 32 : int(room);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t kj = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (kj >= a.nk || (Causal && kj > qi + a.offset)) sc[r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
         }
         float bm = sc[0];
 #pragma unroll
@@ -327,10 +344,8 @@ __global__ void __launch_bounds__(kThreads, 2) attention_fwd_kernel(AttnArgs a) 
                 // Next tile's scores (always from staged LDS; discarded past the last tile).
                 f32x16 snext = half == 0 ? scores(kcur, 1) : scores(knext, 0);
                 consume(scur, vcur, half);
-                if (k0 + 32 < wend) {
-                    prepare(snext, k0 + 32);
-                    scur = snext;
-                }
+                if (k0 + 32 < wend) prepare(snext, k0 + 32);
+                scur = snext;  // unused when the next tile is past wend
             }
         }
     };
@@ -402,6 +417,10 @@ extern "C" int attention_fwd(const void* q, const void* k, const void* v, void* 
     a.nk = nk;
     a.offset = nk - nq;
     a.nqb = int(nqb);
+    a.nbh = int(bh);
+    // Group about one XCD's worth of resident workgroups (32 CUs x 2).
+    const int64_t per_group = 64 / nqb > 1 ? 64 / nqb : 1;
+    a.grp = int(per_group < bh ? per_group : bh);
     a.nwg = int(nqb * bh);
     a.coef = float(double(scale) * kLog2eD);
     const void* fn = dtype == SOFTMAX_F16 ? pick<rws::F16>(head_dim, causal) : pick<rws::BF16>(head_dim, causal);

@@ -306,3 +306,38 @@ def test_magnitudes_every_family(dtype, family):
     else:
         y = run(x, dtype, kernel_id=k.kid)
         check(y, x, dtype, O.softmax(x, dtype), label=name)
+
+
+# ------------------------------------------- the pages' worked examples
+
+# "GPU Kernels - Implementing and optimizing Softmax", section "Per-thread
+# accumulation": 10 columns over 4 threads, threads 0-1 taking three columns
+# and threads 2-3 two; section "The tree reduction": those four partial maxes
+# are 3.1, 7.2, 1.0, 9.5 and the row max is 9.5.  This row has exactly those
+# partial maxes under that partition (the max sits in column 3, a runner-up
+# 9.0 in column 7); the second row is the four partial maxes themselves.
+_WORKED_ROW = [3.1, 7.2, 1.0, 9.5, 2.0, 5.0, 0.5, 9.0, 1.5, 6.0]
+
+
+@pytest.mark.parametrize("stride", [10, 12])
+def test_pages_worked_partition_and_tree(stride):
+    row = np.array(_WORKED_ROW)
+    parts = [row[t::4].max() for t in range(4)]
+    assert parts == [3.1, 7.2, 1.0, 9.5]  # the fixture is the pages' partition
+    x = np.full((2, stride), np.nan)
+    x[0, :10] = row
+    x[1, :4] = parts
+    x[1, 4:10] = -np.inf
+    x = W.cast(x, "f32")
+    want = O.softmax(x, "f32", cols=10)
+    assert np.argmax(want[0]) == 3 and abs(want[0, 3] / want[0, 7] - np.exp(0.5)) < 1e-12
+    for k in _TABLE:
+        if k.causal or k.dtype != W.dtype_code("f32"):
+            continue
+        xd = to_device(x, "f32")
+        if not binding.kernel_fits(k.kid, xd.data_ptr(), xd.data_ptr(), 10, stride, W.dtype_code("f32")):
+            continue
+        _say(f"worked example {k.name} stride={stride}")
+        y = run(x, "f32", cols=10, kernel_id=k.kid)
+        check(y, x, "f32", want, cols=10, label=f"{k.name} stride={stride}")
+        check_padding_untouched(y, 10, "f32", label=k.name)
