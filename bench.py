@@ -437,6 +437,8 @@ def summarize_trace(stats_csv):
     for r in rows:
         out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
     trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if not os.path.exists(trace_csv):  # the trace trimmed to the attention dispatches
+        trace_csv = os.path.join(os.path.dirname(stats_csv), "attn_trace.csv")
     if os.path.exists(trace_csv):
         groups = {}
         for r in csv.DictReader(open(trace_csv)):
