@@ -110,3 +110,32 @@ def test_attention_scores_that_ramp_across_blocks(dtype, direction):
         tol = 4 * 2.0 ** -MANT[dtype] * float(np.max(np.abs(decode(v, dtype))))
         err = float(np.max(np.abs(got - want)))
         assert err <= tol, f"causal={causal}: max abs error {err:.3e} > {tol:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_attention_benchmarked_shape_sampled(dtype):
+    """The benchmarked shape (batch 4, 32 heads, 4096 queries and keys, head
+    dim 128, causal, scale 1/sqrt(128)), run whole in the benchmark's launch
+    configuration; 40 sampled queries checked against the oracle.  Query i of
+    a causal head keeps keys 0..i, so the oracle takes that query alone with
+    those keys (one query, i + 1 keys: the same kept set)."""
+    b, h, n, d = 4, 32, 4096, 128
+    print(f"[gpu-case] attention full size {dtype}", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(95)
+    q, k, v = (W.cast(rng.standard_normal((b, h, n, d), dtype=np.float32), dtype) for _ in range(3))
+    scale = 1.0 / np.sqrt(d)
+    got = _run(q, k, v, dtype, scale, True)
+    picks = [(0, 0, 0), (0, 0, 1), (1, 5, 127), (1, 5, 128), (3, 31, n - 1), (2, 17, n - 64)]
+    picks += [tuple(int(t) for t in rng.integers((0, 0, 0), (b, h, n))) for _ in range(34)]
+    vmax = float(np.max(np.abs(decode(v, dtype))))
+    tol = 4 * 2.0 ** -MANT[dtype] * vmax
+    worst = 0.0
+    for bb, hh, i in picks:
+        qi = np.ascontiguousarray(q[bb:bb + 1, hh:hh + 1, i:i + 1])
+        ki = np.ascontiguousarray(k[bb:bb + 1, hh:hh + 1, :i + 1])
+        vi = np.ascontiguousarray(v[bb:bb + 1, hh:hh + 1, :i + 1])
+        want = O.attention_fwd(qi, ki, vi, dtype, scale, True)[0, 0, 0]
+        err = float(np.max(np.abs(got[bb, hh, i] - want)))
+        worst = max(worst, err)
+        assert err <= tol, f"query ({bb}, {hh}, {i}): max abs error {err:.3e} > {tol:.3e}"
+    assert not np.isnan(got).any()

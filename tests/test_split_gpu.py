@@ -92,3 +92,14 @@ def test_split_equals_single_pass_when_not_split():
     a = _run_split(x, "f32", force=0)
     b = run(x, "f32")
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("key", ["wide_f32", "wide_bf16"])
+def test_split_benchmarked_shapes(key):
+    """The two few-wide-rows workloads the benchmark times (8 x 2^20 fp32 and
+    32 x 2^18 bf16), whole, through the split path it times."""
+    wl = W.WORKLOADS[key]
+    x = wl.generate()
+    print(f"[gpu-case] split full size {wl.name}", file=sys.stderr, flush=True)
+    y = _run_split(x, wl.dtype, force=0)
+    check(y, x, wl.dtype, O.softmax(x, wl.dtype), label=f"split {wl.name}")

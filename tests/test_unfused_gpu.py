@@ -52,3 +52,17 @@ def test_unfused_widths(dtype, cols):
         pytest.skip("the baseline takes whole 16-byte accesses only")
     y = _run_unfused(x, dtype, inplace=(cols == 256))
     check(y, x, dtype, O.softmax(x, dtype), label=f"unfused {dtype} {cols}")
+
+
+@pytest.mark.parametrize("key", ["c3", "c4"])
+def test_unfused_full_size_sampled(key):
+    """The benchmarked full-size shapes (8192 x 4096 fp16, 4096 x 4096 fp32):
+    64 sampled rows (first, last and random ones) against the oracle, which
+    works row by row."""
+    wl = W.WORKLOADS[key]
+    x = wl.generate()
+    print(f"[gpu-case] unfused full size {wl.name}", file=sys.stderr, flush=True)
+    y = _run_unfused(x, wl.dtype)
+    rows = np.unique(np.concatenate([[0, 1, wl.rows - 1], np.random.default_rng(62).integers(0, wl.rows, 61)]))
+    xs = np.ascontiguousarray(x[rows])
+    check(np.ascontiguousarray(y[rows]), xs, wl.dtype, O.softmax(xs, wl.dtype), label=f"unfused full {key}")
