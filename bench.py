@@ -414,12 +414,14 @@ C3_BYTES = 8192 * 4096 * 2  # input bytes of the headline workload (8192 x 4096 
 def summarize_trace(stats_csv):
     """Write profiles/kernel_trace_bench.md from a rocprofv3 --stats kernel_stats.csv."""
     rows = list(csv.DictReader(open(stats_csv)))
+    out_dir = os.path.relpath(os.path.dirname(os.path.abspath(stats_csv)), ROOT)
     out = ["# Kernel trace of the default benchmark run on MI355X (gfx950)", "",
            "Command (repository root):", "",
-           "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- python3 bench.py --no-cpu",
-           "    python3 bench.py --summarize-trace gpurun_out/prof_trace/bench_kernel_stats.csv",
+           f"    rocprofv3 --kernel-trace --stats --output-format csv -d {out_dir} -o bench -- python3 bench.py --no-cpu",
+           f"    python3 bench.py --summarize-trace {os.path.relpath(os.path.abspath(stats_csv), ROOT)}",
            "",
-           "bench.py runs 50 warm-up + 200 timed launches per kernel and shape, over rotating buffer sets of at least 1 GiB.",
+           "bench.py launches each kernel and shape untimed for 0.3 s (clock spin-up), then 50 warm-up + 200 timed"
+           " launches, over rotating buffer sets of at least 1 GiB; the averages below cover all of them.",
            "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal>`:",
            "",
            "- `softmax_row<F32,4,2,2,false>`: c1 128x1000 fp32;",
@@ -447,7 +449,8 @@ def summarize_trace(stats_csv):
                 key = (dt, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
                 groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         if groups:
-            out += ["", "Attention dispatches by launch grid (workgroups = 32 heads x 4 batch x queries / 128):", "",
+            out += ["", "Attention dispatches by launch grid (workgroups = 32 heads x 4 batch x queries / 128), from the"
+                    " per-dispatch trace of the same run:", "",
                     "| dtype | workgroups | keys | calls | average ns | min ns |", "|---|---|---|---|---|---|"]
             for (dt, wg), ds in sorted(groups.items()):
                 heads, per_block = 4 * 32, 128  # batch x heads, queries per workgroup
@@ -478,11 +481,13 @@ def summarize_counters(fetch_csv, write_csv):
     write_b = wr[sm] * w_scale * 1024
     total = fetch_b + write_b
     alg = 2 * C3_BYTES
+    rel = lambda f: os.path.relpath(os.path.abspath(f), ROOT)
+    fdir, wdir = os.path.dirname(rel(fetch_csv)), os.path.dirname(rel(write_csv))
     txt = f"""# HBM traffic of the softmax kernel on 8192 x 4096 fp16 (c3_8192x4096_f16), MI355X (gfx950)
 # Two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), run from the repository root:
-#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o c3 -- python3 bench.py --only c3 --no-cpu --steps 20 --warmup 5
-#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o c3 -- python3 bench.py --only c3 --no-cpu --steps 20 --warmup 5
-# then: python3 bench.py --summarize-counters gpurun_out/prof_fetch/c3_counter_collection.csv gpurun_out/prof_write/c3_counter_collection.csv
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o c3 -- python3 bench.py --only c3 --no-cpu --steps 20 --warmup 5
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o c3 -- python3 bench.py --only c3 --no-cpu --steps 20 --warmup 5
+# then: python3 bench.py --summarize-counters {rel(fetch_csv)} {rel(write_csv)}
 # Counters are KiB per dispatch, averaged over each kernel's dispatches, and calibrated with
 # the plain 16-byte copy kernel (softmax_bench_copy) of the same run, which reads and writes
 # exactly {C3_BYTES} bytes: scale = known KiB / counter KiB.  FETCH_SIZE on this part
