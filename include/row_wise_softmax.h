@@ -228,8 +228,8 @@ int softmax_fwd_split(const void *in, void *out, int64_t rows, int64_t cols, int
  * Triton" (sections "Memory Hierarchy: Why Standard Attention Collapses" and
  * "Writing the Kernel in OpenAI Triton"), whose online softmax is this
  * library's merge rule applied per key block.  Both products run on
- * v_mfma_f32_16x16x32_{f16,bf16}; softmax statistics and the accumulator are
- * fp32.
+ * v_mfma_f32_32x32x16_{f16,bf16}; softmax statistics and the accumulator are
+ * fp32, P is rounded to the input type before the second product.
  *   q, o        [batch][heads][nq][head_dim], dense, 16-byte aligned
  *   k, v        [batch][heads][nk][head_dim], dense, 16-byte aligned
  *   head_dim    64 or 128
@@ -238,7 +238,8 @@ int softmax_fwd_split(const void *in, void *out, int64_t rows, int64_t cols, int
  *               to the last query); a query with no kept key gets o = 0
  *   dtype       SOFTMAX_F16 or SOFTMAX_BF16 (q, k, v and o share it)
  * o must not overlap q, k or v; k and v may be NULL when nk == 0.
- * batch * heads <= 65535, nq <= 2^30.
+ * batch * heads <= 65535, nq <= 2^30, nk * head_dim * 2 < 2^31 (K and V of
+ * one head each under 2 GiB).
  * Errors: BAD_DTYPE, BAD_SHAPE (negative sizes, head_dim, misalignment, too
  * large), BAD_SCALE, NULL_POINTER, OVERLAP, HIP.  batch, heads or nq == 0
  * launches nothing.  Same asynchrony and ownership rules as softmax_fwd.

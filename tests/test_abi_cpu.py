@@ -209,4 +209,6 @@ def test_attention_argument_errors(lib):
     assert a(Q + 2, K, V, O, 1, 1, 64, 64, 64, 0.125, 1, 1) == 2   # misaligned
     assert a(Q, K, V, Q + 64, 1, 1, 64, 64, 64, 0.125, 1, 1) == 4  # o overlaps q
     assert a(Q, K, V, O, 300, 300, 64, 64, 64, 0.125, 1, 1) == 2   # batch * heads > 65535
+    assert a(Q, K, V, O, 1, 1, 64, 1 << 23, 128, 0.125, 1, 1) == 2  # K of one head >= 2 GiB
+    assert a(Q, K, V, O, 1, 1, 64, 1 << 24, 64, 0.125, 1, 1) == 2   # (same bytes at head_dim 64)
     assert a(Q, K, V, O, 0, 1, 64, 64, 64, 0.125, 1, 1) == 0       # empty
