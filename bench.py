@@ -511,6 +511,93 @@ traffic_over_algorithmic: {total / alg:.5f}
     print(txt)
 
 
+ATTN_COUNTER_PASSES = [
+    "SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+    "FETCH_SIZE",
+    "WRITE_SIZE",
+]
+
+
+def summarize_attention_counters(csvs):
+    """Write profiles/counters_attention_b4_h32_d128_causal.txt from rocprofv3 --pmc CSVs of
+    `bench.py --attention-only` (one CSV per counter pass)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))  # (kernel, grid) -> counter -> values
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "attention_fwd_kernel" in name:
+                key = ("bf16" if "BF16" in name else "f16", int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+            elif "copy16" in name:
+                key = ("copy16", int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+            else:
+                continue
+            per[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}
+    copy_key = next((k for k in mean if k[0] == "copy16"), None)
+    copy_bytes = 64 << 20
+    lines = ["# Counters of the fused attention forward (causal, batch 4, 32 heads, head dim 128), MI355X (gfx950)",
+             "# One rocprofv3 pass per line, run from the repository root:"]
+    for i, ctr in enumerate(ATTN_COUNTER_PASSES):
+        d = os.path.dirname(os.path.relpath(os.path.abspath(csvs[i]), ROOT)) if i < len(csvs) else "<dir>"
+        lines.append(f"#   rocprofv3 --pmc {ctr} --output-format csv -d {d} -o a -- python3 bench.py --attention-only"
+                     f" --steps 3 --warmup 1")
+    lines += [f"# then: python3 bench.py --summarize-attention-counters "
+              + " ".join(os.path.relpath(os.path.abspath(c), ROOT) for c in csvs),
+              "# Values are per dispatch, averaged over each shape's dispatches.  FETCH_SIZE is scaled by what it",
+              f"# reads for the plain copy kernel of the same run moving {copy_bytes} bytes each way; WRITE_SIZE likewise.",
+              f"source: attention.hip sha {attention_digest()}"]
+    fscale = wscale = None
+    if copy_key and "FETCH_SIZE" in mean[copy_key]:
+        fscale = copy_bytes / 1024 / mean[copy_key]["FETCH_SIZE"]
+    if copy_key and "WRITE_SIZE" in mean[copy_key]:
+        wscale = copy_bytes / 1024 / mean[copy_key]["WRITE_SIZE"]
+    for (dt, wgs), c in sorted(mean.items()):
+        if dt == "copy16":
+            continue
+        n = wgs // 128 * 128  # 128 (batch, head) pairs, 128 queries per workgroup
+        flops = 4.0 * 4 * 32 * 128 * n * (n + 1) / 2
+        lines.append(f"\n[{dt} n={n} ({wgs} workgroups)]")
+        for k in sorted(c):
+            lines.append(f"{k}: {c[k]:.6g}")
+        if "SQ_INSTS_MFMA" in c:
+            lines.append(f"mfma_expected_from_flops: {flops / 32768:.6g}")
+            lines.append(f"valu_per_mfma: {c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA'] - 1:.3f}  (SQ_INSTS_VALU counts the MFMAs too)")
+        if "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"] > 0:
+            lines.append(f"lds_bank_conflict_fraction: {c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.4f}")
+        if "TCC_HIT_sum" in c:
+            lines.append(f"l2_hit_rate: {c['TCC_HIT_sum'] / (c['TCC_HIT_sum'] + c['TCC_MISS_sum']):.4f}")
+        alg = 8.0 * 4 * 32 * n * 128  # Q, K, V read and O written once, 2 bytes each
+        if "FETCH_SIZE" in c and fscale:
+            lines.append(f"hbm_fetch_bytes: {c['FETCH_SIZE'] * 1024 * fscale:.6g}")
+        if "WRITE_SIZE" in c and wscale:
+            lines.append(f"hbm_write_bytes: {c['WRITE_SIZE'] * 1024 * wscale:.6g}")
+        lines.append(f"algorithmic_bytes (q, k, v, o once): {alg:.6g}")
+    txt = "\n".join(lines) + "\n"
+    path = os.path.join(PROFILE_DIR, "counters_attention_b4_h32_d128_causal.txt")
+    open(path, "w").write(txt)
+    print(txt)
+
+
+def attention_digest() -> str:
+    return hashlib.sha256(open(os.path.join(ROOT, "row_wise_softmax_amd", "csrc", "attention.hip"), "rb").read()
+                          ).hexdigest()[:16]
+
+
+def attention_only(steps: int, warmup: int) -> dict:
+    """The attention shapes alone, plus one 64 MiB plain copy to calibrate the byte counters."""
+    import torch
+    n = (64 << 20) // 4
+    a = torch.zeros(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        binding.bench_copy(a.data_ptr(), b.data_ptr(), n * 4, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del a, b
+    return attention_shapes(steps, warmup)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -525,7 +612,14 @@ def main() -> int:
                     help="write profiles/kernel_trace_bench.md from a rocprofv3 --stats CSV and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/counters_c3_8192x4096_f16.txt from two rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time only the attention shapes (and one calibration copy), for counter runs")
+    ap.add_argument("--summarize-attention-counters", nargs="+", metavar="CSV", default=None,
+                    help="write profiles/counters_attention_b4_h32_d128_causal.txt from the rocprofv3 --pmc CSVs")
     args = ap.parse_args()
+    if args.summarize_attention_counters:
+        summarize_attention_counters(args.summarize_attention_counters)
+        return 0
 
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
@@ -547,6 +641,9 @@ def main() -> int:
     binding._load()
     log(f"[bench] {binding.version()} on {torch.cuda.get_device_name(0)}")
 
+    if args.attention_only:
+        print(json.dumps(attention_only(args.steps, args.warmup)), flush=True)
+        return 0
     if args.sweep:
         out = sweep(args.steps, args.warmup)
         if args.sweep_out:

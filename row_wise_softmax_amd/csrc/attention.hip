@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(kThreads, kResident) attention_fwd_kernel(Attn
             for (int jj = 0; jj < 4; ++jj) {
                 const rws::u32x2 pk = {pack2f<E>(oacc[u][4 * jj] * inv, oacc[u][4 * jj + 1] * inv),
                                        pack2f<E>(oacc[u][4 * jj + 2] * inv, oacc[u][4 * jj + 3] * inv)};
-                rws::st<true>(reinterpret_cast<rws::u32x2*>(ob + qi * D + 32 * u + 8 * jj + 4 * h), pk);
+                rws::st<false>(reinterpret_cast<rws::u32x2*>(ob + qi * D + 32 * u + 8 * jj + 4 * h), pk);
             }
     }
 }
