@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(kThreads, kResident) attention_fwd_kernel(Attn
     u32x4 qf[kKS];
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
-        if (qi < a.nq) qf[s] = rws::ld<true>(reinterpret_cast<const u32x4*>(qb + qi * D + 16 * s + 8 * h));
+        if (qi < a.nq) qf[s] = rws::ld<false>(reinterpret_cast<const u32x4*>(qb + qi * D + 16 * s + 8 * h));
         else qf[s] = u32x4{0, 0, 0, 0};
     }
 
