@@ -121,6 +121,21 @@ def test_one_dimensional_heads_match_the_softmax_oracle(oracle_mod, causal):
     assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
 
 
+def test_huge_scores_keep_their_logistic_weights(oracle_mod):
+    """Scores of 1000 and 999 (exp overflows fp64 past 709): only the shift by
+    the row max keeps them finite.  With two keys the weights are the
+    logistic 1/(1+e^-1) and e^-1/(1+e^-1) (closed form), so
+    O = sigma(1) v0 + (1 - sigma(1)) v1 exactly up to rounding."""
+    q = W.cast(np.array([[[[1.0, 0.0]]]]), "f32")
+    k = W.cast(np.array([[[[1000.0, 0.0], [999.0, 0.0]]]]), "f32")
+    v = W.cast(np.array([[[[2.0, -3.0], [5.0, 7.0]]]]), "f32")
+    got = oracle_mod.attention_fwd(q, k, v, "f32", 1.0, causal=False)[0, 0, 0]
+    w0 = 1.0 / (1.0 + np.exp(-1.0))
+    want = w0 * np.array([2.0, -3.0]) + (1.0 - w0) * np.array([5.0, 7.0])
+    assert np.all(np.isfinite(got))
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+
+
 def test_bad_arguments(oracle_mod):
     q, k, v = _qkv(1, 1, 2, 2, 4, "f16", seed=88)
     with pytest.raises(ValueError):

@@ -40,6 +40,10 @@ MUTANTS = {
     "attn_v_transposed": ("o[c] += p * load_element(v, dtype, kb + j * d + c);",
                           "o[c] += p * load_element(v, dtype, kb + c * nk + j);"),
     "attn_unnormalised": ("const double p = s[j] / sum;", "const double p = s[j];"),
+    "attn_no_max_subtraction": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "attn_first_query_only": ("load_element(q, dtype, qb + i * d + c)", "load_element(q, dtype, qb + c)"),
+    "attn_causal_one_future_key": ("kept = i + (nk - nq) + 1;", "kept = i + (nk - nq) + 2;"),
+    "attn_k_row_stride": ("* load_element(k, dtype, kb + j * d + c);", "* load_element(k, dtype, kb + j + c);"),
 }
 
 
