@@ -424,7 +424,7 @@ def summarize_trace(stats_csv):
            " launches, over rotating buffer sets of at least 1 GiB; the averages below cover all of them.",
            "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal>`:",
            "",
-           "- `softmax_row<F32,4,2,2,false>`: c1 128x1000 fp32;",
+           "- `softmax_row<F32,4,4,1,false>`: c1 128x1000 fp32;",
            "- `softmax_row<F32,4,4,2,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
            "- `softmax_row<F32,4,4,2,true>`: c2 with the mask and 1/8 scale fused (raw scores in);",
            "- `softmax_row<F16,8,4,2,false>`: c3 8192x4096 fp16 (the headline);",

@@ -126,8 +126,13 @@ const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t
         } else if (nacc <= 128) {
             e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1);
         } else if (nacc <= 1024) {
-            // one workgroup per row, two accesses per lane, up to 8 waves
-            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
+            // ragged rows of 129..255 accesses: four waves of one access each
+            // (1000 fp32 columns: 6226 GB/s, against 5915 for two waves of two;
+            // at exactly 256 accesses the two-wave shape stays ahead)
+            if (nacc < 256) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, 1, 1);
+            // otherwise one workgroup per row, two accesses per lane, up to 8 waves
+            if (e == nullptr)
+                e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
         } else {
             // wider rows: four waves with more accesses each (8192 fp32 and
             // 16384 bf16 columns ran 4-5% faster this way than spread over
