@@ -93,10 +93,28 @@ __device__ inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ inline u32x4 lds16(const unsigned short* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Exchange with lane ^ 32 (ds_bpermute: byte address of the source lane).
-__device__ inline float xor32(float v) {
-    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, v)));
+// v_permlane32_swap (gfx950) swaps lanes 32..63 of its first operand with
+// lanes 0..31 of its second (measured on the part).  Given v twice it
+// returns, in every lane L, {v[L % 32], v[L % 32 + 32]} in that order: the
+// values of lanes L and L ^ 32, with no LDS round trip, whose max and sum come
+// out bit-identical in both lanes.  (Each element is copied out before the
+// bit cast: a bit cast of the subscripted result read element 0 twice.)
+__device__ inline void pair_of(float v, float* lo, float* hi) {
+    const int b = __builtin_bit_cast(int, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const int r0 = r[0], r1 = r[1];
+    *lo = __builtin_bit_cast(float, r0);
+    *hi = __builtin_bit_cast(float, r1);
+}
+__device__ inline float pair_max(float v) {
+    float lo, hi;
+    pair_of(v, &lo, &hi);
+    return fmaxf(lo, hi);
+}
+__device__ inline float pair_sum(float v) {
+    float lo, hi;
+    pair_of(v, &lo, &hi);
+    return lo + hi;
 }
 
 // Two fp32 -> one dword of the input type, round to nearest even.
@@ -274,7 +292,7 @@ __global__ void __launch_bounds__(kThreads, kResident) attention_fwd_kernel(Attn
         float bm = sc[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sc[r]);
-        bm = fmaxf(bm, xor32(bm)) * a.coef;  // the query's tile max, log2 domain
+        bm = pair_max(bm) * a.coef;  // the query's tile max, log2 domain
         if (__builtin_amdgcn_ballot_w64(bm > m + kSlack)) {
             const float mnew = fmaxf(m, bm);
             const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);  // m = -inf: 0
@@ -366,7 +384,7 @@ __global__ void __launch_bounds__(kThreads, kResident) attention_fwd_kernel(Attn
     }
 
     // Normalise and store: lane holds O[qi][32u + 8j + 4h + r], r = 0..3 (8 bytes).
-    l += xor32(l);
+    l = pair_sum(l);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (qi < a.nq) {
 #pragma unroll
