@@ -134,9 +134,10 @@ const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t
             if (e == nullptr)
                 e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
         } else {
-            // wider rows: four waves with more accesses each (8192 fp32 and
-            // 16384 bf16 columns ran 4-5% faster this way than spread over
-            // 16 waves); where the table has no such shape, 8 or 16 waves
+            // wider rows: four waves with more accesses each (8192 fp32
+            // columns run 4-5% faster this way than spread over 16 waves; for
+            // 16384 bf16 columns the two shapes trade places between machines
+            // by about 4%); where the table has no such shape, 8 or 16 waves
             const int v4 = pow2_at_least((nacc + 255) / 256);
             for (int w = 4; w <= 16 && e == nullptr; w *= 2) {
                 const int v = v4 * 4 / w;
