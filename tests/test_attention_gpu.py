@@ -139,3 +139,35 @@ def test_attention_benchmarked_shape_sampled(dtype):
         worst = max(worst, err)
         assert err <= tol, f"query ({bb}, {hh}, {i}): max abs error {err:.3e} > {tol:.3e}"
     assert not np.isnan(got).any()
+
+
+def test_attention_tensors_beyond_4gib():
+    """18000 heads of 1024 queries and keys, head dim 128, fp16: each of Q, K,
+    V and O is 4.7 GB, so the heads past the 4 GiB mark test the 64-bit head
+    offsets.  Inputs are made on the device by seeded torch ops; 12 sampled
+    (head, query) pairs, the last head included, go back to the oracle."""
+    import torch
+    b, h, n, d = 1, 18000, 1024, 128
+    print(f"[gpu-case] attention beyond 4 GiB: {b}x{h}x{n}x{d}", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cuda").manual_seed(96)
+    q, k, v = (torch.randn((b, h, n, d), generator=g, device="cuda", dtype=torch.float16) for _ in range(3))
+    o = torch.empty_like(q)
+    scale = 1.0 / np.sqrt(d)
+    binding.attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), b, h, n, n, d, scale, True,
+                          W.dtype_code("f16"), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    picks = [(h - 1, n - 1), (h - 1, 0), (h - 2, 517), (h // 2, 1000), (9000, 63), (17000, 64)]
+    picks += [(int(a), int(c)) for a, c in zip(np.random.default_rng(99).integers(16400, h, 6),
+                                               np.random.default_rng(100).integers(0, n, 6))]
+    assert (h - 1) * n * d * 2 > (1 << 32)
+    tol = 4 * 2.0 ** -MANT["f16"] * float(v.abs().max().item())
+    for hh, i in picks:
+        qi = to_host(q[:, hh:hh + 1, i:i + 1].contiguous(), "f16")
+        ki = to_host(k[:, hh:hh + 1, :i + 1].contiguous(), "f16")
+        vi = to_host(v[:, hh:hh + 1, :i + 1].contiguous(), "f16")
+        want = O.attention_fwd(qi, ki, vi, "f16", scale, True)[0, 0, 0]
+        got = decode(to_host(o[0, hh, i].contiguous(), "f16"), "f16")
+        err = float(np.max(np.abs(got - want)))
+        assert err <= tol, f"head {hh}, query {i}: max abs error {err:.3e} > {tol:.3e}"
+    del q, k, v, o
+    torch.cuda.empty_cache()

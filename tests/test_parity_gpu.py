@@ -341,3 +341,30 @@ def test_pages_worked_partition_and_tree(stride):
         y = run(x, "f32", cols=10, kernel_id=k.kid)
         check(y, x, "f32", want, cols=10, label=f"{k.name} stride={stride}")
         check_padding_untouched(y, 10, "f32", label=k.name)
+
+
+# ------------------------------------------------ extents beyond 4 GiB
+
+def test_extent_beyond_4gib():
+    """1,200,000 rows x 1024 fp32 (4.9 GB each way): rows past the 4 GiB mark
+    must come out right, so every byte offset is 64-bit.  The input is made on
+    the device by seeded torch ops (too large to stage from the host), and 64
+    sampled rows, the last ones included, go back to the oracle."""
+    import torch
+    rows, cols = 1_200_000, 1024
+    _say(f"extent beyond 4 GiB: {rows} x {cols} fp32")
+    g = torch.Generator(device="cuda").manual_seed(97)
+    x = torch.randn((rows, cols), generator=g, device="cuda", dtype=torch.float32) * 3.0
+    y = torch.empty_like(x)
+    binding.softmax_fwd(x.data_ptr(), y.data_ptr(), rows, cols, cols, W.dtype_code("f32"),
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    pick = np.unique(np.concatenate([[0, rows // 2, rows - 2, rows - 1],
+                                     np.random.default_rng(98).integers(1_050_000, rows, 60)]))
+    idx = torch.from_numpy(pick).to("cuda")
+    xs = x.index_select(0, idx).cpu().numpy()
+    ys = y.index_select(0, idx).cpu().numpy()
+    assert int(pick.max()) * cols * 4 > (1 << 32)  # the check reaches past 4 GiB
+    check(ys, xs, "f32", O.softmax(xs, "f32"), label="beyond 4 GiB")
+    del x, y
+    torch.cuda.empty_cache()
