@@ -13,11 +13,12 @@
 //
 // Work split: one workgroup of 4 waves per (batch*head, block of 128
 // queries); each wave owns 32 queries and keeps their Q fragments in
-// registers.  Per block of 64 keys the workgroup stages K (row-major) and V
-// (transposed) in LDS; each wave computes its 64 x 32 transposed score tile
-// with MFMA, updates the row statistics in fp32 (exponentials as 2^(x log2 e)
-// on v_exp_f32), rounds P to the input type in registers and accumulates
-// O^T += V^T P^T.  The 32 x 32 x 16 product does twice the work of a
+// registers.  Per block of 64 keys the workgroup stages K and V (both
+// row-major, rows XOR-swizzled) in LDS; each wave computes its 64 x 32
+// transposed score tile with MFMA, updates the row statistics in fp32
+// (exponentials as 2^(x log2 e) on v_exp_f32), rounds P to the input type in
+// registers and accumulates O^T += V^T P^T, reading its V^T operands with
+// the transposing LDS load.  The 32 x 32 x 16 product does twice the work of a
 // 16 x 16 x 32 one for the same 16 bytes of operand per lane, so every K or V
 // fragment read from LDS feeds twice as many flops: LDS bandwidth, not the
 // matrix cores, is what bounds a wave that owns only 16 queries.
