@@ -277,13 +277,21 @@ SOFTMAX_SOURCES = ("kernel_table.hpp", "softmax_abi.hip", "softmax_kernels.hpp",
                    "table_entries.inc", "table_f16.hip", "table_f32.hip")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments or blank lines (comments cannot change a kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_digest() -> str:
-    """Hash of the softmax kernel sources, to tell whether stored counters still apply."""
+    """Hash of the softmax kernel sources' code, to tell whether stored counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "row_wise_softmax_amd", "csrc")
     for name in SOFTMAX_SOURCES:
         h.update(name.encode())
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        h.update(_code_only(open(os.path.join(csrc, name)).read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -547,7 +555,7 @@ def summarize_attention_counters(csvs):
               + " ".join(os.path.relpath(os.path.abspath(c), ROOT) for c in csvs),
               "# Values are per dispatch, averaged over each shape's dispatches.  FETCH_SIZE is scaled by what it",
               f"# reads for the plain copy kernel of the same run moving {copy_bytes} bytes each way; WRITE_SIZE likewise.",
-              f"source: attention.hip sha {attention_digest()}"]
+              f"source_digest (attention.hip code): {attention_digest()}"]
     fscale = wscale = None
     if copy_key and "FETCH_SIZE" in mean[copy_key]:
         fscale = copy_bytes / 1024 / mean[copy_key]["FETCH_SIZE"]
@@ -581,8 +589,9 @@ def summarize_attention_counters(csvs):
 
 
 def attention_digest() -> str:
-    return hashlib.sha256(open(os.path.join(ROOT, "row_wise_softmax_amd", "csrc", "attention.hip"), "rb").read()
-                          ).hexdigest()[:16]
+    """Hash of attention.hip's code (comments ignored)."""
+    src = open(os.path.join(ROOT, "row_wise_softmax_amd", "csrc", "attention.hip")).read()
+    return hashlib.sha256(_code_only(src).encode()).hexdigest()[:16]
 
 
 def attention_only(steps: int, warmup: int) -> dict:

@@ -111,9 +111,11 @@ int pow2_at_least(int64_t v) {
 // The width dispatch rule, set from the width sweep (bench.py --sweep, bf16
 // and fp32, widths 32 ... 16384 at about 200 MB per tensor): up to 1024
 // 16-byte accesses per row the fastest shape keeps about two loads in flight
-// per lane and spreads the row over as many lanes as that takes; wider rows
-// do best on four waves with more loads each.  `nacc` is the row length in
-// 16-byte accesses.  The causal table holds the same picks.
+// per lane and spreads the row over as many lanes as that takes (ragged rows
+// of 129..255 accesses excepted, see below); wider rows do best on four waves
+// with more loads each.  `nacc` is the row length in 16-byte accesses.  The
+// causal table holds the same picks where it has the shape; it has no
+// four-wave, one-access entry, so its ragged rows keep two waves of two.
 const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype,
                           bool causal) {
     const int vec16 = 16 / elem_bytes(dtype);
