@@ -14,9 +14,9 @@
 // ("Dissecting Memory Bandwidth & SRAM Tiling in Triton", section "The
 // Mathematical Remedy: Online Softmax Tiling").
 //
-// Three kernel shapes, all built on 16-byte coalesced accesses and wave64
-// cross-lane reductions (DPP, ds_swizzle, readlane), with no MFMA (there is
-// no contraction here):
+// Four single-launch kernel shapes, all built on 16-byte coalesced accesses
+// and wave64 cross-lane reductions (DPP, ds_swizzle, readlane), with no MFMA
+// (there is no contraction here):
 //   * packed  -- L lanes of one wave per row (L = 1..64), 64/L rows per wave,
 //                G row groups per wave in flight; no LDS, no barrier;
 //   * row     -- one workgroup of W waves per row, the row held in registers,
@@ -26,6 +26,9 @@
 //   * online  -- one workgroup per row of any width: pass 1 streams the row in
 //                chunks keeping a per-lane (max, sum) pair, pass 2 re-reads,
 //                normalises and writes.
+// plus the split-row pair (several workgroups per row: per-tile (max, sum)
+// into a workspace, then merge and normalise) and a plain copy kernel that
+// serves as the bandwidth reference.
 //
 // Arithmetic (all fp32).  In the single-pass kernels the exponentials are
 // 2^(x*c - a) with one FMA and v_exp_f32, where c = scale * log2(e) (scale 1
