@@ -275,19 +275,20 @@ def softmax(x, out=None, kernel_id: int | None = None, causal: bool = False, sca
         raise ValueError("softmax: input must be a GPU tensor")
     code = _torch_dtype_code(x)
     rows, cols, stride = _as_rows(x)
-    if out is None:
-        out = torch.empty_like(x)
+    if out is None:  # same strides as x (empty_like would make a gapped row view contiguous)
+        out = torch.empty_strided(x.shape, x.stride(), dtype=x.dtype, device=x.device)
     if out.shape != x.shape or out.dtype != x.dtype or out.stride() != x.stride() or out.device != x.device:
         raise ValueError("softmax: out must match the input's shape, dtype, strides and device")
-    stream = torch.cuda.current_stream(x.device).cuda_stream
-    if causal:
-        if kernel_id is None:
-            softmax_fwd_causal(x.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag, code, stream)
+    with torch.cuda.device(x.device):  # the library launches on the current device
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        if causal:
+            if kernel_id is None:
+                softmax_fwd_causal(x.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag, code, stream)
+            else:
+                softmax_fwd_causal_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, scale,
+                                          diag, code, stream)
+        elif kernel_id is None:
+            softmax_fwd(x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
         else:
-            softmax_fwd_causal_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag,
-                                      code, stream)
-    elif kernel_id is None:
-        softmax_fwd(x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
-    else:
-        softmax_fwd_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
+            softmax_fwd_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, code, stream)
     return out
