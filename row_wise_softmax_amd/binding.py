@@ -177,12 +177,18 @@ def attention(q, k, v, scale: float | None = None, causal: bool = False, out=Non
     nk = k.shape[2]
     if tuple(k.shape) != (b, h, nk, d) or tuple(v.shape) != (b, h, nk, d):
         raise ValueError("attention: k and v must be [batch, heads, nk, head_dim] matching q")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("attention: q, k, v must be on one device")
     code = _torch_dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    elif (tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("attention: out must be a contiguous tensor of q's shape, dtype and device")
     scale = 1.0 / float(d) ** 0.5 if scale is None else float(scale)
-    attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), b, h, nq, nk, d, scale, causal, code,
-                  torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), b, h, nq, nk, d, scale, causal,
+                      code, torch.cuda.current_stream(q.device).cuda_stream)
     return out
 
 

@@ -11,7 +11,7 @@ from oracle import oracle as O
 from row_wise_softmax_amd import binding
 from row_wise_softmax_amd import workloads as W
 
-from gpu_util import causal_mask, check, to_device, to_host
+from gpu_util import causal_mask, check, decode, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +85,32 @@ def test_argument_errors():
         binding.softmax(torch.zeros(4, 8, device="cuda"), out=torch.zeros(4, 9, device="cuda"))
     with pytest.raises(ValueError):
         binding.softmax(torch.zeros(2, 4, 8, device="cuda").transpose(0, 1))  # rank 3, not contiguous
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_attention_through_the_torch_call(dtype):
+    _say(f"torch api attention {dtype}")
+    rng = np.random.default_rng(116)
+    q, k, v = (W.cast(rng.standard_normal((2, 3, n, 64)), dtype) for n in (150, 170, 170))
+    qd, kd, vd = (to_device(t, dtype) for t in (q, k, v))
+    got = binding.attention(qd, kd, vd, causal=True)  # scale defaults to 1/sqrt(64)
+    want = O.attention_fwd(q, k, v, dtype, 0.125, True)
+    tol = 4 * 2.0 ** -(11 if dtype == "f16" else 8) * float(np.max(np.abs(decode(v, dtype))))
+    assert float(np.max(np.abs(decode(to_host(got, dtype), dtype) - want))) <= tol
+    out = qd.clone()
+    same = binding.attention(qd, kd, vd, scale=0.125, causal=True, out=out)
+    assert same.data_ptr() == out.data_ptr()
+    assert np.array_equal(to_host(out, dtype), to_host(got, dtype))
+
+
+def test_attention_argument_errors():
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        binding.attention(q[0], q[0], q[0])  # rank 3
+    with pytest.raises(ValueError):
+        binding.attention(q, q[:, :, :8], q)  # k and v shapes differ
+    with pytest.raises(ValueError):
+        binding.attention(q, q, q, out=torch.zeros(1, 2, 16, 64, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        binding.attention(q, q, q.transpose(2, 3).contiguous().transpose(2, 3))  # v not contiguous
