@@ -198,14 +198,16 @@ def split_shapes(steps: int, warmup: int) -> dict:
 
 def attention_shapes(steps: int, warmup: int) -> dict:
     """Fused attention forward (MFMA) on the shapes of the attention page's
-    table: batch 4, 32 heads, head dim 128, causal, seeded N(0, 1) inputs."""
+    table: batch 4, 32 heads, head dim 128, causal, context 1024 ... 32768,
+    seeded N(0, 1) inputs drawn on the device."""
     import torch
     out = {}
-    for dt, n in (("f16", 1024), ("f16", 4096), ("bf16", 4096)):
+    # the context lengths of the attention page's table (fp16), and bf16 at 4096
+    for dt, n in (("f16", 1024), ("f16", 4096), ("f16", 8192), ("f16", 16384), ("f16", 32768), ("bf16", 4096)):
         b, h, d = 4, 32, 128
-        g = torch.Generator(device="cpu").manual_seed(7)
+        g = torch.Generator(device="cuda").manual_seed(7)  # drawn on the device: up to 3 GB of inputs
         tdt = torch_dtype(dt)
-        qkv = [torch.randn((b, h, n, d), generator=g).to(tdt).to("cuda") for _ in range(3)]
+        qkv = [torch.randn((b, h, n, d), generator=g, device="cuda", dtype=torch.float32).to(tdt) for _ in range(3)]
         o = torch.empty_like(qkv[0])
         stream = torch.cuda.current_stream().cuda_stream
         code = W.dtype_code(dt)
@@ -214,7 +216,7 @@ def attention_shapes(steps: int, warmup: int) -> dict:
             binding.attention_fwd(qkv[0].data_ptr(), qkv[1].data_ptr(), qkv[2].data_ptr(), o.data_ptr(), b, h, n, n, d,
                                   1.0 / d ** 0.5, True, code, stream)
 
-        reps = max(3, min(steps, 20))
+        reps = max(3, min(steps, 20 if n <= 8192 else 5))
         ms = time_launches(launch, 1, reps, max(1, min(warmup, 3)))
         flops = 4.0 * b * h * d * (n * (n + 1) / 2)  # two products over the kept (causal) keys
         tf = flops / (ms * 1e-3) / 1e12

@@ -171,3 +171,34 @@ def test_attention_tensors_beyond_4gib():
         assert err <= tol, f"head {hh}, query {i}: max abs error {err:.3e} > {tol:.3e}"
     del q, k, v, o
     torch.cuda.empty_cache()
+
+
+def test_attention_longest_benchmarked_context_sampled():
+    """The longest context the benchmark times (batch 4, 32 heads, 32768
+    queries and keys, head dim 128, causal, fp16), run whole; 10 sampled
+    queries, the last ones of a head included, against the oracle.  Inputs are
+    made on the device by seeded torch ops (3 GB)."""
+    import torch
+    b, h, n, d = 4, 32, 32768, 128
+    print(f"[gpu-case] attention longest context: {b}x{h}x{n}x{d}", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cuda").manual_seed(101)
+    q, k, v = (torch.randn((b, h, n, d), generator=g, device="cuda", dtype=torch.float16) for _ in range(3))
+    o = torch.empty_like(q)
+    scale = 1.0 / np.sqrt(d)
+    binding.attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), b, h, n, n, d, scale, True,
+                          W.dtype_code("f16"), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    picks = [(3, 31, n - 1), (0, 0, n - 2), (2, 7, 16383), (1, 20, 30000), (0, 5, 0)]
+    rng = np.random.default_rng(102)
+    picks += [(int(rng.integers(b)), int(rng.integers(h)), int(rng.integers(n))) for _ in range(5)]
+    tol = 4 * 2.0 ** -MANT["f16"] * float(v.abs().max().item())
+    for bb, hh, i in picks:
+        qi = to_host(q[bb:bb + 1, hh:hh + 1, i:i + 1].contiguous(), "f16")
+        ki = to_host(k[bb:bb + 1, hh:hh + 1, :i + 1].contiguous(), "f16")
+        vi = to_host(v[bb:bb + 1, hh:hh + 1, :i + 1].contiguous(), "f16")
+        want = O.attention_fwd(qi, ki, vi, "f16", scale, True)[0, 0, 0]
+        got = decode(to_host(o[bb, hh, i].contiguous(), "f16"), "f16")
+        err = float(np.max(np.abs(got - want)))
+        assert err <= tol, f"query ({bb}, {hh}, {i}): max abs error {err:.3e} > {tol:.3e}"
+    del q, k, v, o
+    torch.cuda.empty_cache()
