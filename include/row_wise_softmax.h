@@ -233,7 +233,9 @@ int softmax_fwd_split(const void *in, void *out, int64_t rows, int64_t cols, int
  *   q, o        [batch][heads][nq][head_dim], dense, 16-byte aligned
  *   k, v        [batch][heads][nk][head_dim], dense, 16-byte aligned
  *   head_dim    64 or 128
- *   scale       > 0 with scale * log2(e) below 3e38 (typically 1/sqrt(head_dim))
+ *   scale       > 0 with scale * log2(e) below 3e38 (typically 1/sqrt(head_dim));
+ *               every scaled score scale * q.k * log2(e) must also be finite in
+ *               fp32 (magnitude below about 3e38), or outputs may be NaN
  *   causal      0, or 1: query i keeps keys j <= i + (nk - nq) (the mask aligned
  *               to the last query); a query with no kept key gets o = 0
  *   dtype       SOFTMAX_F16 or SOFTMAX_BF16 (q, k, v and o share it)
