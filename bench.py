@@ -694,9 +694,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": head["dtype"],
+        "dtype": "f32",  # the arithmetic: every kernel widens to fp32 and accumulates there
         "data": "synthetic (seeded N(0,1), resident in HBM, rotating buffers > Infinity Cache)",
         "config": {"workload": head["workload"], "rows": head["rows"], "cols": head["cols"],
+                   "storage_dtype": head["dtype"],
                    "kernel": head["kernel"], "buffers": head["buffers"], "peak_gbps": PEAK_GBPS,
                    "copy_kernel_gbps": head.get("copy_kernel_gbps"), "memcpy_gbps": head.get("memcpy_gbps")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
