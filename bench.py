@@ -36,6 +36,10 @@ from row_wise_softmax_amd import binding  # noqa: E402
 from row_wise_softmax_amd import workloads as W  # noqa: E402
 
 METRIC = "achieved HBM GB/s (2·rows·cols·bytes/time) and % of MI355X peak, per shape"
+# The pages' own figure for the same metric and shape: 8192 x 4096 fp16 at about
+# 2.8 TB/s (134.2 MB in 48 us) on an H100 ("fused-softmax-roofline", its
+# results).  Another machine's number: vs_baseline is context, not a target.
+PAGES_GBPS = 2800.0
 PEAK_GBPS = 8000.0
 HEADLINE = "c3"
 FIXED = ["c1", "c2", "c3", "c4"]
@@ -693,7 +697,7 @@ def main() -> int:
         "ms_per_step": round(head["us"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": round(achieved / PAGES_GBPS, 3) if HEADLINE == "c3" else None,
         "dtype": "f32",  # the arithmetic: every kernel widens to fp32 and accumulates there
         "data": "synthetic (seeded N(0,1), resident in HBM, rotating buffers > Infinity Cache)",
         "config": {"workload": head["workload"], "rows": head["rows"], "cols": head["cols"],
