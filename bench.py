@@ -419,6 +419,7 @@ def sweep(steps: int, warmup: int) -> list:
             del res
     # the narrow/wide crossover: widest width a packed kernel wins, narrowest a
     # one-workgroup-per-row kernel wins
+    crossings = []
     for dt in ("bf16", "f32"):
         mine = [r for r in rows_out if r["dtype"] == dt]
         packed = [r["cols"] for r in mine if r["best"].startswith("packed")]
@@ -426,8 +427,8 @@ def sweep(steps: int, warmup: int) -> list:
         cross = {"crossover": dt, "packed_wins_up_to_cols": max(packed) if packed else None,
                  "row_wins_from_cols": min(row) if row else None}
         log(json.dumps(cross))
-        rows_out.append(cross)
-    return rows_out
+        crossings.append(cross)
+    return rows_out + crossings
 
 
 # ------------------------------------------------------------ profile summaries

@@ -216,6 +216,25 @@ int64_t resident_workgroups(const Entry& e, int block) {
     return n;
 }
 
+// Whether a row-kernel launch shifts rows onto 128-byte lines (the kernels'
+// line_shift): only for 16-byte accesses, only when some row starts inside a
+// line, and only when the workgroup has a spare slot for every access the
+// largest shift pushes past its last slot.  Row r's shift is
+// (out / 16 + r * pitch / 16) mod 8, a sequence with period at most 8.
+bool line_shift_fits(const Entry& e, const void* out, int64_t cols, int64_t row_stride) {
+    if (e.variant != SOFTMAX_VARIANT_ROW && e.variant != SOFTMAX_VARIANT_ROW_PF) return false;
+    const int64_t esz = elem_bytes(e.dtype);
+    if (e.vec * esz != 16) return false;
+    const int64_t base = int64_t((uintptr_t(out) >> 4) & 7), pitch = ((row_stride * esz) >> 4) & 7;
+    int64_t most = 0;
+    for (int64_t r = 0; r < 8; ++r) {
+        const int64_t sh = (base + r * pitch) & 7;
+        most = sh > most ? sh : most;
+    }
+    const int64_t slots = int64_t(e.lanes) * e.vpl;
+    return most > 0 && slots >= cols / e.vec + most;
+}
+
 int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, float coef,
            int64_t diag, hipStream_t stream) {
     rws::Args a;
@@ -227,6 +246,7 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     a.nacc = int(cols / e.vec);
     a.cols = int(cols);
     a.coef = coef;
+    a.align = line_shift_fits(e, out, cols, row_stride) ? 1 : 0;
     int block;
     if (e.variant == SOFTMAX_VARIANT_PACKED) {
         const int64_t rows_per_wave = int64_t(64 / e.lanes) * e.groups;

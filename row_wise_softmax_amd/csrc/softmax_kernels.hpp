@@ -307,7 +307,26 @@ struct Args {
     int nacc;         // accesses per row (cols / access width)
     int cols;         // elements per row
     float coef;       // scale * log2(e); log2(e) for the plain softmax
+    int align;        // row kernels: shift each row's accesses onto 128-byte lines
 };
+
+// Line shift of one row.  A 128-byte line holds 8 accesses of 16 bytes.  With
+// the shift s = (address of the row's output / 16) mod 8, thread slot p holds
+// access p - s, so every wave's store instruction covers whole lines and only
+// the row's first and last lines are split with its neighbours.  Rows whose
+// width is not a multiple of 128 bytes otherwise split a line at every wave
+// boundary.  The host enables it only when the workgroup has at least s spare
+// slots for every row.
+constexpr int kLineAccesses = 8;
+
+template <class E, int N>
+__device__ inline int line_shift(const void* row_out, const Args& a) {
+    if constexpr (N * E::kBytes != 16) {
+        return 0;
+    } else {
+        return a.align ? int((reinterpret_cast<uintptr_t>(row_out) >> 4) & (kLineAccesses - 1)) : 0;
+    }
+}
 
 // Columns row `row` keeps: all of them, or j <= row + diag for the causal
 // (scaled, masked) softmax of "Dissecting Memory Bandwidth & SRAM Tiling in
@@ -325,13 +344,14 @@ __device__ inline int kept_cols(int64_t row, const Args& a) {
 }
 
 // Load access `idx` of a row into f, or -inf where the row has nothing to
-// give: past its end, or (causal) past its kept columns.  A causal access
+// give: before its start (a line-shifted slot), past its end, or (causal)
+// past its kept columns.  A causal access
 // wholly past the kept columns is not read at all; the one that straddles
 // them is read and its masked elements set to -inf.
 template <class E, int N, bool Causal, bool Keep = false>
 __device__ inline void load_access(const typename Access<E, N>::raw* p, int idx, int nacc, int kept, float* f) {
     if constexpr (!Causal) {
-        if (idx < nacc) {
+        if (idx >= 0 && idx < nacc) {
             load_elems<E, N, Keep>(p, f);
         } else {
 #pragma unroll
@@ -339,7 +359,7 @@ __device__ inline void load_access(const typename Access<E, N>::raw* p, int idx,
         }
     } else {
         const int first = idx * N;
-        if (first < kept) {
+        if (idx >= 0 && first < kept) {
             load_elems<E, N, Keep>(p, f);
             if (first + N > kept) {
 #pragma unroll
@@ -418,16 +438,19 @@ __global__ void __launch_bounds__(256) softmax_packed(Args a) {
 // --------------------------------------------------------------- row kernel
 //
 // One workgroup of W waves per row; thread t owns accesses t, t + 64W, ...
-// The row stays in registers between the max, the exponentials and the
-// store.  Two barriers per row: after the per-wave maxima reach LDS and after
-// the per-wave sums do (separate slots, so no third barrier guards reuse).
+// less the row's line shift (see line_shift).  The row stays in registers
+// between the max, the exponentials and the store.  Two barriers per row:
+// after the per-wave maxima reach LDS and after the per-wave sums do
+// (separate slots, so no third barrier guards reuse).
 
+// Thread t loads accesses i0, i0 + 64W, ... of the row, i0 = t - s (s: the
+// row's line shift); p addresses access i0.
 template <class E, int N, int W, int V, bool Causal>
-__device__ inline void load_row(const typename Access<E, N>::raw* p, int t, int nacc, int kept,
+__device__ inline void load_row(const typename Access<E, N>::raw* p, int i0, int nacc, int kept,
                                 float (&x)[V][N]) {
     constexpr int kThreads = W * kWave;
 #pragma unroll
-    for (int v = 0; v < V; ++v) load_access<E, N, Causal>(p + v * kThreads, v * kThreads + t, nacc, kept, x[v]);
+    for (int v = 0; v < V; ++v) load_access<E, N, Causal>(p + v * kThreads, v * kThreads + i0, nacc, kept, x[v]);
 }
 
 // Max, exponentials, sum and the normalised store of one row held in x.
@@ -436,8 +459,8 @@ __device__ inline void load_row(const typename Access<E, N>::raw* p, int t, int 
 // red_sum before the next call's first barrier, so the slots can be reused
 // without a third barrier.
 template <class E, int N, int W, int V>
-__device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* q, int t, int nacc, float coef,
-                                  float* red_max, float* red_sum) {
+__device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* q, int t, int i0, int nacc,
+                                  float coef, float* red_max, float* red_sum) {
     constexpr int kThreads = W * kWave;
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
@@ -469,7 +492,8 @@ __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* 
 
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-        if (v * kThreads + t < nacc) {
+        const int idx = v * kThreads + i0;
+        if (idx >= 0 && idx < nacc) {
 #pragma unroll
             for (int e = 0; e < N; ++e) x[v][e] *= r;
             store_elems<E, N>(q + v * kThreads, x[v]);
@@ -487,8 +511,9 @@ __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
     const int t = threadIdx.x;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         float x[V][N];
-        load_row<E, N, W, V, Causal>(in + row * a.stride + t, t, a.nacc, kept_cols<Causal>(row, a), x);
-        finish_row<E, N, W, V>(x, out + row * a.stride + t, t, a.nacc, a.coef, red_max, red_sum);
+        const int i0 = t - line_shift<E, N>(out + row * a.stride, a);
+        load_row<E, N, W, V, Causal>(in + row * a.stride + i0, i0, a.nacc, kept_cols<Causal>(row, a), x);
+        finish_row<E, N, W, V>(x, out + row * a.stride + i0, t, i0, a.nacc, a.coef, red_max, red_sum);
     }
 }
 
@@ -510,17 +535,21 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
     int64_t row = blockIdx.x;
     if (row >= a.rows) return;  // uniform per workgroup: no barrier is skipped by part of it
     float nx[V][N];
-    load_row<E, N, W, V, Causal>(in + row * a.stride + t, t, a.nacc, kept_cols<Causal>(row, a), nx);
+    int ni0 = t - line_shift<E, N>(out + row * a.stride, a);
+    load_row<E, N, W, V, Causal>(in + row * a.stride + ni0, ni0, a.nacc, kept_cols<Causal>(row, a), nx);
     for (; row < a.rows; row += gridDim.x) {
         float x[V][N];
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
             for (int e = 0; e < N; ++e) x[v][e] = nx[v][e];
+        const int i0 = ni0;
         const int64_t next = row + gridDim.x;
-        if (next < a.rows)
-            load_row<E, N, W, V, Causal>(in + next * a.stride + t, t, a.nacc, kept_cols<Causal>(next, a), nx);
-        finish_row<E, N, W, V>(x, out + row * a.stride + t, t, a.nacc, a.coef, red_max, red_sum);
+        if (next < a.rows) {
+            ni0 = t - line_shift<E, N>(out + next * a.stride, a);
+            load_row<E, N, W, V, Causal>(in + next * a.stride + ni0, ni0, a.nacc, kept_cols<Causal>(next, a), nx);
+        }
+        finish_row<E, N, W, V>(x, out + row * a.stride + i0, t, i0, a.nacc, a.coef, red_max, red_sum);
     }
 }
 

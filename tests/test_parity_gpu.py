@@ -14,7 +14,7 @@ from oracle import oracle as O
 from row_wise_softmax_amd import binding
 from row_wise_softmax_amd import workloads as W
 
-from gpu_util import TOL, causal_mask, check, check_padding_untouched, decode, run, to_device, to_host
+from gpu_util import TOL, causal_mask, check, check_padding_untouched, decode, run, sentinel, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -368,3 +368,64 @@ def test_extent_beyond_4gib():
     check(ys, xs, "f32", O.softmax(xs, "f32"), label="beyond 4 GiB")
     del x, y
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------- line-shifted row kernels
+
+_ROW_KERNELS = [k for k in _TABLE if k.variant in ("row", "row_pf") and k.vec_elems * (4 if k.dtype == 0 else 2) == 16]
+
+
+def _at_offset(host: np.ndarray, dtype: str, off: int, fill: int):
+    """A device copy of host starting `off` bytes into a buffer whose other bytes hold `fill`."""
+    import torch
+    esz = 4 if dtype == "f32" else 2
+    n = host.size * esz
+    raw = torch.full((n + 512,), fill, dtype=torch.uint8, device="cuda")
+    view = raw[off:off + n].view(torch.float32 if dtype == "f32" else torch.int16).view(host.shape)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(host).view(np.float32 if dtype == "f32" else np.int16)))
+    return raw, view
+
+
+@pytest.mark.parametrize("kid", [k.kid for k in _ROW_KERNELS], ids=[k.name for k in _ROW_KERNELS])
+def test_line_shifted_rows(kid):
+    """Row kernels move each row's accesses onto 128-byte lines when the
+    workgroup has spare slots.  Here the width leaves exactly 7 spare slots,
+    the pitch is an odd number of 16-byte accesses (so the rows' shifts take
+    all 8 values) and input and output start at different offsets within a
+    line; the output's padding and the bytes around it must stay untouched."""
+    import torch
+    k = _TABLE[kid]
+    dtype = _DT[k.dtype]
+    esz = 4 if dtype == "f32" else 2
+    slots = k.lanes * k.vecs_per_lane
+    nacc = slots - 7
+    cols = nacc * k.vec_elems
+    pitch = nacc if nacc % 2 else nacc + 1
+    stride = pitch * k.vec_elems
+    rows = _rows_for(k, cols)
+    _say(f"line-shifted {k.name} rows={rows} cols={cols} stride={stride}")
+    x = W.random_matrix(seed=300 + kid, rows=rows, cols=cols, dtype=dtype, sigma=3.0, row_stride=stride)
+    x[2, : cols // 2] = W.neg_inf(dtype)
+    in_raw, xd = _at_offset(x, dtype, 80, 0)
+    pad = np.full_like(x, sentinel(dtype))
+    out_raw, yd = _at_offset(pad, dtype, 48, 0xA5)
+    out_addr = yd.data_ptr()
+    shifts = {((out_addr >> 4) + r * pitch) & 7 for r in range(8)}
+    assert max(shifts) == 7 and slots >= nacc + 7  # every shift value occurs and fits
+    stream = torch.cuda.current_stream().cuda_stream
+    code = W.dtype_code(dtype)
+    if k.causal:
+        diag = cols // 2 - rows // 2
+        binding.softmax_fwd_causal_kernel(kid, xd.data_ptr(), out_addr, rows, cols, stride, 0.5, diag, code, stream)
+    else:
+        binding.softmax_fwd_kernel(kid, xd.data_ptr(), out_addr, rows, cols, stride, code, stream)
+    torch.cuda.synchronize()
+    y = to_host(yd, dtype)
+    if k.causal:
+        check(y, x, dtype, O.softmax_causal(x, dtype, 0.5, diag, cols=cols), cols=cols, label=k.name,
+              keep=causal_mask(rows, cols, diag))
+    else:
+        check(y, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=k.name)
+    check_padding_untouched(y, cols, dtype, label=k.name)
+    around = out_raw.cpu().numpy()
+    assert (around[:48] == 0xA5).all() and (around[48 + y.nbytes:] == 0xA5).all(), "bytes outside the output written"
