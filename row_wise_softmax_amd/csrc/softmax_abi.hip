@@ -109,13 +109,12 @@ int pow2_at_least(int64_t v) {
 }
 
 // The width dispatch rule, set from the width sweep (bench.py --sweep, bf16
-// and fp32, widths 32 ... 16384 at about 200 MB per tensor): up to 1024
+// and fp32, widths 32 ... 16384 at about 200 MB per tensor): up to 2048
 // 16-byte accesses per row the fastest shape keeps about two loads in flight
 // per lane and spreads the row over as many lanes as that takes (ragged rows
 // of 129..255 accesses excepted, see below); wider rows do best on four waves
 // with more loads each.  `nacc` is the row length in 16-byte accesses.  The
-// causal table holds the same picks where it has the shape; it has no
-// four-wave, one-access entry, so its ragged rows keep two waves of two.
+// causal table holds the same picks.
 const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype,
                           bool causal) {
     const int vec16 = 16 / elem_bytes(dtype);
@@ -127,19 +126,21 @@ const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t
             e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, pow2_at_least(nacc), 1, 2);
         } else if (nacc <= 128) {
             e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1);
-        } else if (nacc <= 1024) {
+        } else if (nacc <= 2048) {
             // ragged rows of 129..255 accesses: four waves of one access each
             // (1000 fp32 columns: 6226 GB/s, against 5915 for two waves of two;
             // at exactly 256 accesses the two-wave shape stays ahead)
             if (nacc < 256) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, 1, 1);
-            // otherwise one workgroup per row, two accesses per lane, up to 8 waves
+            // otherwise one workgroup per row, two accesses per lane, up to 16
+            // waves (2048 accesses, 16384 bf16 columns: 6150 GB/s on sixteen
+            // waves against 5600 on four waves of eight; 8192 fp32 columns:
+            // 6220 against 6117)
             if (e == nullptr)
                 e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
         } else {
-            // wider rows: four waves with more accesses each (8192 fp32
-            // columns run 4-5% faster this way than spread over 16 waves; for
-            // 16384 bf16 columns the two shapes trade places between machines
-            // by about 4%); where the table has no such shape, 8 or 16 waves
+            // wider rows: four waves with more accesses each (16384 fp32
+            // columns: 5825 GB/s, against 5625 on eight waves and 5613 on
+            // sixteen); where the table has no such shape, 8 or 16 waves
             const int v4 = pow2_at_least((nacc + 255) / 256);
             for (int w = 4; w <= 16 && e == nullptr; w *= 2) {
                 const int v = v4 * 4 / w;

@@ -156,6 +156,20 @@ def test_dispatch_always_picks_a_fitting_kernel(lib, dtype, cols, causal):
     assert binding.kernel_table()[kid2].causal == causal
 
 
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_causal_dispatch_takes_the_plain_shapes(lib, dtype):
+    """Across the sweep's widths the scaled, masked softmax runs the same
+    kernel shape as the plain one: the causal table holds every such pick."""
+    table = binding.kernel_table()
+    esz = 4 if dtype == 0 else 2
+    for cols in (8, 32, 64, 128, 256, 512, 1000, 1024, 2048, 3000, 4096, 8192, 16384):
+        if (cols * esz) % 16:
+            continue
+        plain = table[binding.softmax_select(A, B, cols, cols, dtype, rows=4)].name
+        masked = table[binding.softmax_select(A, B, cols, cols, dtype, rows=4, causal=True)].name
+        assert masked == "causal_" + plain, (cols, plain, masked)
+
+
 def test_bench_copy_argument_errors(lib):
     assert lib.softmax_bench_copy(A, B, 15, None) == 2
     assert lib.softmax_bench_copy(A + 4, B, 16, None) == 2
