@@ -23,6 +23,7 @@ struct Entry {
     int groups;   // packed: row groups per wave; else 1
     int block;    // threads per workgroup (packed: maximum)
     const void* fn;
+    const void* fn_shifted;  // row kernels: the line-shifted instantiation; else null
     const char* name;
 };
 

@@ -247,7 +247,6 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     a.nacc = int(cols / e.vec);
     a.cols = int(cols);
     a.coef = coef;
-    a.align = line_shift_fits(e, out, cols, row_stride) ? 1 : 0;
     int block;
     if (e.variant == SOFTMAX_VARIANT_PACKED) {
         const int64_t rows_per_wave = int64_t(64 / e.lanes) * e.groups;
@@ -266,7 +265,8 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     }
     const int64_t grid = a.nblocks < kMaxGrid ? a.nblocks : kMaxGrid;
     void* args[] = {&a};
-    hipError_t rc = hipLaunchKernel(e.fn, dim3(unsigned(grid)), dim3(unsigned(block)), args, 0, stream);
+    const void* fn = (e.fn_shifted != nullptr && line_shift_fits(e, out, cols, row_stride)) ? e.fn_shifted : e.fn;
+    hipError_t rc = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(unsigned(block)), args, 0, stream);
     if (rc != hipSuccess) {
         (void)hipGetLastError();  // do not leave our failure for the caller's next check
         return SOFTMAX_ERR_HIP;

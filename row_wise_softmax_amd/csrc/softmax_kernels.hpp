@@ -307,7 +307,6 @@ struct Args {
     int nacc;         // accesses per row (cols / access width)
     int cols;         // elements per row
     float coef;       // scale * log2(e); log2(e) for the plain softmax
-    int align;        // row kernels: shift each row's accesses onto 128-byte lines
 };
 
 // Line shift of one row.  A 128-byte line holds 8 accesses of 16 bytes.  With
@@ -315,16 +314,18 @@ struct Args {
 // access p - s, so every wave's store instruction covers whole lines and only
 // the row's first and last lines are split with its neighbours.  Rows whose
 // width is not a multiple of 128 bytes otherwise split a line at every wave
-// boundary.  The host enables it only when the workgroup has at least s spare
-// slots for every row.
+// boundary.  The row kernels take the shift as a template flag (Shift), so
+// unshifted launches run code without it (computing it costs a row kernel
+// whose rows all start at once about 7%); the host picks the shifted
+// instantiation only when the workgroup has spare slots for every row's shift.
 constexpr int kLineAccesses = 8;
 
-template <class E, int N>
-__device__ inline int line_shift(const void* row_out, const Args& a) {
-    if constexpr (N * E::kBytes != 16) {
+template <class E, int N, bool Shift>
+__device__ inline int line_shift(const void* row_out) {
+    if constexpr (!Shift || N * E::kBytes != 16) {
         return 0;
     } else {
-        return a.align ? int((reinterpret_cast<uintptr_t>(row_out) >> 4) & (kLineAccesses - 1)) : 0;
+        return int((reinterpret_cast<uintptr_t>(row_out) >> 4) & (kLineAccesses - 1));
     }
 }
 
@@ -501,7 +502,7 @@ __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* 
     }
 }
 
-template <class E, int N, int W, int V, bool Causal>
+template <class E, int N, int W, int V, bool Causal, bool Shift = false>
 __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
     typedef typename Access<E, N>::raw raw;
     __shared__ float red_max[W];
@@ -511,7 +512,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
     const int t = threadIdx.x;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         float x[V][N];
-        const int i0 = t - line_shift<E, N>(out + row * a.stride, a);
+        const int i0 = t - line_shift<E, N, Shift>(out + row * a.stride);
         load_row<E, N, W, V, Causal>(in + row * a.stride + i0, i0, a.nacc, kept_cols<Causal>(row, a), x);
         finish_row<E, N, W, V>(x, out + row * a.stride + i0, t, i0, a.nacc, a.coef, red_max, red_sum);
     }
@@ -524,7 +525,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
 // before the current row is reduced, so its HBM reads overlap the current
 // row's reductions, exponentials and stores.  The grid is sized to the
 // number of workgroups the chip holds at once.
-template <class E, int N, int W, int V, bool Causal>
+template <class E, int N, int W, int V, bool Causal, bool Shift = false>
 __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
     typedef typename Access<E, N>::raw raw;
     __shared__ float red_max[W];
@@ -535,7 +536,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
     int64_t row = blockIdx.x;
     if (row >= a.rows) return;  // uniform per workgroup: no barrier is skipped by part of it
     float nx[V][N];
-    int ni0 = t - line_shift<E, N>(out + row * a.stride, a);
+    int ni0 = t - line_shift<E, N, Shift>(out + row * a.stride);
     load_row<E, N, W, V, Causal>(in + row * a.stride + ni0, ni0, a.nacc, kept_cols<Causal>(row, a), nx);
     for (; row < a.rows; row += gridDim.x) {
         float x[V][N];
@@ -546,7 +547,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
         const int i0 = ni0;
         const int64_t next = row + gridDim.x;
         if (next < a.rows) {
-            ni0 = t - line_shift<E, N>(out + next * a.stride, a);
+            ni0 = t - line_shift<E, N, Shift>(out + next * a.stride);
             load_row<E, N, W, V, Causal>(in + next * a.stride + ni0, ni0, a.nacc, kept_cols<Causal>(next, a), nx);
         }
         finish_row<E, N, W, V>(x, out + row * a.stride + i0, t, i0, a.nacc, a.coef, red_max, red_sum);
