@@ -325,14 +325,22 @@ def cpu_baseline(res: Resident, budget_s: float) -> dict:
     wl = res.wl
     x = res.x_host
     times = []
-    t_all = time.perf_counter()
-    ref = None
-    while True:
-        t0 = time.perf_counter()
-        ref = oracle.softmax(x, wl.dtype)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_all >= budget_s:
-            break
+    # pinned to one core of those this process may use (the calling thread
+    # only), so the figure does not move with the scheduler's migrations
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        t_all = time.perf_counter()
+        ref = None
+        while True:
+            t0 = time.perf_counter()
+            ref = oracle.softmax(x, wl.dtype)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_all >= budget_s:
+                break
+    finally:
+        os.sched_setaffinity(0, allowed)
     mean = sum(times) / len(times)
     # The oracle's result also checks the benchmarked GPU output (recomputed
     # here: the copy-ceiling timings reuse the output buffers).
@@ -349,7 +357,7 @@ def cpu_baseline(res: Resident, budget_s: float) -> dict:
     err = float(np.max(np.abs(yd - ref)))
     out = {"value": round(wl.bytes / mean / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"the whole {wl.name} input, {len(times)} run(s), {mean:.2f} s each, "
-                     f"single-threaded fp64 C, same GB/s formula",
+                     f"single-threaded fp64 C pinned to core {core}, same GB/s formula",
            "gpu_max_abs_err_vs_oracle": err}
     out["all_threads"] = oracle_threaded(x, wl, max(2.0, budget_s / 3))
     return out
