@@ -310,11 +310,11 @@ struct Args {
 };
 
 // Line shift of one row.  A 128-byte line holds 8 accesses of 16 bytes.  With
-// the shift s = (address of the row's output / 16) mod 8, thread slot p holds
-// access p - s, so every wave's store instruction covers whole lines and only
-// the row's first and last lines are split with its neighbours.  Rows whose
-// width is not a multiple of 128 bytes otherwise split a line at every wave
-// boundary.  The row kernels take the shift as a template flag (Shift), so
+// the shift s = (address of the row's output / 16) mod 8, the row kernels'
+// slot p (see first_access) holds access p - s, so every store instruction
+// covers whole lines and only the row's first and last lines are split with
+// its neighbours.  Rows whose width is not a multiple of 128 bytes otherwise
+// split a line at every instruction's 1 KiB boundary.  The row kernels take the shift as a template flag (Shift), so
 // unshifted launches run code without it (computing it costs a row kernel
 // whose rows all start at once about 7%); the host picks the shifted
 // instantiation only when the workgroup has spare slots for every row's shift.
