@@ -202,3 +202,36 @@ def test_attention_longest_benchmarked_context_sampled():
         assert err <= tol, f"query ({bb}, {hh}, {i}): max abs error {err:.3e} > {tol:.3e}"
     del q, k, v, o
     torch.cuda.empty_cache()
+
+
+def _random_case(case):
+    rng = np.random.default_rng([83, case])
+    d = int(rng.choice([64, 128]))
+    b, h = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    nq = int(rng.integers(1, 700))
+    nk = int(rng.choice([nq, int(rng.integers(0, 700))]))
+    dtype = ["f16", "bf16"][int(rng.integers(0, 2))]
+    causal = bool(rng.random() < 0.5)
+    scale = float(rng.uniform(0.02, 0.4))
+    sigma = float(rng.uniform(0.3, 3.0))
+    return b, h, nq, nk, d, dtype, causal, scale, sigma
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_attention_random_shapes(case):
+    """Seeded random batch, heads, query and key counts (equal or not, keys
+    possibly none), head dim, dtype, causality, scale and input spread."""
+    b, h, nq, nk, d, dtype, causal, scale, sigma = _random_case(case)
+    print(f"[gpu-case] attention random #{case}: {dtype} b{b} h{h} nq{nq} nk{nk} d{d} causal={causal}",
+          file=sys.stderr, flush=True)
+    rng = np.random.default_rng([84, case])
+    q = W.cast(sigma * rng.standard_normal((b, h, nq, d)), dtype)
+    k = W.cast(sigma * rng.standard_normal((b, h, nk, d)), dtype)
+    v = W.cast(rng.standard_normal((b, h, nk, d)), dtype)
+    got = _run(q, k, v, dtype, scale, causal)
+    want = O.attention_fwd(q, k, v, dtype, scale, causal)
+    vmax = float(np.max(np.abs(decode(v, dtype)))) if v.size else 1.0
+    tol = 4 * 2.0 ** -MANT[dtype] * max(vmax, 1.0)
+    assert not np.isnan(got).any()
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert err <= tol, f"max abs error {err:.3e} > {tol:.3e}"
