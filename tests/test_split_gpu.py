@@ -103,3 +103,27 @@ def test_split_benchmarked_shapes(key):
     print(f"[gpu-case] split full size {wl.name}", file=sys.stderr, flush=True)
     y = _run_split(x, wl.dtype, force=0)
     check(y, x, wl.dtype, O.softmax(x, wl.dtype), label=f"split {wl.name}")
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_split_random_calls(case):
+    """Seeded random rows (1..40), widths (1..300000, log-uniform), padding,
+    dtype, pointer offset (aligned or not), in place or not, forced split or
+    the library's choice; padding must stay untouched."""
+    rng = np.random.default_rng([79, case])
+    dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+    cols = max(1, int(round(float(np.exp(rng.uniform(0.0, np.log(300000.0)))))))
+    rows = int(rng.integers(1, 41))
+    stride = cols + int(rng.choice([0, 0, 8, 13]))
+    offset = int(rng.choice([0, 0, 0, 1, 8]))
+    inplace = bool(rng.random() < 0.2)
+    force = int(rng.integers(0, 2))
+    print(f"[gpu-case] split random #{case}: {dtype} rows={rows} cols={cols} stride={stride} offset={offset} "
+          f"inplace={inplace} force={force}", file=sys.stderr, flush=True)
+    x = W.random_matrix(seed=700 + case, rows=rows, cols=cols, dtype=dtype, sigma=float(rng.uniform(0.5, 4.0)),
+                        row_stride=stride)
+    x[0, : cols // 3] = W.neg_inf(dtype)
+    y = _run_split(x, dtype, cols=cols, force=force, inplace=inplace, offset=offset)
+    check(y, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"split random #{case}")
+    if not inplace:
+        check_padding_untouched(y, cols, dtype, label=f"split random #{case}")
