@@ -441,6 +441,36 @@ def sweep(steps: int, warmup: int) -> list:
 
 # ------------------------------------------------------------ profile summaries
 
+def summarize_sweep(sweep_json: str) -> None:
+    """Write profiles/sweep_c5_widths.md (the crossover report) from `bench.py --sweep --sweep-out` JSON."""
+    rows = json.load(open(sweep_json))
+    src = os.path.relpath(os.path.abspath(sweep_json), ROOT)
+    out = ["# Width sweep on MI355X (gfx950): every plain table kernel at every c5 width", "",
+           "Commands (repository root):", "",
+           f"    python3 bench.py --sweep --sweep-out {src}",
+           f"    python3 bench.py --summarize-sweep {src}", "",
+           "About 200 MB of input per tensor, rotating buffer sets of at least 1 GiB, 0.3 s spin-up per width; GB/s by",
+           "the metric's 2·rows·cols·size bytes.  `pick` is the kernel the width dispatch chooses, `best` the fastest",
+           "kernel measured; the last column lists the next four.", "",
+           "| dtype | cols | rows | pick | pick GB/s | best | best GB/s | next |", "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        if "cols" not in r:
+            continue
+        nxt = ", ".join(f"{n} {g:.0f}" for n, g in r["top5"][1:5])
+        out.append(f"| {r['dtype']} | {r['cols']} | {r['rows']} | {r['dispatch']} | {r['dispatch_gbps']:.0f} | "
+                   f"{r['best']} | {r['best_gbps']:.0f} | {nxt} |")
+    out.append("")
+    for r in rows:
+        if "crossover" in r:
+            out.append(f"- {r['crossover']}: the packed kernel (several rows per wave) wins up to "
+                       f"{r['packed_wins_up_to_cols']} columns; one workgroup per row wins from "
+                       f"{r['row_wins_from_cols']} columns.")
+    path = os.path.join(ROOT, "profiles", "sweep_c5_widths.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
+
+
 C3_BYTES = 8192 * 4096 * 2  # input bytes of the headline workload (8192 x 4096 fp16)
 
 
@@ -648,6 +678,8 @@ def main() -> int:
                     help="write profiles/counters_c3_8192x4096_f16.txt from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the attention shapes (and one calibration copy), for counter runs")
+    ap.add_argument("--summarize-sweep", metavar="SWEEP_JSON", default=None,
+                    help="write profiles/sweep_c5_widths.md from a --sweep-out file")
     ap.add_argument("--summarize-attention-counters", nargs="+", metavar="CSV", default=None,
                     help="write profiles/counters_attention_b4_h32_d128_causal.txt from the rocprofv3 --pmc CSVs")
     args = ap.parse_args()
@@ -655,6 +687,9 @@ def main() -> int:
         summarize_attention_counters(args.summarize_attention_counters)
         return 0
 
+    if args.summarize_sweep:
+        summarize_sweep(args.summarize_sweep)
+        return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return 0
