@@ -465,7 +465,7 @@ def summarize_sweep(sweep_json: str) -> None:
             out.append(f"- {r['crossover']}: the packed kernel (several rows per wave) wins up to "
                        f"{r['packed_wins_up_to_cols']} columns; one workgroup per row wins from "
                        f"{r['row_wins_from_cols']} columns.")
-    path = os.path.join(ROOT, "profiles", "sweep_c5_widths.md")
+    path = os.path.join(PROFILE_DIR, "sweep_c5_widths.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
     print(path)
@@ -485,13 +485,14 @@ def summarize_trace(stats_csv):
            "",
            "bench.py launches each kernel and shape untimed for 0.3 s (clock spin-up), then 50 warm-up + 200 timed"
            " launches, over rotating buffer sets of at least 1 GiB; the averages below cover all of them.",
-           "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal>`:",
+           "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal,"
+           " line shift>`:",
            "",
-           "- `softmax_row<F32,4,4,1,false>`: c1 128x1000 fp32;",
-           "- `softmax_row<F32,4,4,2,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
-           "- `softmax_row<F32,4,4,2,true>`: c2 with the mask and 1/8 scale fused (raw scores in);",
-           "- `softmax_row<F16,8,4,2,false>`: c3 8192x4096 fp16 (the headline);",
-           "- `softmax_row<F32,4,8,2,false>`: c4 4096x4096 fp32;",
+           "- `softmax_row<F32,4,4,1,false,true>`: c1 128x1000 fp32 (4000-byte rows, line-shifted);",
+           "- `softmax_row<F32,4,4,2,false,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
+           "- `softmax_row<F32,4,4,2,true,false>`: c2 with the mask and 1/8 scale fused (raw scores in);",
+           "- `softmax_row<F16,8,4,2,false,false>`: c3 8192x4096 fp16 (the headline);",
+           "- `softmax_row<F32,4,8,2,false,false>`: c4 4096x4096 fp32;",
            "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape;",
            "- `unfused_reduce` / `unfused_elementwise`: the five-kernel unfused softmax on c3 and c4 (max, sub, exp, sum, div);",
            "- `softmax_online` (single pass) and `softmax_split_stats` + `softmax_split_norm` (split rows):"

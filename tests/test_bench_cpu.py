@@ -1,0 +1,104 @@
+"""Host logic of bench.py, on the CPU: the one-GPU refusal, the counter
+calibration and its source-digest guard, and the profile summaries.  Every
+summary is written into a temporary directory, never over the committed
+profiles."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.fixture
+def profile_dir(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    return tmp_path
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line for a run that did not happen
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counter_calibration_and_digest_guard(profile_dir, tmp_path):
+    """The copy kernel moves exactly C3_BYTES each way, so its counter reading
+    fixes the scale; the softmax's bytes are its reading times that scale."""
+    kib = bench.C3_BYTES / 1024
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    sm, cp = "void rws::softmax_row<rws::F16, 8, 4, 2, false, false>(rws::Args)", "void rws::copy16<4>(...)"
+    # FETCH reads half the true bytes, WRITE reads them exactly; the softmax re-reads 1% of its input
+    _counter_csv(fetch, "FETCH_SIZE", [(cp, kib / 2), (cp, kib / 2), (sm, 1.01 * kib / 2)])
+    _counter_csv(write, "WRITE_SIZE", [(cp, kib), (sm, kib), (sm, kib)])
+    bench.summarize_counters(str(fetch), str(write))
+    got = bench.stored_traffic("c3_8192x4096_f16")
+    assert got is not None
+    assert got["bytes"] == pytest.approx(2.01 * bench.C3_BYTES, rel=1e-6)
+    text = (profile_dir / "counters_c3_8192x4096_f16.txt").read_text()
+    assert f"source_digest: {bench.source_digest()}" in text
+    assert "traffic_over_algorithmic: 1.00500" in text
+    # counters taken on other kernel sources are not reported
+    (profile_dir / "counters_c3_8192x4096_f16.txt").write_text(
+        text.replace(bench.source_digest(), "0000000000000000"))
+    assert bench.stored_traffic("c3_8192x4096_f16") is None
+
+
+def test_digest_ignores_comments_only(tmp_path):
+    code = "int f(int x) {  // add one\n    return x + 1;  /* done */\n}\n"
+    assert bench._code_only(code) == bench._code_only(code.replace("add one", "increment"))
+    assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
+
+
+def test_sweep_summary(profile_dir, tmp_path):
+    rows = [
+        {"workload": "w", "dtype": "bf16", "cols": 64, "rows": 10, "dispatch": "packed_a", "dispatch_gbps": 6400.0,
+         "best": "packed_a", "best_gbps": 6400.0, "top5": [["packed_a", 6400.0], ["row_b", 6000.0]]},
+        {"workload": "w", "dtype": "bf16", "cols": 4096, "rows": 10, "dispatch": "row_c", "dispatch_gbps": 6300.0,
+         "best": "row_d", "best_gbps": 6350.0, "top5": [["row_d", 6350.0], ["row_c", 6300.0]]},
+        {"crossover": "bf16", "packed_wins_up_to_cols": 64, "row_wins_from_cols": 4096},
+    ]
+    src = tmp_path / "sweep.json"
+    src.write_text(json.dumps(rows))
+    bench.summarize_sweep(str(src))
+    text = (profile_dir / "sweep_c5_widths.md").read_text()
+    assert "| bf16 | 64 | 10 | packed_a | 6400 | packed_a | 6400 | row_b 6000 |" in text
+    assert "| bf16 | 4096 | 10 | row_c | 6300 | row_d | 6350 | row_c 6300 |" in text
+    assert "wins up to 64 columns; one workgroup per row wins from 4096 columns" in text
+
+
+def test_trace_summary_groups_attention_by_grid(profile_dir, tmp_path):
+    stats = tmp_path / "bench_kernel_stats.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow({"Name": "void rws::softmax_row<rws::F16, 8, 4, 2, false, false>(rws::Args)", "Calls": 3,
+                    "AverageNs": 22306.4, "MinNs": 20478, "MaxNs": 32076})
+    trace = tmp_path / "attn_trace.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp",
+                                          "End_Timestamp"])
+        w.writeheader()
+        for start, end in ((0, 1000), (5000, 7000)):
+            w.writerow({"Kernel_Name": "attention_fwd_kernel<rws::F16, 128, true>", "Grid_Size_X": 1024 * 256,
+                        "Workgroup_Size_X": 256, "Start_Timestamp": start, "End_Timestamp": end})
+    bench.summarize_trace(str(stats))
+    text = (profile_dir / "kernel_trace_bench.md").read_text()
+    assert "| 3 | 22306 | 20478 | 32076 |" in text
+    assert "| f16 | 1024 | 1024 | 2 | 1500 | 1000 |" in text
