@@ -343,6 +343,42 @@ def test_pages_worked_partition_and_tree(stride):
         check_padding_untouched(y, 10, "f32", label=k.name)
 
 
+# "Dissecting Memory Bandwidth & SRAM Tiling in Triton", section "Writing the
+# Kernel in OpenAI Triton": a row of 6 columns read by a block of 8 lanes
+# takes the mask [T, T, T, T, T, T, F, F]; the two masked lanes must add
+# nothing.  Here the two columns past the row hold a huge finite value, so a
+# kernel that read them would get another max and another sum.  The same
+# shape is run at the level of elements (6 of 8 columns, scalar accesses) and
+# of 16-byte accesses (6 of 8 accesses), through every table kernel that fits.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("unit", ["element", "access"])
+def test_pages_mask_example(dtype, unit):
+    mask = np.arange(8) < 6
+    assert mask.tolist() == [True] * 6 + [False] * 2  # the pages' mask for n_cols 6, BLOCK 8
+    vec = 16 // (4 if dtype == "f32" else 2)
+    per = 1 if unit == "element" else vec
+    cols, stride = 6 * per, 8 * per
+    rng = np.random.default_rng([31, per])
+    x = np.full((5, stride), 3.0e4)
+    x[:, :cols] = 2.0 * rng.standard_normal((5, cols))
+    x[1, : cols // 2] = -np.inf
+    x = W.cast(x, dtype)
+    want = O.softmax(x, dtype, cols=cols)
+    ran = 0
+    for k in _TABLE:
+        if k.causal or k.dtype != W.dtype_code(dtype):
+            continue
+        xd = to_device(x, dtype)
+        if not binding.kernel_fits(k.kid, xd.data_ptr(), xd.data_ptr(), cols, stride, W.dtype_code(dtype)):
+            continue
+        _say(f"mask example {k.name} cols={cols} stride={stride}")
+        y = run(x, dtype, cols=cols, kernel_id=k.kid)
+        check(y, x, dtype, want, cols=cols, label=f"{k.name} {unit}")
+        check_padding_untouched(y, cols, dtype, label=k.name)
+        ran += 1
+    assert ran > 0
+
+
 # ------------------------------------------------ extents beyond 4 GiB
 
 def test_extent_beyond_4gib():
