@@ -663,6 +663,64 @@ def attention_only(steps: int, warmup: int) -> dict:
     return attention_shapes(steps, warmup)
 
 
+def wide_only(steps: int, warmup: int) -> dict:
+    """The few-wide-rows shapes alone, plus one 64 MiB plain copy to calibrate the byte counters."""
+    import torch
+    n = (64 << 20) // 4
+    a = torch.zeros(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        binding.bench_copy(a.data_ptr(), b.data_ptr(), n * 4, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del a, b
+    return split_shapes(steps, warmup)
+
+
+def summarize_wide_counters(fetch_csv, write_csv):
+    """Write profiles/counters_wide_rows.txt: HBM bytes per dispatch of the
+    single-pass online kernel and of the two split-row kernels on the few-wide-
+    rows shapes, from two rocprofv3 --pmc runs of `bench.py --wide-only`."""
+
+    def avg(f, counter):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in d.items()}
+
+    fe, wr = avg(fetch_csv, "FETCH_SIZE"), avg(write_csv, "WRITE_SIZE")
+    cp = next(k for k in fe if "copy16" in k)
+    kib = (64 << 20) / 1024
+    f_scale, w_scale = kib / fe[cp], kib / wr[cp]
+    tensors = {"F32": ("wide_f32", W.WORKLOADS["wide_f32"]), "BF16": ("wide_bf16", W.WORKLOADS["wide_bf16"])}
+    rel = lambda f: os.path.relpath(os.path.abspath(f), ROOT)
+    fdir, wdir = os.path.dirname(rel(fetch_csv)), os.path.dirname(rel(write_csv))
+    lines = [
+        "# HBM traffic of the single-pass online kernel and of the split-row kernels on few, wide rows, MI355X (gfx950)",
+        "# Two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), run from the repository root:",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o w -- python3 bench.py --wide-only --steps 20 --warmup 5",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o w -- python3 bench.py --wide-only --steps 20 --warmup 5",
+        f"# then: python3 bench.py --summarize-wide-counters {rel(fetch_csv)} {rel(write_csv)}",
+        "# KiB per dispatch averaged over each kernel's dispatches, calibrated with a 64 MiB plain copy of the same run",
+        f"# (fetch scale {f_scale:.4f}, write scale {w_scale:.4f}).  Bytes are per launch, over rotating buffer sets of at",
+        "# least 1 GiB, so every launch's first read comes from HBM; 'x input' divides by the tensor's bytes.",
+        f"source_digest: {source_digest()}", ""]
+    for name in sorted(fe):
+        if not any(t in name for t in ("softmax_online", "softmax_split_stats", "softmax_split_norm")):
+            continue
+        elem = "BF16" if "BF16" in name else "F32"
+        key, wl = tensors[elem]
+        size = wl.rows * wl.cols * (4 if elem == "F32" else 2)
+        fb, wb = fe[name] * f_scale * 1024, wr.get(name, 0.0) * w_scale * 1024
+        lines.append(f"{name[:72]}  [{key} {wl.rows}x{wl.cols}]")
+        lines.append(f"  fetch_bytes: {fb:.0f}  ({fb / size:.3f} x input)")
+        lines.append(f"  write_bytes: {wb:.0f}  ({wb / size:.3f} x input)")
+    path = os.path.join(PROFILE_DIR, "counters_wide_rows.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -679,6 +737,10 @@ def main() -> int:
                     help="write profiles/counters_c3_8192x4096_f16.txt from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the attention shapes (and one calibration copy), for counter runs")
+    ap.add_argument("--wide-only", action="store_true",
+                    help="time only the few-wide-rows shapes (and one calibration copy), for counter runs")
+    ap.add_argument("--summarize-wide-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write profiles/counters_wide_rows.txt from two rocprofv3 --pmc CSVs of --wide-only")
     ap.add_argument("--summarize-sweep", metavar="SWEEP_JSON", default=None,
                     help="write profiles/sweep_c5_widths.md from a --sweep-out file")
     ap.add_argument("--summarize-attention-counters", nargs="+", metavar="CSV", default=None,
@@ -690,6 +752,9 @@ def main() -> int:
 
     if args.summarize_sweep:
         summarize_sweep(args.summarize_sweep)
+        return 0
+    if args.summarize_wide_counters:
+        summarize_wide_counters(*args.summarize_wide_counters)
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
@@ -713,6 +778,9 @@ def main() -> int:
 
     if args.attention_only:
         print(json.dumps(attention_only(args.steps, args.warmup)), flush=True)
+        return 0
+    if args.wide_only:
+        print(json.dumps(wide_only(args.steps, args.warmup)), flush=True)
         return 0
     if args.sweep:
         out = sweep(args.steps, args.warmup)
