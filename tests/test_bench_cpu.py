@@ -102,3 +102,19 @@ def test_trace_summary_groups_attention_by_grid(profile_dir, tmp_path):
     text = (profile_dir / "kernel_trace_bench.md").read_text()
     assert "| 3 | 22306 | 20478 | 32076 |" in text
     assert "| f16 | 1024 | 1024 | 2 | 1500 | 1000 |" in text
+
+
+def test_wide_counter_summary(profile_dir, tmp_path):
+    """Each kernel's bytes are its counter reading times the copy's calibration,
+    reported against its own tensor's bytes."""
+    kib = (64 << 20) / 1024
+    f32_kib = 8 * (1 << 20) * 4 / 1024
+    online = "void rws::softmax_online<rws::F32, 4, 16, 4, false>(rws::Args)"
+    cp = "void rws::copy16<4>(...)"
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [(cp, kib / 2), (online, 1.5 * f32_kib / 2)])
+    _counter_csv(write, "WRITE_SIZE", [(cp, kib), (online, f32_kib)])
+    bench.summarize_wide_counters(str(fetch), str(write))
+    text = (profile_dir / "counters_wide_rows.txt").read_text()
+    assert "[wide_f32 8x1048576]" in text
+    assert "(1.500 x input)" in text and "(1.000 x input)" in text
