@@ -226,3 +226,28 @@ def test_attention_argument_errors(lib):
     assert a(Q, K, V, O, 1, 1, 64, 1 << 23, 128, 0.125, 1, 1) == 2  # K of one head >= 2 GiB
     assert a(Q, K, V, O, 1, 1, 64, 1 << 24, 64, 0.125, 1, 1) == 2   # (same bytes at head_dim 64)
     assert a(Q, K, V, O, 0, 1, 64, 64, 64, 0.125, 1, 1) == 0       # empty
+
+
+# The width dispatch's picks at the BASELINE configs and the sweep widths (the
+# "pick" column of the measured sweep); a change to the rule must change this
+# table knowingly.
+_PICKS = {
+    ("f32", 1000): "row_f32_w4_v1", ("f32", 2048): "row_f32_w4_v2", ("f16", 4096): "row_f16_w4_v2",
+    ("f32", 4096): "row_f32_w8_v2",
+    ("bf16", 32): "packed_bf16_l4_v1_g2", ("bf16", 64): "packed_bf16_l8_v1_g2", ("bf16", 128): "packed_bf16_l16_v1_g2",
+    ("bf16", 256): "packed_bf16_l32_v1_g2", ("bf16", 512): "packed_bf16_l64_v1_g2",
+    ("bf16", 1000): "packed_bf16_l64_v2_g1", ("bf16", 1024): "packed_bf16_l64_v2_g1", ("bf16", 2048): "row_bf16_w2_v2",
+    ("bf16", 3000): "row_bf16_w4_v2", ("bf16", 4096): "row_bf16_w4_v2", ("bf16", 8192): "row_bf16_w8_v2",
+    ("bf16", 16384): "row_bf16_w16_v2",
+    ("f32", 32): "packed_f32_l8_v1_g2", ("f32", 64): "packed_f32_l16_v1_g2", ("f32", 128): "packed_f32_l32_v1_g2",
+    ("f32", 256): "packed_f32_l64_v1_g2", ("f32", 512): "packed_f32_l64_v2_g1", ("f32", 1024): "row_f32_w2_v2",
+    ("f32", 3000): "row_f32_w8_v2", ("f32", 8192): "row_f32_w16_v2", ("f32", 16384): "row_f32_w4_v16",
+}
+
+
+@pytest.mark.parametrize("key", sorted(_PICKS), ids=[f"{d}-{c}" for d, c in sorted(_PICKS)])
+def test_dispatch_picks_the_measured_shapes(lib, key):
+    dtype, cols = key
+    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    kid = binding.softmax_select(A, B, cols, cols, code, rows=4)
+    assert binding.kernel_table()[kid].name == _PICKS[key]
