@@ -191,7 +191,8 @@ def split_shapes(steps: int, warmup: int) -> dict:
              "single_pass_kernel": kernel_name(res), "single_pass_us": round(one * 1e3, 3),
              "single_pass_gbps": round(wl.bytes / (one * 1e-3) / 1e9, 1),
              "split_us": round(spl * 1e3, 3), "split_gbps": round(wl.bytes / (spl * 1e-3) / 1e9, 1),
-             "note": "gbps by the metric's 2*rows*cols*size bytes; the split path moves up to 1.5x that"}
+             "note": "gbps by the metric's 2*rows*cols*size bytes; in the counter runs (profiles/counters_wide_rows.txt) "
+                     "the single-pass online kernel moved 1.00-1.04x and the split path 1.5x those bytes"}
         log(f"[bench] {wl.name}: softmax_fwd {d['single_pass_us']} us ({d['single_pass_gbps']} GB/s)"
             f"  split {d['split_us']} us ({d['split_gbps']} GB/s)")
         out[key] = d
