@@ -27,7 +27,7 @@ def _gpu():
 
 
 # (dtype, rows, cols): shapes the dispatch sends to the packed, row, online and line-shifted row kernels
-_JOBS = [("f32", 300, 96), ("bf16", 120, 4096), ("f16", 20, 40000), ("f32", 64, 3000)]
+_JOBS = [("f32", 300, 96), ("bf16", 120, 4096), ("f16", 8, 70000), ("f32", 64, 3000)]
 
 
 def test_threads_on_their_own_streams():
