@@ -104,6 +104,44 @@ def time_launches(launch, n_buf: int, steps: int, warmup: int, spin_s: float = S
     return start.elapsed_time(stop) / steps
 
 
+def time_graph(res, n_launch: int, replays: int = 5) -> float:
+    """Mean ms per launch when `n_launch` softmax launches (cycling the buffer
+    sets) are captured in one HIP graph and the graph is replayed: the same
+    kernels without the host's per-launch cost, which bounds the eager rate of
+    launches a few microseconds long."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    eager_stream = res.stream
+    try:
+        res.stream = side.cuda_stream
+        with torch.cuda.stream(side):  # warm-up off the capture, as torch asks
+            for i in range(3):
+                res.softmax(i % res.n)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            res.stream = torch.cuda.current_stream().cuda_stream
+            for i in range(n_launch):
+                res.softmax(i % res.n)
+    finally:
+        res.stream = eager_stream
+    torch.cuda.synchronize()
+    graph.replay()  # untimed
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    start.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (replays * n_launch)
+    graph.reset()
+    return ms
+
+
 class Resident:
     """R copies of one input in HBM plus R outputs."""
 
@@ -265,6 +303,10 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfus
         d["copy_kernel_gbps"] = round(wl.bytes / (cms * 1e-3) / 1e9, 1)
         d["memcpy_gbps"] = round(wl.bytes / (mms * 1e-3) / 1e9, 1)
         d["frac_of_copy"] = round(gbps / d["copy_kernel_gbps"], 4)
+    # The same launches replayed from one captured graph: no host cost per launch.
+    gms = time_graph(res, max(steps, res.n))
+    d["graph_us"] = round(gms * 1e3, 3)
+    d["graph_gbps"] = round(wl.bytes / (gms * 1e-3) / 1e9, 1)
     # Warm: one buffer pair launched over and over, so input and output stay in
     # the 256 MB Infinity Cache (and, for small shapes, in L2).  Not HBM-bound;
     # reported for reference only, never as the shape's number.
