@@ -6,8 +6,11 @@ its ctypes binding and the seeded input generators.  PyTorch is used only for
 device memory and streams.
 """
 from .binding import (  # noqa: F401
+    attention,
+    attention_fwd,
     softmax,
     softmax_fwd,
+    softmax_fwd_split,
     softmax_fwd_causal,
     softmax_fwd_kernel,
     softmax_select,
