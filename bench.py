@@ -706,6 +706,35 @@ def attention_only(steps: int, warmup: int) -> dict:
     return attention_shapes(steps, warmup)
 
 
+def result_line(head: dict, shapes: dict, steps: int, warmup: int, cpu: dict | None, traffic: dict | None) -> dict:
+    """The one JSON line: the headline shape's achieved GB/s as `value`, its roofline, the CPU baseline
+    and every measured shape."""
+    achieved = head["gbps"]
+    return {
+        "metric": METRIC,
+        "value": achieved,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(head["us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(achieved / PAGES_GBPS, 3) if HEADLINE == "c3" else None,
+        "dtype": "f32",  # the arithmetic: every kernel widens to fp32 and accumulates there
+        "data": "synthetic (seeded N(0,1), resident in HBM, rotating buffers > Infinity Cache)",
+        "config": {"workload": head["workload"], "rows": head["rows"], "cols": head["cols"],
+                   "storage_dtype": head["dtype"],
+                   "kernel": head["kernel"], "buffers": head["buffers"], "peak_gbps": PEAK_GBPS,
+                   "copy_kernel_gbps": head.get("copy_kernel_gbps"), "memcpy_gbps": head.get("memcpy_gbps")},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": (round(traffic["bytes"]) if traffic else None)},
+        "cpu_baseline": cpu,
+        "shapes": {k: {kk: vv for kk, vv in v.items() if kk != "_res"} for k, v in shapes.items()},
+    }
+
+
 def wide_only(steps: int, warmup: int) -> dict:
     """The few-wide-rows shapes alone, plus one 64 MiB plain copy to calibrate the byte counters."""
     import torch
@@ -851,31 +880,7 @@ def main() -> int:
     if not args.no_cpu:
         log(f"[bench] cpu baseline: oracle on {head['workload']} for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(res, args.cpu_seconds)
-    traffic = stored_traffic(head["workload"])
-    achieved = head["gbps"]
-    line = {
-        "metric": METRIC,
-        "value": achieved,
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(head["us"] / 1e3, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": round(achieved / PAGES_GBPS, 3) if HEADLINE == "c3" else None,
-        "dtype": "f32",  # the arithmetic: every kernel widens to fp32 and accumulates there
-        "data": "synthetic (seeded N(0,1), resident in HBM, rotating buffers > Infinity Cache)",
-        "config": {"workload": head["workload"], "rows": head["rows"], "cols": head["cols"],
-                   "storage_dtype": head["dtype"],
-                   "kernel": head["kernel"], "buffers": head["buffers"], "peak_gbps": PEAK_GBPS,
-                   "copy_kernel_gbps": head.get("copy_kernel_gbps"), "memcpy_gbps": head.get("memcpy_gbps")},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBPS, 4),
-                     "traffic": (round(traffic["bytes"]) if traffic else None)},
-        "cpu_baseline": cpu,
-        "shapes": {k: {kk: vv for kk, vv in v.items() if kk != "_res"} for k, v in shapes.items()},
-    }
+    line = result_line(head, shapes, args.steps, args.warmup, cpu, stored_traffic(head["workload"]))
     print(json.dumps(line), flush=True)
     return 0
 

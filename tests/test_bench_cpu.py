@@ -118,3 +118,26 @@ def test_wide_counter_summary(profile_dir, tmp_path):
     text = (profile_dir / "counters_wide_rows.txt").read_text()
     assert "[wide_f32 8x1048576]" in text
     assert "(1.500 x input)" in text and "(1.000 x input)" in text
+
+
+def test_result_line_contract():
+    """The JSON line's fields, from a stand-in measurement of the headline shape."""
+    head = {"workload": "c3_8192x4096_f16", "rows": 8192, "cols": 4096, "dtype": "f16", "kernel": "row_f16_w4_v2",
+            "buffers": 8, "us": 23.0, "gbps": 5835.6, "copy_kernel_gbps": 5900.0, "memcpy_gbps": 5100.0,
+            "_res": object()}
+    cpu = {"value": 0.4, "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": "s"}
+    line = bench.result_line(head, {"c3": head}, 200, 50, cpu, {"bytes": 134223438.2})
+    json.dumps(line)  # serialisable: the resources handle is dropped
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in line
+    assert line["value"] == 5835.6 and line["unit"] == "GB/s" and line["n_gpus"] == 1
+    assert line["ms_per_step"] == 0.023 and line["higher_is_better"] is True and line["scaling"] == "weak"
+    assert line["config"]["workload"] == "c3_8192x4096_f16" and "model" not in line["config"]
+    assert line["vs_baseline"] == round(5835.6 / 2800.0, 3)
+    r = line["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["frac"] == round(5835.6 / 8000.0, 4) and r["traffic"] == 134223438
+    assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] == 1
+    assert "_res" not in line["shapes"]["c3"]
+    assert bench.result_line(head, {}, 1, 1, None, None)["roofline"]["traffic"] is None
