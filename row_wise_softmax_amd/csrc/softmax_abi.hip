@@ -115,8 +115,8 @@ int pow2_at_least(int64_t v) {
 // of 129..255 accesses excepted, see below); wider rows do best on four waves
 // with more loads each.  `nacc` is the row length in 16-byte accesses.  The
 // causal table holds the same picks.
-const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype,
-                          bool causal) {
+const Entry* select_entry(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
+                          int dtype, bool causal) {
     const int vec16 = 16 / elem_bytes(dtype);
     if (aligned16(in, out, cols, row_stride, dtype)) {
         const int64_t nacc = cols / vec16;
@@ -129,8 +129,15 @@ const Entry* select_entry(const void* in, const void* out, int64_t cols, int64_t
         } else if (nacc <= 2048) {
             // ragged rows of 129..255 accesses: four waves of one access each
             // (1000 fp32 columns: 6226 GB/s, against 5915 for two waves of two;
-            // at exactly 256 accesses the two-wave shape stays ahead)
-            if (nacc < 256) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, 1, 1);
+            // at exactly 256 accesses the two-wave shape stays ahead).  fp32
+            // tensors of 8192 rows or more take two accesses per lane on the
+            // same four waves, half the slots idle: 0.5-5% faster at 520, 600,
+            // 700, 800 and 1000 columns with 8 K-49 K rows, but up to 4%
+            // slower with 1 K rows, and 15-25% slower for bf16 at any count.
+            if (nacc < 256) {
+                const int v = dtype == SOFTMAX_F32 && rows >= 8192 ? 2 : 1;
+                e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, v, 1);
+            }
             // otherwise one workgroup per row, two accesses per lane, up to 16
             // waves (2048 accesses, 16384 bf16 columns: 6150 GB/s on sixteen
             // waves against 5600 on four waves of eight; 8192 fp32 columns:
@@ -282,7 +289,7 @@ int fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_strid
     float coef = float(kLog2eD);
     if (causal && !coef_of(scale, &coef)) return SOFTMAX_ERR_BAD_SCALE;
     if (empty) return SOFTMAX_OK;
-    const Entry* e = select_entry(in, out, cols, row_stride, dtype, causal);
+    const Entry* e = select_entry(in, out, rows, cols, row_stride, dtype, causal);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
     return launch(*e, in, out, rows, cols, row_stride, coef, diag, static_cast<hipStream_t>(stream));
 }
@@ -308,7 +315,7 @@ int select_id(const void* in, const void* out, int64_t rows, int64_t cols, int64
     int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
     if (st != SOFTMAX_OK) return st;
     const Entry* e =
-        select_entry(in, out, cols > 0 ? cols : 1, row_stride > 0 ? row_stride : 1, dtype, causal);
+        select_entry(in, out, rows, cols > 0 ? cols : 1, row_stride > 0 ? row_stride : 1, dtype, causal);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
     *kernel_id = id_of(e);
     return SOFTMAX_OK;

@@ -228,26 +228,38 @@ def test_attention_argument_errors(lib):
     assert a(Q, K, V, O, 0, 1, 64, 64, 64, 0.125, 1, 1) == 0       # empty
 
 
-# The width dispatch's picks at the BASELINE configs and the sweep widths (the
-# "pick" column of the measured sweep); a change to the rule must change this
-# table knowingly.
+# The width dispatch's picks at the BASELINE configs and the sweep widths, at
+# those workloads' row counts (the "pick" column of the measured sweep); a
+# change to the rule must change this table knowingly.
 _PICKS = {
-    ("f32", 1000): "row_f32_w4_v1", ("f32", 2048): "row_f32_w4_v2", ("f16", 4096): "row_f16_w4_v2",
-    ("f32", 4096): "row_f32_w8_v2",
-    ("bf16", 32): "packed_bf16_l4_v1_g2", ("bf16", 64): "packed_bf16_l8_v1_g2", ("bf16", 128): "packed_bf16_l16_v1_g2",
-    ("bf16", 256): "packed_bf16_l32_v1_g2", ("bf16", 512): "packed_bf16_l64_v1_g2",
-    ("bf16", 1000): "packed_bf16_l64_v2_g1", ("bf16", 1024): "packed_bf16_l64_v2_g1", ("bf16", 2048): "row_bf16_w2_v2",
-    ("bf16", 3000): "row_bf16_w4_v2", ("bf16", 4096): "row_bf16_w4_v2", ("bf16", 8192): "row_bf16_w8_v2",
-    ("bf16", 16384): "row_bf16_w16_v2",
-    ("f32", 32): "packed_f32_l8_v1_g2", ("f32", 64): "packed_f32_l16_v1_g2", ("f32", 128): "packed_f32_l32_v1_g2",
-    ("f32", 256): "packed_f32_l64_v1_g2", ("f32", 512): "packed_f32_l64_v2_g1", ("f32", 1024): "row_f32_w2_v2",
-    ("f32", 3000): "row_f32_w8_v2", ("f32", 8192): "row_f32_w16_v2", ("f32", 16384): "row_f32_w4_v16",
+    "c1": "row_f32_w4_v1", "c2": "row_f32_w4_v2", "c3": "row_f16_w4_v2", "c4": "row_f32_w8_v2",
+    "c5_bf16_32": "packed_bf16_l4_v1_g2", "c5_bf16_64": "packed_bf16_l8_v1_g2", "c5_bf16_128": "packed_bf16_l16_v1_g2",
+    "c5_bf16_256": "packed_bf16_l32_v1_g2", "c5_bf16_512": "packed_bf16_l64_v1_g2",
+    "c5_bf16_1000": "packed_bf16_l64_v2_g1", "c5_bf16_1024": "packed_bf16_l64_v2_g1", "c5_bf16_2048": "row_bf16_w2_v2",
+    "c5_bf16_3000": "row_bf16_w4_v2", "c5_bf16_4096": "row_bf16_w4_v2", "c5_bf16_8192": "row_bf16_w8_v2",
+    "c5_bf16_16384": "row_bf16_w16_v2",
+    "c5_f32_32": "packed_f32_l8_v1_g2", "c5_f32_64": "packed_f32_l16_v1_g2", "c5_f32_128": "packed_f32_l32_v1_g2",
+    "c5_f32_256": "packed_f32_l64_v1_g2", "c5_f32_512": "packed_f32_l64_v2_g1", "c5_f32_1000": "row_f32_w4_v2",
+    "c5_f32_1024": "row_f32_w2_v2", "c5_f32_2048": "row_f32_w4_v2", "c5_f32_3000": "row_f32_w8_v2",
+    "c5_f32_4096": "row_f32_w8_v2", "c5_f32_8192": "row_f32_w16_v2", "c5_f32_16384": "row_f32_w4_v16",
 }
 
 
-@pytest.mark.parametrize("key", sorted(_PICKS), ids=[f"{d}-{c}" for d, c in sorted(_PICKS)])
+@pytest.mark.parametrize("key", sorted(_PICKS))
 def test_dispatch_picks_the_measured_shapes(lib, key):
-    dtype, cols = key
-    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
-    kid = binding.softmax_select(A, B, cols, cols, code, rows=4)
+    from row_wise_softmax_amd import workloads as W
+    wl = W.WORKLOADS[key]
+    code = W.dtype_code(wl.dtype)
+    a, b = 1 << 40, 1 << 41  # far apart: no overlap at any of these sizes (never dereferenced)
+    kid = binding.softmax_select(a, b, wl.cols, wl.cols, code, rows=wl.rows)
     assert binding.kernel_table()[kid].name == _PICKS[key]
+
+
+def test_fp32_ragged_rule_follows_the_row_count(lib):
+    """Ragged fp32 rows of 129..255 accesses: one access per lane below 8192
+    rows, two from 8192 rows on; bf16 keeps one at any count."""
+    a, b = 1 << 40, 1 << 41
+    names = lambda cols, code, rows: binding.kernel_table()[binding.softmax_select(a, b, cols, cols, code,
+                                                                                      rows=rows)].name
+    assert names(1000, 0, 8191) == "row_f32_w4_v1" and names(1000, 0, 8192) == "row_f32_w4_v2"
+    assert names(2000, 2, 8191) == "row_bf16_w4_v1" and names(2000, 2, 100000) == "row_bf16_w4_v1"
