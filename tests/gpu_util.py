@@ -122,3 +122,29 @@ def check_padding_untouched(y_raw: np.ndarray, cols: int, dtype: str, label: str
         else:
             same = pad == want
         assert same.all(), f"{label}: output padding between cols and row_stride was written"
+
+
+def check_every_row(y_raw: np.ndarray, x: np.ndarray, dtype: str, label: str = "",
+                    chunk_elems: int = 1 << 21, threads: int = 16) -> float:
+    """Element-by-element comparison of a large GPU output with the oracle, over every row.
+
+    The rows are cut into chunks of about ``chunk_elems`` elements; each
+    chunk is run through the oracle and compared with ``check`` on a pool of
+    host threads (the oracle's C call and numpy's large-array loops release
+    the interpreter lock).  Returns the largest absolute error."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as O
+
+    rows, cols = x.shape
+    step = max(1, chunk_elems // max(cols, 1))
+    starts = list(range(0, rows, step))
+
+    def one(r0: int) -> float:
+        r1 = min(rows, r0 + step)
+        xs = x[r0:r1]
+        return check(y_raw[r0:r1], xs, dtype, O.softmax(xs, dtype), label=f"{label} rows {r0}..{r1 - 1}")
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        errs = list(ex.map(one, starts))
+    return max(errs) if errs else 0.0
