@@ -278,7 +278,12 @@ def kernel_name(res: Resident) -> str:
     return binding.kernel_table()[kid].name
 
 
-def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfused: bool = False) -> dict:
+def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfused: bool = False,
+                  light: bool = False, oracle_timing: bool = True) -> dict:
+    """One shape: the dispatch pick timed over rotating buffers, and (with_copy) the
+    same-size copy kernel.  `light` skips the memcpy, graph and warm-cache figures
+    (the width sweep's 24 tensors); `oracle_timing` adds the single-threaded
+    oracle's rate on the same input (the whole input, or a bounded row sample)."""
     wl = W.WORKLOADS[key]
     log(f"[bench] {wl.name}: generating and uploading")
     res = Resident(wl)
@@ -287,6 +292,8 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfus
     d = {"workload": wl.name, "rows": wl.rows, "cols": wl.cols, "dtype": wl.dtype,
          "kernel": kernel_name(res), "buffers": res.n, "us": round(ms * 1e3, 3),
          "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
+    if oracle_timing:
+        d["oracle_1core"] = oracle_rate(res.x_host, wl)
     if with_unfused:
         import torch
         nbytes = binding.unfused_workspace_bytes(wl.rows, wl.cols, res.code)
@@ -299,10 +306,16 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfus
         del ws
     if with_copy:
         cms = time_launches(res.copy, res.n, steps, warmup)
-        mms = time_launches(res.memcpy, res.n, steps, warmup)
         d["copy_kernel_gbps"] = round(wl.bytes / (cms * 1e-3) / 1e9, 1)
-        d["memcpy_gbps"] = round(wl.bytes / (mms * 1e-3) / 1e9, 1)
         d["frac_of_copy"] = round(gbps / d["copy_kernel_gbps"], 4)
+        if not light:
+            mms = time_launches(res.memcpy, res.n, steps, warmup)
+            d["memcpy_gbps"] = round(wl.bytes / (mms * 1e-3) / 1e9, 1)
+    if light:
+        log(f"[bench] {wl.name}: {d['us']} us  {d['gbps']} GB/s  ({100 * d['frac_of_peak']:.1f}% of 8 TB/s, "
+            f"{d.get('frac_of_copy', 0):.3f} of copy)  kernel={d['kernel']}")
+        d["_res"] = res
+        return d
     # The same launches replayed from one captured graph: no host cost per launch.
     gms = time_graph(res, max(steps, res.n))
     d["graph_us"] = round(gms * 1e3, 3)
@@ -437,13 +450,47 @@ def oracle_threaded(x: np.ndarray, wl, budget_s: float) -> dict:
                       f"{mean:.3f} s each", "cpu": cpu}
 
 
-def sweep(steps: int, warmup: int) -> list:
-    """Every fitting table kernel at every width of the sweep, bf16 and fp32."""
+ORACLE_SAMPLE_ELEMS = 1 << 21  # rows of about this many elements time the oracle on the large inputs
+
+
+def oracle_rate(x: np.ndarray, wl) -> dict:
+    """The single-threaded fp64 oracle on this shape's input, pinned to one core:
+    the whole input when it has at most ORACLE_SAMPLE_ELEMS * 16 elements (best
+    of 3 for inputs under 1 MB, one run otherwise), else the leading rows of
+    about ORACLE_SAMPLE_ELEMS elements.  GB/s by the metric's formula on the
+    rows timed."""
+    from oracle import oracle
+    rows = wl.rows if wl.rows * wl.cols <= ORACLE_SAMPLE_ELEMS * 16 else max(1, ORACLE_SAMPLE_ELEMS // wl.cols)
+    part = np.ascontiguousarray(x[:rows])
+    reps = 3 if part.nbytes < 1_000_000 else 1
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        best = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.softmax(part, wl.dtype)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+    finally:
+        os.sched_setaffinity(0, allowed)
+    nbytes = W.algorithmic_bytes(rows, wl.cols, wl.dtype)
+    return {"rows_timed": rows, "seconds": round(best, 4), "gbps": round(nbytes / best / 1e9, 3),
+            "runs": reps, "cores": 1}
+
+
+def sweep(steps: int, warmup: int, keys: list | None = None) -> list:
+    """Every fitting table kernel at every width of the sweep, bf16 and fp32
+    (or at the workloads named in `keys`)."""
     table = binding.kernel_table()
     rows_out = []
-    for dt in ("bf16", "f32"):
-        for w in W.SWEEP_WIDTHS:
-            wl = W.WORKLOADS[f"c5_{dt}_{w}"]
+    if keys is None:
+        keys = [f"c5_{dt}_{w}" for dt in ("bf16", "f32") for w in W.SWEEP_WIDTHS]
+    for key in keys:
+        if True:
+            wl = W.WORKLOADS[key]
+            dt, w = wl.dtype, wl.cols
             res = Resident(wl)
             chosen = kernel_name(res)
             results = []
@@ -461,7 +508,7 @@ def sweep(steps: int, warmup: int) -> list:
             results.sort(reverse=True)
             best = results[0]
             chosen_gbps = next(g for g, n, _ in results if n == chosen) if any(n == chosen for _, n, _ in results) else None
-            line = {"workload": wl.name, "dtype": dt, "cols": w, "rows": wl.rows, "dispatch": chosen,
+            line = {"workload": wl.name, "key": key, "dtype": dt, "cols": w, "rows": wl.rows, "dispatch": chosen,
                     "dispatch_gbps": round(chosen_gbps, 1) if chosen_gbps else None,
                     "best": best[1], "best_gbps": round(best[0], 1),
                     "top5": [(n, round(g, 1)) for g, n, _ in results[:5]]}
@@ -472,7 +519,9 @@ def sweep(steps: int, warmup: int) -> list:
     # one-workgroup-per-row kernel wins
     crossings = []
     for dt in ("bf16", "f32"):
-        mine = [r for r in rows_out if r["dtype"] == dt]
+        mine = [r for r in rows_out if r["dtype"] == dt and r["key"].startswith("c5_")]
+        if not mine:
+            continue
         packed = [r["cols"] for r in mine if r["best"].startswith("packed")]
         row = [r["cols"] for r in mine if r["best"].startswith(("row_", "rowpf_"))]
         cross = {"crossover": dt, "packed_wins_up_to_cols": max(packed) if packed else None,
@@ -485,14 +534,22 @@ def sweep(steps: int, warmup: int) -> list:
 # ------------------------------------------------------------ profile summaries
 
 def summarize_sweep(sweep_json: str) -> None:
-    """Write profiles/sweep_c5_widths.md (the crossover report) from `bench.py --sweep --sweep-out` JSON."""
+    """Write profiles/sweep_c5_widths.md (the crossover report) from `bench.py --sweep --sweep-out` JSON,
+    or profiles/sweep_fixed_shapes.md when the sweep ran on other workloads (--sweep-keys)."""
     rows = json.load(open(sweep_json))
     src = os.path.relpath(os.path.abspath(sweep_json), ROOT)
-    out = ["# Width sweep on MI355X (gfx950): every plain table kernel at every c5 width", "",
+    keys = [r["key"] for r in rows if "key" in r]
+    c5 = all(k.startswith("c5_") for k in keys)
+    title = ("every plain table kernel at every c5 width" if c5 else
+             "every plain table kernel at the exact shapes " + ", ".join(keys))
+    cmd = f"    python3 bench.py --sweep --sweep-out {src}" if c5 else \
+        f"    python3 bench.py --sweep --sweep-keys {','.join(keys)} --sweep-out {src}"
+    out = [f"# Kernel sweep on MI355X (gfx950): {title}", "",
            "Commands (repository root):", "",
-           f"    python3 bench.py --sweep --sweep-out {src}",
+           cmd,
            f"    python3 bench.py --summarize-sweep {src}", "",
-           "About 200 MB of input per tensor, rotating buffer sets of at least 1 GiB, 0.3 s spin-up per width; GB/s by",
+           ("About 200 MB of input per tensor" if c5 else "The workloads' exact shapes") +
+           ", rotating buffer sets of at least 1 GiB, 0.3 s spin-up per shape; GB/s by",
            "the metric's 2·rows·cols·size bytes.  `pick` is the kernel the width dispatch chooses, `best` the fastest",
            "kernel measured; the last column lists the next four.", "",
            "| dtype | cols | rows | pick | pick GB/s | best | best GB/s | next |", "|---|---|---|---|---|---|---|---|"]
@@ -504,11 +561,11 @@ def summarize_sweep(sweep_json: str) -> None:
                    f"{r['best']} | {r['best_gbps']:.0f} | {nxt} |")
     out.append("")
     for r in rows:
-        if "crossover" in r:
+        if "crossover" in r and c5:
             out.append(f"- {r['crossover']}: the packed kernel (several rows per wave) wins up to "
                        f"{r['packed_wins_up_to_cols']} columns; one workgroup per row wins from "
                        f"{r['row_wins_from_cols']} columns.")
-    path = os.path.join(PROFILE_DIR, "sweep_c5_widths.md")
+    path = os.path.join(PROFILE_DIR, "sweep_c5_widths.md" if c5 else "sweep_fixed_shapes.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
     print(path)
@@ -706,6 +763,139 @@ def attention_only(steps: int, warmup: int) -> dict:
     return attention_shapes(steps, warmup)
 
 
+COPY_SIZES_MIB = (8, 16, 32, 64, 128, 256, 512, 1024)
+
+
+def copy_ceiling(steps: int, warmup: int, sizes=COPY_SIZES_MIB) -> list:
+    """The copy kernel and its two directions alone (read-only, write-only) at each
+    size in MiB of input, over rotating buffers of at least 1 GiB in all, timed like
+    the softmax (spin-up, warm-up, events).  GB/s: bytes read plus bytes written."""
+    import torch
+    out = []
+    stream = torch.cuda.current_stream().cuda_stream
+    for mib in sizes:
+        nbytes = mib << 20
+        n = n_buffers(2 * nbytes)
+        src = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        r = {"mib": mib, "bytes": nbytes, "buffers": n}
+        for mode, name in ((0, "copy"), (1, "read"), (2, "write")):
+            ms = time_launches(lambda i, m=mode: binding.bench_stream(src[i].data_ptr(), dst[i].data_ptr(), nbytes, m,
+                                                                       stream), n, steps, warmup)
+            moved = 2 * nbytes if mode == 0 else nbytes
+            r[f"{name}_us"] = round(ms * 1e3, 3)
+            r[f"{name}_gbps"] = round(moved / (ms * 1e-3) / 1e9, 1)
+        log(f"[bench] copy ceiling {mib} MiB: copy {r['copy_gbps']}  read {r['read_gbps']}  write {r['write_gbps']} GB/s")
+        out.append(r)
+        del src, dst
+        torch.cuda.synchronize()
+    return out
+
+
+def summarize_copy_sizes(json_path: str) -> None:
+    """Write profiles/copy_ceiling_sizes.md from `bench.py --copy-sizes --copy-out` JSON
+    (or from a default bench line, which carries the same table as copy_ceiling)."""
+    d = json.load(open(json_path))
+    rows = d["copy_ceiling"] if isinstance(d, dict) else d
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    out = ["# Copy ceiling by size on MI355X (gfx950): the 16-byte copy kernel and its two directions", "",
+           "Command (repository root):", "",
+           f"    python3 bench.py --copy-sizes --copy-out {src}",
+           f"    python3 bench.py --summarize-copy-sizes {src}", "",
+           "Kernels: `softmax_bench_stream` modes 0 (copy, `copy16<4>`), 1 (read-only, `read16<4>`) and 2 (write-only,",
+           "`write16<4>`), 256 threads, four 16-byte non-temporal accesses per thread in flight, grid-stride.  Rotating",
+           "buffer sets of at least 1 GiB, 0.3 s spin-up, then warm-up and timed launches between HIP events.  GB/s counts",
+           "bytes read plus bytes written (copy: 2 x size, the softmax metric's byte count for the same input size).", "",
+           "| input size | copy µs | copy GB/s | % of 8 TB/s | read-only GB/s | write-only GB/s |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['mib']} MiB | {r['copy_us']:.2f} | {r['copy_gbps']:.0f} | {100 * r['copy_gbps'] / PEAK_GBPS:.1f} | "
+                   f"{r['read_gbps']:.0f} | {r['write_gbps']:.0f} |")
+    path = os.path.join(PROFILE_DIR, "copy_ceiling_sizes.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(path).read())
+
+
+def counter_shapes(keys: list, reps: int = 10) -> list:
+    """The dispatch pick of each named workload `reps` times over rotating buffers,
+    then a 64 MiB copy kernel to calibrate the byte counters (counter runs)."""
+    import torch
+    manifest = []
+    for key in keys:
+        wl = W.WORKLOADS[key]
+        res = Resident(wl)
+        for i in range(reps):
+            res.softmax(i % res.n)
+        torch.cuda.synchronize()
+        manifest.append({"key": key, "workload": wl.name, "rows": wl.rows, "cols": wl.cols, "dtype": wl.dtype,
+                         "kernel": kernel_name(res), "input_bytes": wl.rows * wl.cols * W.elem_size(wl.dtype)})
+        log(f"[bench] counters {wl.name}: {reps} launches of {manifest[-1]['kernel']}")
+        del res
+    n = (64 << 20) // 4
+    a = torch.zeros(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        binding.bench_copy(a.data_ptr(), b.data_ptr(), n * 4, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return manifest
+
+
+def summarize_shape_counters(fetch_csv: str, write_csv: str, manifest_json: str) -> None:
+    """Write profiles/counters_c5_wide_widths.txt: HBM bytes per dispatch of the dispatch
+    pick at each workload of a `bench.py --counter-shapes` run (two rocprofv3 --pmc runs)."""
+    manifest = json.load(open(manifest_json))
+    tags = {"f32": "F32", "f16": "F16", "bf16": "BF16"}
+
+    def per_group(path, counter):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            wg = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+            d[(name, wg)].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in d.items()}
+
+    fe, wr = per_group(fetch_csv, "FETCH_SIZE"), per_group(write_csv, "WRITE_SIZE")
+    cp = next(k for k in fe if "copy16" in k[0])
+    cpw = next(k for k in wr if "copy16" in k[0])
+    kib = (64 << 20) / 1024
+    f_scale, w_scale = kib / fe[cp], kib / wr[cpw]
+    rel = lambda f: os.path.relpath(os.path.abspath(f), ROOT)
+    keys = ",".join(m["key"] for m in manifest)
+    lines = [
+        "# HBM traffic of the dispatch pick on the wide c5 sweep widths, MI355X (gfx950)",
+        "# Two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), run from the repository root:",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {os.path.dirname(rel(fetch_csv))} -o s -- "
+        f"python3 bench.py --counter-shapes {keys} --manifest-out {rel(manifest_json)}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {os.path.dirname(rel(write_csv))} -o s -- "
+        f"python3 bench.py --counter-shapes {keys} --manifest-out {rel(manifest_json)}",
+        f"# then: python3 bench.py --summarize-shape-counters {rel(fetch_csv)} {rel(write_csv)} {rel(manifest_json)}",
+        "# KiB per dispatch averaged over each shape's 10 dispatches (rotating buffers of at least 1 GiB), calibrated",
+        f"# with a 64 MiB plain copy of the same run (fetch scale {f_scale:.4f}, write scale {w_scale:.4f}).",
+        "# 'x input' divides by the tensor's bytes; a single-pass kernel's ideal is 1.000 for both.",
+        f"source_digest: {source_digest()}", ""]
+    for m in manifest:
+        tag = tags[m["dtype"]]
+        hits = [k for k in fe if k[1] == m["rows"] and f"<rws::{tag}," in k[0] and "softmax_" in k[0]]
+        if len(hits) != 1:
+            lines.append(f"{m['key']}: no unique dispatch group found ({len(hits)} candidates)")
+            continue
+        k = hits[0]
+        fb = fe[k] * f_scale * 1024
+        wb = wr.get(k, 0.0) * w_scale * 1024
+        size = m["input_bytes"]
+        lines.append(f"{m['key']}  [{m['workload']}, {m['kernel']}]")
+        lines.append(f"  fetch_bytes: {fb:.0f}  ({fb / size:.4f} x input)")
+        lines.append(f"  write_bytes: {wb:.0f}  ({wb / size:.4f} x input)")
+        lines.append(f"  traffic_over_algorithmic: {(fb + wb) / (2 * size):.4f}")
+    path = os.path.join(PROFILE_DIR, "counters_c5_wide_widths.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def result_line(head: dict, shapes: dict, steps: int, warmup: int, cpu: dict | None, traffic: dict | None) -> dict:
     """The one JSON line: the headline shape's achieved GB/s as `value`, its roofline, the CPU baseline
     and every measured shape."""
@@ -817,7 +1007,29 @@ def main() -> int:
                     help="write profiles/sweep_c5_widths.md from a --sweep-out file")
     ap.add_argument("--summarize-attention-counters", nargs="+", metavar="CSV", default=None,
                     help="write profiles/counters_attention_b4_h32_d128_causal.txt from the rocprofv3 --pmc CSVs")
+    ap.add_argument("--sweep-keys", default=None,
+                    help="with --sweep: comma-separated workload keys to sweep (default: the 24 c5 tensors)")
+    ap.add_argument("--copy-sizes", action="store_true",
+                    help="time the copy, read-only and write-only streams at 8 MiB ... 1 GiB and exit")
+    ap.add_argument("--copy-out", default=None, help="with --copy-sizes: write the table as JSON here")
+    ap.add_argument("--summarize-copy-sizes", metavar="JSON", default=None,
+                    help="write profiles/copy_ceiling_sizes.md from a --copy-out file (or a bench JSON line)")
+    ap.add_argument("--counter-shapes", default=None,
+                    help="launch the dispatch pick of these workload keys 10 times each, for counter runs")
+    ap.add_argument("--manifest-out", default=None, help="with --counter-shapes: write what ran as JSON here")
+    ap.add_argument("--summarize-shape-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "MANIFEST_JSON"),
+                    default=None, help="write profiles/counters_c5_wide_widths.txt from two --pmc runs")
+    ap.add_argument("--no-sweep-widths", action="store_true",
+                    help="leave the 24 width-sweep tensors out of the default run")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="leave the copy-ceiling table out of the default run")
     args = ap.parse_args()
+    if args.summarize_copy_sizes:
+        summarize_copy_sizes(args.summarize_copy_sizes)
+        return 0
+    if args.summarize_shape_counters:
+        summarize_shape_counters(*args.summarize_shape_counters)
+        return 0
     if args.summarize_attention_counters:
         summarize_attention_counters(args.summarize_attention_counters)
         return 0
@@ -855,10 +1067,24 @@ def main() -> int:
         print(json.dumps(wide_only(args.steps, args.warmup)), flush=True)
         return 0
     if args.sweep:
-        out = sweep(args.steps, args.warmup)
+        out = sweep(args.steps, args.warmup, args.sweep_keys.split(",") if args.sweep_keys else None)
         if args.sweep_out:
             with open(args.sweep_out, "w") as f:
                 json.dump(out, f, indent=1)
+        return 0
+    if args.copy_sizes:
+        table = copy_ceiling(args.steps, args.warmup)
+        if args.copy_out:
+            with open(args.copy_out, "w") as f:
+                json.dump(table, f, indent=1)
+        print(json.dumps(table), flush=True)
+        return 0
+    if args.counter_shapes:
+        manifest = counter_shapes(args.counter_shapes.split(","))
+        if args.manifest_out:
+            with open(args.manifest_out, "w") as f:
+                json.dump(manifest, f, indent=1)
+        print(json.dumps(manifest), flush=True)
         return 0
 
     keys = args.only.split(",") if args.only else FIXED
@@ -869,10 +1095,19 @@ def main() -> int:
         shapes[key] = measure_shape(key, args.steps, args.warmup, with_copy=True, with_unfused=key in ("c3", "c4"))
         if key != HEADLINE:
             del shapes[key]["_res"]  # free its buffers before the next shape
+    copy_table = None
     if args.only is None:
         shapes["c2_fused"] = causal_c2(args.steps, args.warmup)
         shapes.update(split_shapes(args.steps, args.warmup))
         shapes.update(attention_shapes(args.steps, args.warmup))
+        if not args.no_sweep_widths:
+            for dt in ("bf16", "f32"):
+                for w in W.SWEEP_WIDTHS:
+                    key = f"c5_{dt}_{w}"
+                    shapes[key] = measure_shape(key, args.steps, args.warmup, with_copy=True, light=True)
+                    del shapes[key]["_res"]
+        if not args.no_copy_ceiling:
+            copy_table = copy_ceiling(args.steps, args.warmup)
 
     head = shapes[HEADLINE]
     res = head.pop("_res")
@@ -881,6 +1116,13 @@ def main() -> int:
         log(f"[bench] cpu baseline: oracle on {head['workload']} for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(res, args.cpu_seconds)
     line = result_line(head, shapes, args.steps, args.warmup, cpu, stored_traffic(head["workload"]))
+    if copy_table is not None:
+        line["copy_ceiling"] = copy_table
+    wide = [v for k, v in shapes.items() if k.startswith("c5_") and v["cols"] >= 2048]
+    if wide:
+        line["sweep_widths_ge_2048"] = {
+            "min_frac_of_peak": min(v["frac_of_peak"] for v in wide),
+            "at_or_above_0.8": sum(v["frac_of_peak"] >= 0.8 for v in wide), "of": len(wide)}
     print(json.dumps(line), flush=True)
     return 0
 

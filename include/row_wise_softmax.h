@@ -184,6 +184,20 @@ const char *softmax_version(void);
 int softmax_bench_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
 /*
+ * softmax_bench_stream -- the copy's two directions timed apart, with the same
+ * 16-byte accesses and grid as softmax_bench_copy, so that the bench can show
+ * what a read-once/write-once kernel can reach at each size:
+ *   mode 0  copy src -> dst (softmax_bench_copy);
+ *   mode 1  read `bytes` from src; dst must hold 4 writable bytes, where the
+ *           kernel stores one word only in the unlikely case that the XOR of
+ *           all the data equals a fixed value (the store keeps the loads);
+ *   mode 2  write `bytes` of a fixed pattern to dst; src is unused.
+ * Errors: BAD_KERNEL (other modes), NULL_POINTER, BAD_SHAPE (negative, not a
+ * multiple of 16, misaligned), OVERLAP (mode 0), HIP.
+ */
+int softmax_bench_stream(const void *src, void *dst, int64_t bytes, int mode, void *stream);
+
+/*
  * ---- Split-row softmax: few, wide rows ----
  *
  * With one workgroup per row, a matrix of few wide rows (say 8 x 1,048,576)

@@ -76,6 +76,8 @@ def _load():
     lib.softmax_version.argtypes = []
     lib.softmax_bench_copy.restype = i32
     lib.softmax_bench_copy.argtypes = [vp, vp, i64, vp]
+    lib.softmax_bench_stream.restype = i32
+    lib.softmax_bench_stream.argtypes = [vp, vp, i64, i32, vp]
     lib.softmax_split_workspace_bytes.restype = i64
     lib.softmax_split_workspace_bytes.argtypes = [i64, i64, i32]
     lib.softmax_fwd_split.restype = i32
@@ -143,6 +145,12 @@ def bench_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None
     """Plain 16-byte-vector device copy (the achievable-bandwidth reference)."""
     lib = _load()
     _check(lib.softmax_bench_copy(src_ptr, dst_ptr, nbytes, stream), "softmax_bench_copy")
+
+
+def bench_stream(src_ptr: int, dst_ptr: int, nbytes: int, mode: int, stream: int = 0) -> None:
+    """The copy's directions apart: mode 0 copy, 1 read-only, 2 write-only (bandwidth references)."""
+    lib = _load()
+    _check(lib.softmax_bench_stream(src_ptr, dst_ptr, nbytes, mode, stream), "softmax_bench_stream")
 
 
 def split_workspace_bytes(rows: int, cols: int, dtype: int) -> int:
@@ -252,13 +260,18 @@ def _torch_dtype_code(t) -> int:
 
 
 def _as_rows(t):
+    """(rows, cols, row_stride) of the row matrix a tensor holds, or ValueError.
+
+    The last dimension must have unit stride whatever the rank (a strided or
+    expanded 1-D view is not one row of adjacent elements); a 2-D tensor may
+    have gapped rows; higher ranks must be contiguous."""
     if t.dim() < 1:
         raise ValueError("softmax: input must have at least one dimension")
-    if t.dim() == 1:
-        return 1, t.shape[0], t.shape[0]
-    if t.stride(-1) != 1:
-        raise ValueError("softmax: the last dimension must be contiguous")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("softmax: the last dimension must be contiguous (unit stride)")
     cols = t.shape[-1]
+    if t.dim() == 1:
+        return 1, cols, cols
     if t.dim() == 2:
         return t.shape[0], cols, (t.stride(0) if t.shape[0] > 1 else cols)
     if not t.is_contiguous():
@@ -272,11 +285,17 @@ def softmax(x, out=None, kernel_id: int | None = None, causal: bool = False, sca
 
     ``out`` (optional) must match ``x`` in shape, dtype and strides; it may be
     ``x`` itself (in place).  With ``causal=True`` row i keeps columns
-    j <= i + diag and the kept entries are multiplied by ``scale`` first (rows
-    count over all leading dimensions).  The call is asynchronous on torch's
-    current stream.
+    j <= i + diag and the kept entries are multiplied by ``scale`` first; the
+    causal form takes one matrix (1-D or 2-D input) only, since the library
+    counts the row index i over the whole call.  The call is asynchronous on
+    torch's current stream.
     """
     import torch
+    if causal and x.dim() > 2:
+        # Flattening [..., n, n] would number rows across matrices, so every
+        # matrix after the first would keep (almost) every column.
+        raise ValueError("softmax: causal=True takes a 1-D or 2-D tensor (one score matrix); "
+                         "call it once per matrix of a batched [..., n, n] input")
     if not x.is_cuda:
         raise ValueError("softmax: input must be a GPU tensor")
     code = _torch_dtype_code(x)

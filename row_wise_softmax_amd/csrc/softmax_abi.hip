@@ -360,8 +360,11 @@ int64_t split_tiles(int64_t cols, const SplitPair& k) {
     return (nacc + k.tile - 1) / k.tile;
 }
 
+// Workspace bytes of the split path (8 per tile, rounded up to 256), or -1
+// when the count would not fit in int64.
 int64_t split_workspace(int64_t rows, int64_t cols, int dtype) {
     const int64_t tiles = split_tiles(cols, split_for(dtype, false));
+    if (tiles > 0 && rows > (INT64_MAX - 255) / 8 / tiles) return -1;
     return ((rows * tiles * 8 + 255) / 256) * 256;
 }
 
@@ -389,6 +392,14 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
     return SOFTMAX_OK;
 }
 
+// Whether a softmax_fwd_split call takes the split path (force 1, or few rows
+// that span two or more tiles).
+bool takes_split(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                 int force) {
+    const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
+    return force == 1 || (rows < kSplitMaxRows && split_tiles(cols, k) >= 2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -406,12 +417,11 @@ int softmax_fwd_split(const void* in, void* out, int64_t rows, int64_t cols, int
     int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
     if (st != SOFTMAX_OK || empty) return st;
     if (force != 0 && force != 1) return SOFTMAX_ERR_BAD_KERNEL;
-    const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
-    const bool split = force == 1 || (rows < kSplitMaxRows && split_tiles(cols, k) >= 2);
-    if (!split) return fwd(in, out, rows, cols, row_stride, dtype, false, 1.0f, 0, stream);
+    if (!takes_split(in, out, rows, cols, row_stride, dtype, force))
+        return fwd(in, out, rows, cols, row_stride, dtype, false, 1.0f, 0, stream);
     if (workspace == nullptr) return SOFTMAX_ERR_NULL_POINTER;
     const int64_t need = split_workspace(rows, cols, dtype);
-    if (uintptr_t(workspace) % 256 || workspace_size < need) return SOFTMAX_ERR_BAD_SHAPE;
+    if (need < 0 || uintptr_t(workspace) % 256 || workspace_size < need) return SOFTMAX_ERR_BAD_SHAPE;
     const int64_t esz = elem_bytes(dtype);
     const int64_t extent = ((rows - 1) * row_stride + cols) * esz;
     const uintptr_t a = uintptr_t(in), b = uintptr_t(out), w = uintptr_t(workspace);
@@ -420,7 +430,6 @@ int softmax_fwd_split(const void* in, void* out, int64_t rows, int64_t cols, int
     return launch_split(in, out, rows, cols, row_stride, dtype, static_cast<float*>(workspace),
                         static_cast<hipStream_t>(stream));
 }
-
 
 int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
                 void* stream) {
@@ -497,6 +506,43 @@ const char* softmax_status_string(int status) {
 }
 
 const char* softmax_version(void) { return "row_wise_softmax_amd 0.2.0 (gfx950)"; }
+
+int softmax_bench_stream(const void* src, void* dst, int64_t bytes, int mode, void* stream) {
+    if (mode == 0) return softmax_bench_copy(src, dst, bytes, stream);
+    if (mode != 1 && mode != 2) return SOFTMAX_ERR_BAD_KERNEL;
+    if (bytes < 0 || bytes % 16) return SOFTMAX_ERR_BAD_SHAPE;
+    if (bytes == 0) return SOFTMAX_OK;
+    if (dst == nullptr || (mode == 1 && src == nullptr)) return SOFTMAX_ERR_NULL_POINTER;
+    if ((mode == 1 && uintptr_t(src) % 16) || uintptr_t(dst) % 16) return SOFTMAX_ERR_BAD_SHAPE;
+    constexpr int kU = 4;
+    const int64_t n = bytes / 16;
+    int64_t grid = (n + 256 * kU - 1) / (256 * kU);
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    int64_t nn = n;
+    hipError_t rc;
+    if (mode == 1) {
+        const rws::u32x4* s = static_cast<const rws::u32x4*>(src);
+        unsigned* sink = static_cast<unsigned*>(dst);
+        // Any value: should the data's XOR ever equal it, the one word the
+        // kernel then stores lands in dst's first 4 bytes, which the caller
+        // provides for that.
+        unsigned never = 0x7fbadbadu;
+        void* args[] = {&s, &sink, &nn, &never};
+        rc = hipLaunchKernel((const void*)&rws::read16<kU>, dim3(unsigned(grid)), dim3(256), args, 0,
+                             static_cast<hipStream_t>(stream));
+    } else {
+        rws::u32x4* d = static_cast<rws::u32x4*>(dst);
+        unsigned value = 0x3c003c00u;
+        void* args[] = {&d, &nn, &value};
+        rc = hipLaunchKernel((const void*)&rws::write16<kU>, dim3(unsigned(grid)), dim3(256), args, 0,
+                             static_cast<hipStream_t>(stream));
+    }
+    if (rc != hipSuccess) {
+        (void)hipGetLastError();
+        return SOFTMAX_ERR_HIP;
+    }
+    return SOFTMAX_OK;
+}
 
 int softmax_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (bytes < 0 || bytes % 16) return SOFTMAX_ERR_BAD_SHAPE;

@@ -799,4 +799,37 @@ __global__ void __launch_bounds__(256) copy16(const u32x4* src, u32x4* dst, int6
     }
 }
 
+// Read-only and write-only streams of the same shape: the two halves of the
+// copy, to show how much of a copy's time each direction costs at a size.
+// The read kernel folds its data into one word and stores it only if it equals
+// `never`, a value the caller picks so that the store does not happen; the
+// loads cannot be dropped.
+template <int U>
+__global__ void __launch_bounds__(256) read16(const u32x4* src, unsigned* sink, int64_t n, unsigned never) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+    unsigned acc = 0;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; base < n; base += stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v[u] = u32x4{0, 0, 0, 0};
+            if (base + (int64_t)u * blockDim.x < n) v[u] = ld<true>(src + base + (int64_t)u * blockDim.x);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == never) sink[0] = acc;
+}
+
+template <int U>
+__global__ void __launch_bounds__(256) write16(u32x4* dst, int64_t n, unsigned value) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * U;
+    const u32x4 v = {value, value, value, value};
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; base < n; base += stride) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + (int64_t)u * blockDim.x < n) st<true>(dst + base + (int64_t)u * blockDim.x, v);
+    }
+}
+
 }  // namespace rws

@@ -178,6 +178,17 @@ def test_bench_copy_argument_errors(lib):
     assert lib.softmax_bench_copy(A, B, 0, None) == 0
 
 
+def test_bench_stream_argument_errors(lib):
+    st = lib.softmax_bench_stream
+    assert st(A, B, 64, 3, None) == 5       # unknown mode
+    assert st(A, B, 15, 1, None) == 2
+    assert st(A + 4, B, 16, 1, None) == 2   # misaligned source of the read stream
+    assert st(0, B, 16, 1, None) == 1
+    assert st(A, 0, 16, 2, None) == 1
+    assert st(A, A + 16, 64, 0, None) == 4  # mode 0 is the copy, with its overlap check
+    assert st(A, B, 0, 2, None) == 0
+
+
 def test_unfused_baseline_argument_errors(lib):
     ws = binding.unfused_workspace_bytes(4, 8, 0)
     assert ws > 2 * 4 * 8 * 4
@@ -263,3 +274,35 @@ def test_fp32_ragged_rule_follows_the_row_count(lib):
                                                                                       rows=rows)].name
     assert names(1000, 0, 8191) == "row_f32_w4_v1" and names(1000, 0, 8192) == "row_f32_w4_v2"
     assert names(2000, 2, 8191) == "row_bf16_w4_v1" and names(2000, 2, 100000) == "row_bf16_w4_v1"
+
+
+# ----------------------------------------------- torch-level argument checks
+# _as_rows only reads shapes and strides, so CPU tensors exercise it; nothing
+# here reaches the library.
+
+def test_strided_or_expanded_last_dim_is_rejected():
+    import torch
+    base = torch.arange(10, dtype=torch.float32)
+    for bad in (base[::2],                                       # 1-D, stride 2
+                torch.tensor([1.0]).expand(5),                    # 1-D, stride 0
+                base.view(2, 5)[:, ::2],                          # 2-D, last stride 2
+                torch.tensor([[1.0]]).expand(3, 4)):              # 2-D, last stride 0
+        with pytest.raises(ValueError, match="unit stride"):
+            binding._as_rows(bad)
+
+
+def test_row_shapes_of_accepted_views():
+    import torch
+    assert binding._as_rows(torch.zeros(7)) == (1, 7, 7)
+    assert binding._as_rows(torch.zeros(1).expand(1)) == (1, 1, 1)
+    assert binding._as_rows(torch.zeros(6, 10)[:, :7]) == (6, 7, 10)   # gapped rows keep their pitch
+    assert binding._as_rows(torch.zeros(1, 10)[:, :7]) == (1, 7, 7)
+    assert binding._as_rows(torch.zeros(2, 3, 5)) == (6, 5, 5)
+    with pytest.raises(ValueError, match="contiguous"):
+        binding._as_rows(torch.zeros(2, 3, 6)[:, :, :5])
+
+
+def test_causal_on_a_batch_of_matrices_is_rejected():
+    import torch
+    with pytest.raises(ValueError, match="causal=True takes a 1-D or 2-D"):
+        binding.softmax(torch.zeros(2, 4, 4), causal=True)

@@ -141,3 +141,55 @@ def test_result_line_contract():
     assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] == 1
     assert "_res" not in line["shapes"]["c3"]
     assert bench.result_line(head, {}, 1, 1, None, None)["roofline"]["traffic"] is None
+
+
+def test_fixed_shape_sweep_summary_goes_to_its_own_file(profile_dir, tmp_path):
+    rows = [{"workload": "c3_8192x4096_f16", "key": "c3", "dtype": "f16", "cols": 4096, "rows": 8192,
+             "dispatch": "row_f16_w4_v2", "dispatch_gbps": 5800.0, "best": "row_f16_w4_v2", "best_gbps": 5800.0,
+             "top5": [["row_f16_w4_v2", 5800.0], ["row_f16_w8_v1", 5700.0]]}]
+    src = tmp_path / "fixed.json"
+    src.write_text(json.dumps(rows))
+    bench.summarize_sweep(str(src))
+    text = (profile_dir / "sweep_fixed_shapes.md").read_text()
+    assert "--sweep-keys c3" in text
+    assert "| f16 | 4096 | 8192 | row_f16_w4_v2 | 5800 | row_f16_w4_v2 | 5800 | row_f16_w8_v1 5700 |" in text
+    assert not (profile_dir / "sweep_c5_widths.md").exists()
+
+
+def test_copy_size_summary(profile_dir, tmp_path):
+    table = [{"mib": 64, "bytes": 64 << 20, "buffers": 8, "copy_us": 22.5, "copy_gbps": 5965.2, "read_us": 11.0,
+              "read_gbps": 6100.5, "write_us": 11.2, "write_gbps": 5991.8}]
+    src = tmp_path / "copy.json"
+    src.write_text(json.dumps({"value": 1.0, "copy_ceiling": table}))  # a bench line carries the same table
+    bench.summarize_copy_sizes(str(src))
+    text = (profile_dir / "copy_ceiling_sizes.md").read_text()
+    assert "| 64 MiB | 22.50 | 5965 | 74.6 | 6100 | 5992 |" in text
+
+
+def test_shape_counter_summary(profile_dir, tmp_path):
+    """Dispatch groups are found by element type and grid (one workgroup per row),
+    and scaled by the 64 MiB copy's calibration."""
+    kib = (64 << 20) / 1024
+    rows, cols = 3051, 16384
+    size = rows * cols * 4
+    row = "void rws::softmax_row<rws::F32, 4, 4, 16, false, false>(rws::Args)"
+    cp = "void rws::copy16<4>(unsigned int __vector(4) const*, unsigned int __vector(4)*, long)"
+    fields = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value"]
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    for path, counter, vals in ((fetch, "FETCH_SIZE", (kib / 2, 1.02 * size / 1024 / 2)),
+                                (write, "WRITE_SIZE", (kib, size / 1024))):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=fields)
+            w.writeheader()
+            w.writerow({"Kernel_Name": cp, "Grid_Size": 4096 * 256, "Workgroup_Size": 256, "Counter_Name": counter,
+                        "Counter_Value": vals[0]})
+            w.writerow({"Kernel_Name": row, "Grid_Size": rows * 256, "Workgroup_Size": 256, "Counter_Name": counter,
+                        "Counter_Value": vals[1]})
+    manifest = tmp_path / "m.json"
+    manifest.write_text(json.dumps([{"key": "c5_f32_16384", "workload": "c5_sweep_3051x16384_f32", "rows": rows,
+                                     "cols": cols, "dtype": "f32", "kernel": "row_f32_w4_v16", "input_bytes": size}]))
+    bench.summarize_shape_counters(str(fetch), str(write), str(manifest))
+    text = (profile_dir / "counters_c5_wide_widths.txt").read_text()
+    assert "c5_f32_16384  [c5_sweep_3051x16384_f32, row_f32_w4_v16]" in text
+    assert "(1.0200 x input)" in text and "(1.0000 x input)" in text
+    assert "traffic_over_algorithmic: 1.0100" in text
