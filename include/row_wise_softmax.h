@@ -63,6 +63,7 @@ extern "C" {
 #define SOFTMAX_ERR_BAD_KERNEL 5   /* forced kernel id unknown, of another dtype or kind, or unable to take this width / alignment */
 #define SOFTMAX_ERR_HIP 6          /* the HIP runtime refused the launch */
 #define SOFTMAX_ERR_BAD_SCALE 7    /* causal entry points: scale not > 0, or scale * log2(e) not below 3e38 */
+#define SOFTMAX_ERR_SCRATCH_LIMIT 8 /* softmax_fwd_split_noalloc: the split needs more than its static scratch */
 
 /* Kernel variants of the compiled table. */
 #define SOFTMAX_VARIANT_PACKED 0 /* L lanes of a wave per row, 64/L rows per wave (narrow rows) */
@@ -232,6 +233,27 @@ int softmax_bench_stream(const void *src, void *dst, int64_t bytes, int mode, vo
 int64_t softmax_split_workspace_bytes(int64_t rows, int64_t cols, int dtype);
 int softmax_fwd_split(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
                       void *workspace, int64_t workspace_size, int force, void *stream);
+
+/*
+ * softmax_fwd_split_noalloc -- softmax_fwd_split for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The (max, sum)
+ * pairs of the split path live in a static device array of
+ * SOFTMAX_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; the call allocates nothing and calls no
+ * allocating routine.  Same arguments, dispatch, kernels and results as
+ * softmax_fwd_split without its workspace pair.
+ *   Limit: a split call needing more than SOFTMAX_NOALLOC_SCRATCH_BYTES of
+ *   workspace (softmax_split_workspace_bytes) returns
+ *   SOFTMAX_ERR_SCRATCH_LIMIT before any HIP call.
+ *   Sharing: every call on one GPU uses that GPU's one array.  Calls whose
+ *   executions overlap on one GPU (other streams, other threads) race and
+ *   may produce wrong results: serialise them.  A call reads only what its
+ *   own first kernel wrote, so nothing needs clearing between calls.
+ */
+#define SOFTMAX_NOALLOC_SCRATCH_BYTES (1 << 20)
+int softmax_fwd_split_noalloc(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
+                              int dtype, int force, void *stream);
 
 /*
  * ---- Fused attention forward on the matrix cores ----

@@ -82,6 +82,8 @@ def _load():
     lib.softmax_split_workspace_bytes.argtypes = [i64, i64, i32]
     lib.softmax_fwd_split.restype = i32
     lib.softmax_fwd_split.argtypes = [vp, vp, i64, i64, i64, i32, vp, i64, i32, vp]
+    lib.softmax_fwd_split_noalloc.restype = i32
+    lib.softmax_fwd_split_noalloc.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
     lib.attention_fwd.restype = i32
     lib.attention_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp]
     lib.softmax_unfused_workspace_bytes.restype = i64
@@ -163,6 +165,19 @@ def softmax_fwd_split(in_ptr: int, out_ptr: int, rows: int, cols: int, row_strid
     lib = _load()
     _check(lib.softmax_fwd_split(in_ptr, out_ptr, rows, cols, row_stride, dtype, workspace_ptr, workspace_size,
                                  force, stream), "softmax_fwd_split")
+
+
+# Bytes of the library's static split-path scratch (SOFTMAX_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def softmax_fwd_split_noalloc(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int, dtype: int,
+                              force: int = 0, stream: int = 0) -> None:
+    """softmax_fwd_split without a workspace: the split path's partials go to the
+    library's static per-device scratch (calls overlapping on one GPU race)."""
+    lib = _load()
+    _check(lib.softmax_fwd_split_noalloc(in_ptr, out_ptr, rows, cols, row_stride, dtype, force, stream),
+           "softmax_fwd_split_noalloc")
 
 
 def attention_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, batch: int, heads: int, nq: int, nk: int,

@@ -392,6 +392,35 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
     return SOFTMAX_OK;
 }
 
+// ---- the split path without a caller workspace
+//
+// `scratch` is the split path's workspace for softmax_fwd_split_noalloc: one
+// copy per device, held until the process ends.  In host code its name is a
+// host-side stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept in g_scratch.  Launches take that address, never the name.
+static __device__ __align__(256) unsigned char scratch[SOFTMAX_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<uintptr_t> g_scratch[kMaxDevices];  // 0 = not yet looked up
+
+// The current device's address of `scratch`, or nullptr if HIP cannot give it.
+void* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    const uintptr_t known = g_scratch[dev].load(std::memory_order_acquire);
+    if (known != 0) return reinterpret_cast<void*>(known);
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_scratch[dev].store(reinterpret_cast<uintptr_t>(ptr), std::memory_order_release);
+    return ptr;
+}
+
 // Whether a softmax_fwd_split call takes the split path (force 1, or few rows
 // that span two or more tiles).
 bool takes_split(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
@@ -428,6 +457,22 @@ int softmax_fwd_split(const void* in, void* out, int64_t rows, int64_t cols, int
     if ((w < a + uint64_t(extent) && a < w + uint64_t(need)) || (w < b + uint64_t(extent) && b < w + uint64_t(need)))
         return SOFTMAX_ERR_OVERLAP;
     return launch_split(in, out, rows, cols, row_stride, dtype, static_cast<float*>(workspace),
+                        static_cast<hipStream_t>(stream));
+}
+
+int softmax_fwd_split_noalloc(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                              int force, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK || empty) return st;
+    if (force != 0 && force != 1) return SOFTMAX_ERR_BAD_KERNEL;
+    if (!takes_split(in, out, rows, cols, row_stride, dtype, force))
+        return fwd(in, out, rows, cols, row_stride, dtype, false, 1.0f, 0, stream);
+    const int64_t need = split_workspace(rows, cols, dtype);
+    if (need < 0 || need > int64_t(SOFTMAX_NOALLOC_SCRATCH_BYTES)) return SOFTMAX_ERR_SCRATCH_LIMIT;
+    void* part = scratch_on_current_device();
+    if (part == nullptr) return SOFTMAX_ERR_HIP;
+    return launch_split(in, out, rows, cols, row_stride, dtype, static_cast<float*>(part),
                         static_cast<hipStream_t>(stream));
 }
 
@@ -501,6 +546,7 @@ const char* softmax_status_string(int status) {
         case SOFTMAX_ERR_BAD_KERNEL: return "kernel id unknown, of the other kind (plain or causal), or unable to take this dtype, width, stride or alignment";
         case SOFTMAX_ERR_HIP: return "HIP runtime refused the launch";
         case SOFTMAX_ERR_BAD_SCALE: return "bad scale (must be > 0 with scale * log2(e) below 3e38)";
+        case SOFTMAX_ERR_SCRATCH_LIMIT: return "the split path needs more workspace than the static scratch buffer holds (SOFTMAX_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

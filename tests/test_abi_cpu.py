@@ -48,7 +48,7 @@ def test_library_is_built_for_gfx950():
 
 def test_version_and_status_strings(lib):
     assert "gfx950" in binding.version()
-    for st in range(8):
+    for st in range(9):
         assert lib.softmax_status_string(st) != b"unknown status"
     assert lib.softmax_status_string(99) == b"unknown status"
 
@@ -306,3 +306,18 @@ def test_causal_on_a_batch_of_matrices_is_rejected():
     import torch
     with pytest.raises(ValueError, match="causal=True takes a 1-D or 2-D"):
         binding.softmax(torch.zeros(2, 4, 4), causal=True)
+
+
+def test_noalloc_split_rejects_before_any_launch(lib):
+    """Host addresses: every case is refused by validation or the scratch limit."""
+    nal = lib.softmax_fwd_split_noalloc
+    far = A + (1 << 46)  # an output address past every input extent below
+    assert nal(A, far, 4, 1 << 20, 1 << 20, 0, 2, None) == 5          # force not 0 or 1
+    assert nal(A, far, 512, 1 << 20, 1 << 20, 0, 1, None) == 8        # 2 MiB of pairs > 1 MiB scratch
+    assert nal(A, far, 1 << 40, 8, 8, 1, 1, None) == 8                # one tile per row, far too many rows
+    assert nal(A, B, -1, 8, 8, 0, 1, None) == 2
+    assert nal(A, A + 8, 4, 64, 64, 0, 1, None) == 4                  # partial overlap
+    assert nal(A, B, 0, 64, 64, 0, 1, None) == 0                      # empty: nothing launched
+    assert binding.NOALLOC_SCRATCH_BYTES == 1 << 20
+    text = open(HEADER).read()
+    assert "#define SOFTMAX_NOALLOC_SCRATCH_BYTES (1 << 20)" in text
