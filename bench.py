@@ -792,25 +792,57 @@ def copy_ceiling(steps: int, warmup: int, sizes=COPY_SIZES_MIB) -> list:
     return out
 
 
-def summarize_copy_sizes(json_path: str) -> None:
+def trace_by_stream_size(trace_csv: str) -> dict:
+    """Average dispatch ns of copy16 / read16 / write16 per input size in MiB, from a
+    rocprofv3 kernel-trace CSV (the grid is size / 16 KiB workgroups of 256 threads)."""
+    got = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        kind = next((k for k in ("copy16", "read16", "write16") if f"rws::{k}<" in name), None)
+        if kind is None:
+            continue
+        mib = int(r["Grid_Size_X"]) // 256 * 16384 // (1 << 20)
+        got[(kind, mib)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: sum(v) / len(v) for k, v in got.items()}
+
+
+def summarize_copy_sizes(json_path: str, trace_csv: str | None = None) -> None:
     """Write profiles/copy_ceiling_sizes.md from `bench.py --copy-sizes --copy-out` JSON
-    (or from a default bench line, which carries the same table as copy_ceiling)."""
+    (or from a default bench line, which carries the same table as copy_ceiling), with
+    the per-dispatch averages of a rocprofv3 kernel trace of the same run if given."""
     d = json.load(open(json_path))
     rows = d["copy_ceiling"] if isinstance(d, dict) else d
     src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    trace = trace_by_stream_size(trace_csv) if trace_csv else {}
+    # the event-timed table: a default bench line (its copy_ceiling) or a --copy-sizes file
+    cmd = [f"    python3 bench.py > {src}" if isinstance(d, dict) else f"    python3 bench.py --copy-sizes --copy-out {src}"]
+    if trace_csv:
+        tdir = os.path.dirname(os.path.relpath(os.path.abspath(trace_csv), ROOT))
+        cmd.append(f"    rocprofv3 --kernel-trace --stats --output-format csv -d {tdir} -o cs -- "
+                   f"python3 bench.py --copy-sizes --copy-out {tdir}/copy_sizes.json")
+    cmd.append(f"    python3 bench.py --summarize-copy-sizes {src}" +
+               (f" {os.path.relpath(os.path.abspath(trace_csv), ROOT)}" if trace_csv else ""))
     out = ["# Copy ceiling by size on MI355X (gfx950): the 16-byte copy kernel and its two directions", "",
-           "Command (repository root):", "",
-           f"    python3 bench.py --copy-sizes --copy-out {src}",
-           f"    python3 bench.py --summarize-copy-sizes {src}", "",
+           "Command (repository root):", "", *cmd, "",
            "Kernels: `softmax_bench_stream` modes 0 (copy, `copy16<4>`), 1 (read-only, `read16<4>`) and 2 (write-only,",
            "`write16<4>`), 256 threads, four 16-byte non-temporal accesses per thread in flight, grid-stride.  Rotating",
            "buffer sets of at least 1 GiB, 0.3 s spin-up, then warm-up and timed launches between HIP events.  GB/s counts",
            "bytes read plus bytes written (copy: 2 x size, the softmax metric's byte count for the same input size).", "",
-           "| input size | copy µs | copy GB/s | % of 8 TB/s | read-only GB/s | write-only GB/s |",
-           "|---|---|---|---|---|---|"]
+           "| input size | copy µs | copy GB/s | % of 8 TB/s | read-only GB/s | write-only GB/s |"
+           + (" copy µs, trace | read µs, trace | write µs, trace |" if trace else ""),
+           "|---|---|---|---|---|---|" + ("---|---|---|" if trace else "")]
     for r in rows:
-        out.append(f"| {r['mib']} MiB | {r['copy_us']:.2f} | {r['copy_gbps']:.0f} | {100 * r['copy_gbps'] / PEAK_GBPS:.1f} | "
-                   f"{r['read_gbps']:.0f} | {r['write_gbps']:.0f} |")
+        line = (f"| {r['mib']} MiB | {r['copy_us']:.2f} | {r['copy_gbps']:.0f} | {100 * r['copy_gbps'] / PEAK_GBPS:.1f} | "
+                f"{r['read_gbps']:.0f} | {r['write_gbps']:.0f} |")
+        if trace:
+            line += "".join(f" {trace[(k, r['mib'])] / 1e3:.2f} |" if (k, r["mib"]) in trace else " |"
+                            for k in ("copy16", "read16", "write16"))
+        out.append(line)
+    if trace:
+        out += ["", "The first columns are event-timed in an unprofiled run (the first command).  The trace columns are"
+                " kernel durations from a second run under rocprofv3 (the second command), averaged over every dispatch"
+                " of that kernel and size (spin-up, warm-up and timed launches); the profiler spaces dispatches out, so"
+                " that run's own event timings are not used."]
     path = os.path.join(PROFILE_DIR, "copy_ceiling_sizes.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
@@ -1012,8 +1044,9 @@ def main() -> int:
     ap.add_argument("--copy-sizes", action="store_true",
                     help="time the copy, read-only and write-only streams at 8 MiB ... 1 GiB and exit")
     ap.add_argument("--copy-out", default=None, help="with --copy-sizes: write the table as JSON here")
-    ap.add_argument("--summarize-copy-sizes", metavar="JSON", default=None,
-                    help="write profiles/copy_ceiling_sizes.md from a --copy-out file (or a bench JSON line)")
+    ap.add_argument("--summarize-copy-sizes", nargs="+", metavar="JSON [TRACE_CSV]", default=None,
+                    help="write profiles/copy_ceiling_sizes.md from a --copy-out file (or a bench JSON line) and,"
+                         " optionally, the rocprofv3 kernel-trace CSV of the same run")
     ap.add_argument("--counter-shapes", default=None,
                     help="launch the dispatch pick of these workload keys 10 times each, for counter runs")
     ap.add_argument("--manifest-out", default=None, help="with --counter-shapes: write what ran as JSON here")
@@ -1025,7 +1058,7 @@ def main() -> int:
                     help="leave the copy-ceiling table out of the default run")
     args = ap.parse_args()
     if args.summarize_copy_sizes:
-        summarize_copy_sizes(args.summarize_copy_sizes)
+        summarize_copy_sizes(*args.summarize_copy_sizes[:2])
         return 0
     if args.summarize_shape_counters:
         summarize_shape_counters(*args.summarize_shape_counters)
