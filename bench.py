@@ -511,7 +511,8 @@ def sweep(steps: int, warmup: int, keys: list | None = None) -> list:
             line = {"workload": wl.name, "key": key, "dtype": dt, "cols": w, "rows": wl.rows, "dispatch": chosen,
                     "dispatch_gbps": round(chosen_gbps, 1) if chosen_gbps else None,
                     "best": best[1], "best_gbps": round(best[0], 1),
-                    "top5": [(n, round(g, 1)) for g, n, _ in results[:5]]}
+                    "top5": [(n, round(g, 1)) for g, n, _ in results[:5]],
+                    "all": [(n, round(g, 1)) for g, n, _ in results]}
             log(json.dumps(line))
             rows_out.append(line)
             del res
@@ -806,6 +807,78 @@ def trace_by_stream_size(trace_csv: str) -> dict:
     return {k: sum(v) / len(v) for k, v in got.items()}
 
 
+CHUNK_COPY_MIB = 192  # about the c5 tensors' 200 MB; a multiple of every chunk shape
+
+
+def chunk_copy(steps: int, warmup: int, mib: int = CHUNK_COPY_MIB, rounds: int = 3) -> list:
+    """The row kernels' access pattern without their arithmetic: softmax_bench_chunk_copy
+    at every shape, and the plain copy kernel, on `mib` MiB over rotating buffers; the
+    median of `rounds` interleaved timings each."""
+    import torch
+    nbytes = mib << 20
+    n = n_buffers(2 * nbytes)
+    src = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    stream = torch.cuda.current_stream().cuda_stream
+    cands = {"copy16": lambda i: binding.bench_copy(src[i].data_ptr(), dst[i].data_ptr(), nbytes, stream)}
+    for w, v in binding.CHUNK_COPY_SHAPES:
+        cands[f"w{w}_v{v}"] = (lambda i, w=w, v=v: binding.bench_chunk_copy(src[i].data_ptr(), dst[i].data_ptr(),
+                                                                            nbytes, w, v, stream))
+    got = {k: [] for k in cands}
+    spin_up(cands["copy16"], n, SPIN_S)
+    for _ in range(rounds):
+        for k, f in cands.items():
+            ms = time_launches(f, n, steps, warmup, spin_s=0.02)
+            got[k].append(2 * nbytes / (ms * 1e-3) / 1e9)
+    out = []
+    for k, vals in got.items():
+        w, v = (None, None) if k == "copy16" else (int(k.split("_")[0][1:]), int(k.split("_")[1][1:]))
+        out.append({"kernel": k, "waves": w, "accesses": v, "chunk_kib": (w * 64 * v * 16 // 1024) if w else None,
+                    "gbps": round(float(np.median(vals)), 1), "runs": [round(x, 1) for x in vals]})
+        log(f"[bench] chunk copy {k}: {out[-1]['gbps']} GB/s")
+    del src, dst
+    torch.cuda.synchronize()
+    return out
+
+
+def summarize_chunk_copy(json_path: str, bench_json: str | None = None) -> None:
+    """Write profiles/chunk_copy_shapes.md from `bench.py --chunk-copy --chunk-out` JSON and,
+    optionally, a default bench line whose c5 shapes give each row kernel's own rate."""
+    rows = json.load(open(json_path))
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    users = collections.defaultdict(list)
+    if bench_json:
+        line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        for key, sh in line.get("shapes", {}).items():
+            k = sh.get("kernel", "")
+            if key.startswith("c5_") and k.startswith("row_"):
+                _, dt, w, v = k.split("_")
+                users[(int(w[1:]), int(v[1:]))].append(f"{dt} {sh['cols']}: {sh['gbps']:.0f}")
+    cmd = [f"    python3 bench.py --chunk-copy --chunk-out {src}"]
+    if bench_json:
+        cmd.append(f"    python3 bench.py > {os.path.relpath(os.path.abspath(bench_json), ROOT)}")
+    cmd.append(f"    python3 bench.py --summarize-chunk-copy {src}" +
+               (f" {os.path.relpath(os.path.abspath(bench_json), ROOT)}" if bench_json else ""))
+    out = ["# The row kernels' access pattern alone: copies in per-workgroup chunks, MI355X (gfx950)", "",
+           "Commands (repository root):", "", *cmd, "",
+           f"`softmax_bench_chunk_copy` on {CHUNK_COPY_MIB} MiB (about a c5 tensor): each workgroup of W waves copies one",
+           "contiguous chunk of W x 64 x V 16-byte accesses the way the row kernels read and write a row (wave w its run of",
+           "64 V accesses, all loads, a barrier, all stores), with no arithmetic.  `copy16` is the grid-stride copy kernel.",
+           "Median of three interleaved timings over rotating buffers of at least 1 GiB; GB/s = 2 x size / time.  The",
+           "last column lists the c5 widths whose dispatch pick is the row kernel of that shape, with that kernel's GB/s",
+           "from the default bench run.", "",
+           "| kernel | waves | accesses per lane | chunk KiB | GB/s | runs | softmax row kernels of this shape (GB/s) |",
+           "|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: (r["chunk_kib"] or 0, r["waves"] or 0)):
+        use = "; ".join(users.get((r["waves"], r["accesses"]), []))
+        out.append(f"| {r['kernel']} | {r['waves'] or ''} | {r['accesses'] or ''} | {r['chunk_kib'] or ''} | "
+                   f"{r['gbps']:.0f} | {', '.join(f'{x:.0f}' for x in r['runs'])} | {use} |")
+    path = os.path.join(PROFILE_DIR, "chunk_copy_shapes.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def summarize_copy_sizes(json_path: str, trace_csv: str | None = None) -> None:
     """Write profiles/copy_ceiling_sizes.md from `bench.py --copy-sizes --copy-out` JSON
     (or from a default bench line, which carries the same table as copy_ceiling), with
@@ -1047,6 +1120,11 @@ def main() -> int:
     ap.add_argument("--summarize-copy-sizes", nargs="+", metavar="JSON [TRACE_CSV]", default=None,
                     help="write profiles/copy_ceiling_sizes.md from a --copy-out file (or a bench JSON line) and,"
                          " optionally, the rocprofv3 kernel-trace CSV of the same run")
+    ap.add_argument("--chunk-copy", action="store_true",
+                    help="time the chunked copies shaped like the row kernels (192 MiB) and exit")
+    ap.add_argument("--chunk-out", default=None, help="with --chunk-copy: write the table as JSON here")
+    ap.add_argument("--summarize-chunk-copy", nargs="+", metavar="JSON [BENCH_JSON]", default=None,
+                    help="write profiles/chunk_copy_shapes.md from a --chunk-out file (and a default bench line)")
     ap.add_argument("--counter-shapes", default=None,
                     help="launch the dispatch pick of these workload keys 10 times each, for counter runs")
     ap.add_argument("--manifest-out", default=None, help="with --counter-shapes: write what ran as JSON here")
@@ -1057,6 +1135,9 @@ def main() -> int:
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="leave the copy-ceiling table out of the default run")
     args = ap.parse_args()
+    if args.summarize_chunk_copy:
+        summarize_chunk_copy(*args.summarize_chunk_copy[:2])
+        return 0
     if args.summarize_copy_sizes:
         summarize_copy_sizes(*args.summarize_copy_sizes[:2])
         return 0
@@ -1109,6 +1190,13 @@ def main() -> int:
         table = copy_ceiling(args.steps, args.warmup)
         if args.copy_out:
             with open(args.copy_out, "w") as f:
+                json.dump(table, f, indent=1)
+        print(json.dumps(table), flush=True)
+        return 0
+    if args.chunk_copy:
+        table = chunk_copy(args.steps, args.warmup)
+        if args.chunk_out:
+            with open(args.chunk_out, "w") as f:
                 json.dump(table, f, indent=1)
         print(json.dumps(table), flush=True)
         return 0

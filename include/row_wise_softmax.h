@@ -199,6 +199,19 @@ int softmax_bench_copy(const void *src, void *dst, int64_t bytes, void *stream);
 int softmax_bench_stream(const void *src, void *dst, int64_t bytes, int mode, void *stream);
 
 /*
+ * softmax_bench_chunk_copy -- a copy shaped like the row kernels without their
+ * arithmetic: each workgroup of `waves` waves copies one contiguous chunk of
+ * waves * 64 * accesses 16-byte accesses (wave w its run of 64 * accesses,
+ * each lane `accesses` loads 1 KiB apart), all loads, a barrier, then all
+ * stores.  Its rate per chunk size shows what the row kernels' access
+ * pattern alone allows at a given row size.
+ *   (waves, accesses) in {(4,2), (8,2), (4,4), (16,2), (4,8), (8,4), (4,16),
+ *   (8,8), (16,4)}; bytes a multiple of the chunk.
+ * Errors: BAD_KERNEL (other shapes), BAD_SHAPE, NULL_POINTER, OVERLAP, HIP.
+ */
+int softmax_bench_chunk_copy(const void *src, void *dst, int64_t bytes, int waves, int accesses, void *stream);
+
+/*
  * ---- Split-row softmax: few, wide rows ----
  *
  * With one workgroup per row, a matrix of few wide rows (say 8 x 1,048,576)

@@ -76,6 +76,8 @@ def _load():
     lib.softmax_version.argtypes = []
     lib.softmax_bench_copy.restype = i32
     lib.softmax_bench_copy.argtypes = [vp, vp, i64, vp]
+    lib.softmax_bench_chunk_copy.restype = i32
+    lib.softmax_bench_chunk_copy.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.softmax_bench_stream.restype = i32
     lib.softmax_bench_stream.argtypes = [vp, vp, i64, i32, vp]
     lib.softmax_split_workspace_bytes.restype = i64
@@ -153,6 +155,15 @@ def bench_stream(src_ptr: int, dst_ptr: int, nbytes: int, mode: int, stream: int
     """The copy's directions apart: mode 0 copy, 1 read-only, 2 write-only (bandwidth references)."""
     lib = _load()
     _check(lib.softmax_bench_stream(src_ptr, dst_ptr, nbytes, mode, stream), "softmax_bench_stream")
+
+
+CHUNK_COPY_SHAPES = ((4, 2), (8, 2), (4, 4), (16, 2), (4, 8), (8, 4), (4, 16), (8, 8), (16, 4))
+
+
+def bench_chunk_copy(src_ptr: int, dst_ptr: int, nbytes: int, waves: int, accesses: int, stream: int = 0) -> None:
+    """Copy in per-workgroup chunks shaped like the row kernels (waves x 64 x accesses x 16 bytes)."""
+    lib = _load()
+    _check(lib.softmax_bench_chunk_copy(src_ptr, dst_ptr, nbytes, waves, accesses, stream), "softmax_bench_chunk_copy")
 
 
 def split_workspace_bytes(rows: int, cols: int, dtype: int) -> int:

@@ -590,6 +590,39 @@ int softmax_bench_stream(const void* src, void* dst, int64_t bytes, int mode, vo
     return SOFTMAX_OK;
 }
 
+int softmax_bench_chunk_copy(const void* src, void* dst, int64_t bytes, int waves, int accesses, void* stream) {
+    struct Shape { int w, v; const void* fn; };
+    static const Shape kShapes[] = {
+        {4, 2, (const void*)&rws::chunk_copy16<4, 2>},   {8, 2, (const void*)&rws::chunk_copy16<8, 2>},
+        {4, 4, (const void*)&rws::chunk_copy16<4, 4>},   {16, 2, (const void*)&rws::chunk_copy16<16, 2>},
+        {4, 8, (const void*)&rws::chunk_copy16<4, 8>},   {8, 4, (const void*)&rws::chunk_copy16<8, 4>},
+        {4, 16, (const void*)&rws::chunk_copy16<4, 16>}, {8, 8, (const void*)&rws::chunk_copy16<8, 8>},
+        {16, 4, (const void*)&rws::chunk_copy16<16, 4>},
+    };
+    const Shape* k = nullptr;
+    for (const Shape& sh : kShapes)
+        if (sh.w == waves && sh.v == accesses) k = &sh;
+    if (k == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    const int64_t chunk = int64_t(waves) * 64 * accesses * 16;
+    if (bytes < 0 || bytes % chunk) return SOFTMAX_ERR_BAD_SHAPE;
+    if (bytes == 0) return SOFTMAX_OK;
+    if (src == nullptr || dst == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    if (uintptr_t(src) % 16 || uintptr_t(dst) % 16) return SOFTMAX_ERR_BAD_SHAPE;
+    const uintptr_t a = uintptr_t(src), b = uintptr_t(dst);
+    if (a < b + uint64_t(bytes) && b < a + uint64_t(bytes)) return SOFTMAX_ERR_OVERLAP;
+    int64_t n = bytes / chunk;
+    const int64_t grid = n < kMaxGrid ? n : kMaxGrid;
+    const rws::u32x4* s = static_cast<const rws::u32x4*>(src);
+    rws::u32x4* d = static_cast<rws::u32x4*>(dst);
+    void* args[] = {&s, &d, &n};
+    if (hipLaunchKernel(k->fn, dim3(unsigned(grid)), dim3(unsigned(waves * 64)), args, 0,
+                        static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return SOFTMAX_ERR_HIP;
+    }
+    return SOFTMAX_OK;
+}
+
 int softmax_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (bytes < 0 || bytes % 16) return SOFTMAX_ERR_BAD_SHAPE;
     if (bytes == 0) return SOFTMAX_OK;

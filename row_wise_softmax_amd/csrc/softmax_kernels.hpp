@@ -799,6 +799,26 @@ __global__ void __launch_bounds__(256) copy16(const u32x4* src, u32x4* dst, int6
     }
 }
 
+// Copy in contiguous per-workgroup chunks of W * 64 * V 16-byte accesses,
+// shaped like the row kernels without their arithmetic: wave w loads its run
+// of 64 V accesses (lane l: accesses 64 V w + l + 64 v), the workgroup waits
+// at a barrier, then stores them.  Timing the chunk sizes of the row kernels
+// this way separates the cost of the access pattern from the softmax's own.
+template <int W, int V>
+__global__ void __launch_bounds__(W * kWave) chunk_copy16(const u32x4* src, u32x4* dst, int64_t nchunks) {
+    const int t = threadIdx.x;
+    const int64_t wave_run = int64_t(t / kWave) * (kWave * V) + (t % kWave);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t base = c * (W * kWave * V) + wave_run;
+        u32x4 x[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = ld<true>(src + base + v * kWave);
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < V; ++v) st<true>(dst + base + v * kWave, x[v]);
+    }
+}
+
 // Read-only and write-only streams of the same shape: the two halves of the
 // copy, to show how much of a copy's time each direction costs at a size.
 // The read kernel folds its data into one word and stores it only if it equals

@@ -321,3 +321,15 @@ def test_noalloc_split_rejects_before_any_launch(lib):
     assert binding.NOALLOC_SCRATCH_BYTES == 1 << 20
     text = open(HEADER).read()
     assert "#define SOFTMAX_NOALLOC_SCRATCH_BYTES (1 << 20)" in text
+
+
+def test_bench_chunk_copy_argument_errors(lib):
+    cc = lib.softmax_bench_chunk_copy
+    far = A + (1 << 40)
+    assert cc(A, far, 64 << 10, 3, 16, None) == 5     # no such shape
+    assert cc(A, far, (64 << 10) + 16, 4, 16, None) == 2  # not a whole number of 64 KiB chunks
+    assert cc(A + 4, far, 64 << 10, 4, 16, None) == 2
+    assert cc(0, far, 64 << 10, 4, 16, None) == 1
+    assert cc(A, A + 1024, 64 << 10, 4, 16, None) == 4
+    assert cc(A, far, 0, 4, 16, None) == 0
+    assert binding.CHUNK_COPY_SHAPES[-1] == (16, 4)

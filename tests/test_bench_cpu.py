@@ -193,3 +193,20 @@ def test_shape_counter_summary(profile_dir, tmp_path):
     assert "c5_f32_16384  [c5_sweep_3051x16384_f32, row_f32_w4_v16]" in text
     assert "(1.0200 x input)" in text and "(1.0000 x input)" in text
     assert "traffic_over_algorithmic: 1.0100" in text
+
+
+def test_chunk_copy_summary_lists_the_row_kernels_of_each_shape(profile_dir, tmp_path):
+    rows = [{"kernel": "copy16", "waves": None, "accesses": None, "chunk_kib": None, "gbps": 6400.0,
+             "runs": [6400.0, 6390.0, 6410.0]},
+            {"kernel": "w4_v16", "waves": 4, "accesses": 16, "chunk_kib": 64, "gbps": 6050.0,
+             "runs": [6050.0, 6040.0, 6060.0]}]
+    src = tmp_path / "cc.json"
+    src.write_text(json.dumps(rows))
+    line = {"value": 1.0, "shapes": {"c5_f32_16384": {"kernel": "row_f32_w4_v16", "cols": 16384, "gbps": 6143.1},
+                                     "c3": {"kernel": "row_f16_w4_v2", "cols": 4096, "gbps": 5800.0}}}
+    bj = tmp_path / "bench.json"
+    bj.write_text(json.dumps(line) + "\n")
+    bench.summarize_chunk_copy(str(src), str(bj))
+    text = (profile_dir / "chunk_copy_shapes.md").read_text()
+    assert "| w4_v16 | 4 | 16 | 64 | 6050 | 6050, 6040, 6060 | f32 16384: 6143 |" in text
+    assert "| copy16 |  |  |  | 6400 |" in text
