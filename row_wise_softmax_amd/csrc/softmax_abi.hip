@@ -102,6 +102,9 @@ bool aligned16(const void* in, const void* out, int64_t cols, int64_t row_stride
            (cols * esz) % 16 == 0;
 }
 
+// Two rounds of the chip's wave slots: 256 CUs x 4 SIMDs x 8 waves, twice.
+constexpr int64_t kFewRowWaves = 2 * 256 * 4 * 8;
+
 int pow2_at_least(int64_t v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -144,6 +147,18 @@ const Entry* select_entry(const void* in, const void* out, int64_t rows, int64_t
             // 6220 against 6117)
             if (e == nullptr)
                 e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
+            // Few rows: when the whole job fills the chip's wave slots at most
+            // twice, every workgroup of a round starts, loads and computes
+            // together, and HBM idles while a round computes.  The row kernel's
+            // persistent twin (same shape, grid = resident workgroups, the next
+            // row's loads issued before the current row's reductions) keeps
+            // loads in flight: 1-5% faster at one round or less, 2-21% at two
+            // (4096 x 4096 bf16: 5044 -> 5973 GB/s; 2048 x 2048 fp32: 5080 ->
+            // 5170).  From four rounds on the plain kernel is 1-7% ahead.
+            if (e != nullptr && rows * (e->lanes / 64) <= kFewRowWaves) {
+                const Entry* pf = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, e->lanes, e->vpl, 1);
+                if (pf != nullptr) e = pf;
+            }
         } else {
             // wider rows: four waves with more accesses each (16384 fp32
             // columns: 5825 GB/s, against 5625 on eight waves and 5613 on

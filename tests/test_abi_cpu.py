@@ -243,7 +243,7 @@ def test_attention_argument_errors(lib):
 # those workloads' row counts (the "pick" column of the measured sweep); a
 # change to the rule must change this table knowingly.
 _PICKS = {
-    "c1": "row_f32_w4_v1", "c2": "row_f32_w4_v2", "c3": "row_f16_w4_v2", "c4": "row_f32_w8_v2",
+    "c1": "rowpf_f32_w4_v1", "c2": "rowpf_f32_w4_v2", "c3": "row_f16_w4_v2", "c4": "row_f32_w8_v2",
     "c5_bf16_32": "packed_bf16_l4_v1_g2", "c5_bf16_64": "packed_bf16_l8_v1_g2", "c5_bf16_128": "packed_bf16_l16_v1_g2",
     "c5_bf16_256": "packed_bf16_l32_v1_g2", "c5_bf16_512": "packed_bf16_l64_v1_g2",
     "c5_bf16_1000": "packed_bf16_l64_v2_g1", "c5_bf16_1024": "packed_bf16_l64_v2_g1", "c5_bf16_2048": "row_bf16_w2_v2",
@@ -264,6 +264,19 @@ def test_dispatch_picks_the_measured_shapes(lib, key):
     a, b = 1 << 40, 1 << 41  # far apart: no overlap at any of these sizes (never dereferenced)
     kid = binding.softmax_select(a, b, wl.cols, wl.cols, code, rows=wl.rows)
     assert binding.kernel_table()[kid].name == _PICKS[key]
+
+
+def test_few_rows_take_the_persistent_twin(lib):
+    """Row shapes whose rows x waves fill the chip's 8192 wave slots at most twice
+    run the persistent twin of the same shape, plain and causal."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
+                                                                               causal=causal)].name
+    assert pick(4096, 2, 4096) == "rowpf_bf16_w4_v2" and pick(4096, 2, 4097) == "row_bf16_w4_v2"
+    assert pick(8192, 2, 2048) == "rowpf_bf16_w8_v2" and pick(8192, 2, 2049) == "row_bf16_w8_v2"
+    assert pick(2048, 0, 2048, causal=True) == "causal_rowpf_f32_w4_v2"
+    assert pick(16384, 0, 16) == "row_f32_w4_v16"  # rows past the register-resident two-access shapes keep theirs
 
 
 def test_fp32_ragged_rule_follows_the_row_count(lib):
