@@ -575,6 +575,34 @@ def summarize_sweep(sweep_json: str) -> None:
 C3_BYTES = 8192 * 4096 * 2  # input bytes of the headline workload (8192 x 4096 fp16)
 
 
+def softmax_dispatch_table(groups_csv: str) -> list:
+    """Rows of the trace summary for the softmax kernels, one per (kernel, grid): a kernel
+    template serves several shapes, so its overall average mixes them.  A row kernel's grid
+    is one workgroup per row, which names the workload."""
+    by_rows = collections.defaultdict(list)
+    for key, wl in W.WORKLOADS.items():
+        by_rows[(wl.rows, {"f32": "F32", "f16": "F16", "bf16": "BF16"}[wl.dtype])].append(key)
+    rel = os.path.relpath(os.path.abspath(groups_csv), ROOT)
+    out = ["", f"Softmax dispatches by launch grid, from the per-dispatch trace reduced with"
+               f" `python3 bench.py --group-trace <trace csv> {rel}`; for a row kernel the grid is one workgroup"
+               " per row, so its row count names the workload:", "",
+           "| kernel | workgroups | threads each | workload | calls | average ns | min ns |", "|---|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(groups_csv)):
+        name = r["Kernel_Name"]
+        if "rws::softmax_" not in name:
+            continue
+        block = int(r["Workgroup_Size_X"])
+        wgs = int(r["Grid_Size_X"]) // block
+        tag = next((t for t in ("BF16", "F16", "F32") if f"rws::{t}," in name), "")
+        label = ""
+        if "softmax_row" in name:
+            label = ", ".join(k for k in by_rows.get((wgs, tag), []) if not k.startswith("wide"))
+        short = name.replace("void rws::", "").replace("(rws::Args)", "").replace("rws::", "")
+        out.append(f"| `{short}` | {wgs} | {block} | {label} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                   f"{float(r['MinNs']):.0f} |")
+    return out
+
+
 def summarize_trace(stats_csv):
     """Write profiles/kernel_trace_bench.md from a rocprofv3 --stats kernel_stats.csv."""
     rows = list(csv.DictReader(open(stats_csv)))
@@ -582,6 +610,9 @@ def summarize_trace(stats_csv):
     out = ["# Kernel trace of the default benchmark run on MI355X (gfx950)", "",
            "Command (repository root):", "",
            f"    rocprofv3 --kernel-trace --stats --output-format csv -d {out_dir} -o bench -- python3 bench.py --no-cpu",
+           *([f"    python3 bench.py --group-trace {out_dir}/bench_kernel_trace.csv "
+              f"{os.path.relpath(os.path.abspath(stats_csv.replace('_kernel_stats.csv', '_dispatch_groups.csv')), ROOT)}"]
+             if os.path.exists(stats_csv.replace("_kernel_stats.csv", "_dispatch_groups.csv")) else []),
            f"    python3 bench.py --summarize-trace {os.path.relpath(os.path.abspath(stats_csv), ROOT)}",
            "",
            "bench.py launches each kernel and shape untimed for 0.3 s (clock spin-up), then 50 warm-up + 200 timed"
@@ -589,12 +620,15 @@ def summarize_trace(stats_csv):
            "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal,"
            " line shift>`:",
            "",
-           "- `softmax_row<F32,4,4,1,false,true>`: c1 128x1000 fp32 (4000-byte rows, line-shifted);",
-           "- `softmax_row<F32,4,4,2,false,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
-           "- `softmax_row<F32,4,4,2,true,false>`: c2 with the mask and 1/8 scale fused (raw scores in);",
+           "- `softmax_row_pf<F32,4,4,1,false,true>`: c1 128x1000 fp32 (4000-byte rows, line-shifted; few rows:"
+           " the persistent twin);",
+           "- `softmax_row_pf<F32,4,4,2,false,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
+           "- `softmax_row_pf<F32,4,4,2,true,false>`: c2 with the mask and 1/8 scale fused (raw scores in);",
            "- `softmax_row<F16,8,4,2,false,false>`: c3 8192x4096 fp16 (the headline);",
            "- `softmax_row<F32,4,8,2,false,false>`: c4 4096x4096 fp32;",
-           "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape;",
+           "- `softmax_packed<...>` and `softmax_row<...>` at the 24 width-sweep tensors (c5), each once per width;",
+           "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape; `copy16<4>`,"
+           " `read16<4>` and `write16<4>` also at 8 MiB-1 GiB (the copy-ceiling table);",
            "- `unfused_reduce` / `unfused_elementwise`: the five-kernel unfused softmax on c3 and c4 (max, sub, exp, sum, div);",
            "- `softmax_online` (single pass) and `softmax_split_stats` + `softmax_split_norm` (split rows):"
            " 8 x 1048576 fp32 and 32 x 262144 bf16;",
@@ -603,23 +637,35 @@ def summarize_trace(stats_csv):
            "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    groups_csv = stats_csv.replace("_kernel_stats.csv", "_dispatch_groups.csv")
+    if os.path.exists(groups_csv):
+        out += softmax_dispatch_table(groups_csv)
     trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
     if not os.path.exists(trace_csv):  # the trace trimmed to the attention dispatches
         trace_csv = os.path.join(os.path.dirname(stats_csv), "attn_trace.csv")
+    if not os.path.exists(trace_csv) and os.path.exists(groups_csv):
+        trace_csv = groups_csv
     if os.path.exists(trace_csv):
-        groups = {}
+        groups = {}  # (dtype, workgroups) -> [calls, total ns, min ns]
         for r in csv.DictReader(open(trace_csv)):
-            if "attention_fwd_kernel" in r["Kernel_Name"]:
-                dt = "bf16" if "BF16" in r["Kernel_Name"] else "f16"
-                key = (dt, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
-                groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            if "attention_fwd_kernel" not in r["Kernel_Name"]:
+                continue
+            dt = "bf16" if "BF16" in r["Kernel_Name"] else "f16"
+            key = (dt, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+            if "AverageNs" in r:  # already reduced per (kernel, grid)
+                n, tot, lo = int(r["Calls"]), float(r["AverageNs"]) * int(r["Calls"]), float(r["MinNs"])
+            else:
+                n, tot = 1, float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                lo = tot
+            g = groups.setdefault(key, [0, 0.0, float("inf")])
+            g[0], g[1], g[2] = g[0] + n, g[1] + tot, min(g[2], lo)
         if groups:
             out += ["", "Attention dispatches by launch grid (workgroups = 32 heads x 4 batch x queries / 128), from the"
                     " per-dispatch trace of the same run:", "",
                     "| dtype | workgroups | keys | calls | average ns | min ns |", "|---|---|---|---|---|---|"]
-            for (dt, wg), ds in sorted(groups.items()):
+            for (dt, wg), (n, tot, lo) in sorted(groups.items()):
                 heads, per_block = 4 * 32, 128  # batch x heads, queries per workgroup
-                out.append(f"| {dt} | {wg} | {wg // heads * per_block} | {len(ds)} | {sum(ds) / len(ds):.0f} | {min(ds)} |")
+                out.append(f"| {dt} | {wg} | {wg // heads * per_block} | {n} | {tot / n:.0f} | {lo:.0f} |")
     path = os.path.join(PROFILE_DIR, "kernel_trace_bench.md")
     open(path, "w").write("\n".join(out) + "\n")
     print(open(path).read())
@@ -803,7 +849,10 @@ def trace_by_stream_size(trace_csv: str) -> dict:
         if kind is None:
             continue
         mib = int(r["Grid_Size_X"]) // 256 * 16384 // (1 << 20)
-        got[(kind, mib)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        if "AverageNs" in r:  # a per-(kernel, grid) summary of the trace: weight by its calls
+            got[(kind, mib)] += [float(r["AverageNs"])] * int(r["Calls"])
+        else:
+            got[(kind, mib)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return {k: sum(v) / len(v) for k, v in got.items()}
 
 
@@ -879,6 +928,20 @@ def summarize_chunk_copy(json_path: str, bench_json: str | None = None) -> None:
     print("\n".join(out))
 
 
+def group_trace(trace_csv: str, out_csv: str) -> None:
+    """Reduce a rocprofv3 per-dispatch kernel trace to one line per (kernel, grid, workgroup):
+    calls, average and minimum duration.  The full trace of a default run is too large to keep."""
+    g = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        g[(r["Kernel_Name"][:160], r["Grid_Size_X"], r["Workgroup_Size_X"])].append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    with open(out_csv, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Calls", "AverageNs", "MinNs"])
+        for (k, gx, wx), v in sorted(g.items()):
+            w.writerow([k, gx, wx, len(v), sum(v) / len(v), min(v)])
+
+
 def summarize_copy_sizes(json_path: str, trace_csv: str | None = None) -> None:
     """Write profiles/copy_ceiling_sizes.md from `bench.py --copy-sizes --copy-out` JSON
     (or from a default bench line, which carries the same table as copy_ceiling), with
@@ -891,8 +954,14 @@ def summarize_copy_sizes(json_path: str, trace_csv: str | None = None) -> None:
     cmd = [f"    python3 bench.py > {src}" if isinstance(d, dict) else f"    python3 bench.py --copy-sizes --copy-out {src}"]
     if trace_csv:
         tdir = os.path.dirname(os.path.relpath(os.path.abspath(trace_csv), ROOT))
-        cmd.append(f"    rocprofv3 --kernel-trace --stats --output-format csv -d {tdir} -o cs -- "
-                   f"python3 bench.py --copy-sizes --copy-out {tdir}/copy_sizes.json")
+        if os.path.basename(trace_csv).startswith("bench_"):  # the default run's trace (bench.py --no-cpu)
+            cmd.append(f"    rocprofv3 --kernel-trace --stats --output-format csv -d {tdir} -o bench -- "
+                       f"python3 bench.py --no-cpu")
+            cmd.append(f"    python3 bench.py --group-trace {tdir}/bench_kernel_trace.csv "
+                       f"{os.path.relpath(os.path.abspath(trace_csv), ROOT)}")
+        else:
+            cmd.append(f"    rocprofv3 --kernel-trace --stats --output-format csv -d {tdir} -o cs -- "
+                       f"python3 bench.py --copy-sizes --copy-out {tdir}/copy_sizes.json")
     cmd.append(f"    python3 bench.py --summarize-copy-sizes {src}" +
                (f" {os.path.relpath(os.path.abspath(trace_csv), ROOT)}" if trace_csv else ""))
     out = ["# Copy ceiling by size on MI355X (gfx950): the 16-byte copy kernel and its two directions", "",
@@ -1019,7 +1088,7 @@ def result_line(head: dict, shapes: dict, steps: int, warmup: int, cpu: dict | N
         "dtype": "f32",  # the arithmetic: every kernel widens to fp32 and accumulates there
         "data": "synthetic (seeded N(0,1), resident in HBM, rotating buffers > Infinity Cache)",
         "config": {"workload": head["workload"], "rows": head["rows"], "cols": head["cols"],
-                   "storage_dtype": head["dtype"],
+                   "storage_dtype": head["dtype"], "accum_dtype": "f32",
                    "kernel": head["kernel"], "buffers": head["buffers"], "peak_gbps": PEAK_GBPS,
                    "copy_kernel_gbps": head.get("copy_kernel_gbps"), "memcpy_gbps": head.get("memcpy_gbps")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
@@ -1125,6 +1194,8 @@ def main() -> int:
     ap.add_argument("--chunk-out", default=None, help="with --chunk-copy: write the table as JSON here")
     ap.add_argument("--summarize-chunk-copy", nargs="+", metavar="JSON [BENCH_JSON]", default=None,
                     help="write profiles/chunk_copy_shapes.md from a --chunk-out file (and a default bench line)")
+    ap.add_argument("--group-trace", nargs=2, metavar=("TRACE_CSV", "OUT_CSV"), default=None,
+                    help="reduce a rocprofv3 kernel trace to per-(kernel, grid) averages and exit")
     ap.add_argument("--counter-shapes", default=None,
                     help="launch the dispatch pick of these workload keys 10 times each, for counter runs")
     ap.add_argument("--manifest-out", default=None, help="with --counter-shapes: write what ran as JSON here")
@@ -1135,6 +1206,9 @@ def main() -> int:
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="leave the copy-ceiling table out of the default run")
     args = ap.parse_args()
+    if args.group_trace:
+        group_trace(*args.group_trace)
+        return 0
     if args.summarize_chunk_copy:
         summarize_chunk_copy(*args.summarize_chunk_copy[:2])
         return 0

@@ -210,3 +210,34 @@ def test_chunk_copy_summary_lists_the_row_kernels_of_each_shape(profile_dir, tmp
     text = (profile_dir / "chunk_copy_shapes.md").read_text()
     assert "| w4_v16 | 4 | 16 | 64 | 6050 | 6050, 6040, 6060 | f32 16384: 6143 |" in text
     assert "| copy16 |  |  |  | 6400 |" in text
+
+
+def test_trace_reduction_and_per_grid_softmax_rows(profile_dir, tmp_path):
+    """group_trace keeps one line per (kernel, grid); the summary names a row kernel's
+    workload by its grid (one workgroup per row) and reads attention grids from it."""
+    trace = tmp_path / "bench_kernel_trace.csv"
+    fields = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    c3 = "void rws::softmax_row<rws::F16, 8, 4, 2, false, false>(rws::Args)"
+    att = "void (anonymous namespace)::attention_fwd_kernel<rws::F16, 128, true>((anonymous namespace)::AttnArgs)"
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for s0, s1 in ((0, 22000), (50000, 73000)):
+            w.writerow({"Kernel_Name": c3, "Grid_Size_X": 8192 * 256, "Workgroup_Size_X": 256,
+                        "Start_Timestamp": s0, "End_Timestamp": s1})
+        w.writerow({"Kernel_Name": att, "Grid_Size_X": 1024 * 256, "Workgroup_Size_X": 256,
+                    "Start_Timestamp": 0, "End_Timestamp": 48000})
+    groups = tmp_path / "bench_dispatch_groups.csv"
+    bench.group_trace(str(trace), str(groups))
+    rows = list(csv.DictReader(open(groups)))
+    assert len(rows) == 2 and {r["Calls"] for r in rows} == {"2", "1"}
+    trace.unlink()  # the summary must work from the reduced file alone
+    stats = tmp_path / "bench_kernel_stats.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow({"Name": c3, "Calls": 2, "AverageNs": 22500, "MinNs": 22000, "MaxNs": 23000})
+    bench.summarize_trace(str(stats))
+    text = (profile_dir / "kernel_trace_bench.md").read_text()
+    assert "| `softmax_row<F16, 8, 4, 2, false, false>` | 8192 | 256 | c3 | 2 | 22500 | 22000 |" in text
+    assert "| f16 | 1024 | 1024 | 1 | 48000 | 48000 |" in text
