@@ -420,22 +420,18 @@ def cpu_baseline(res: Resident, budget_s: float) -> dict:
 
 
 def oracle_threaded(x: np.ndarray, wl, budget_s: float) -> dict:
-    """The same oracle function over contiguous row ranges, one range per host
-    thread (the C call releases the GIL), for a multi-core reference figure."""
-    from concurrent.futures import ThreadPoolExecutor
+    """The same oracle function over contiguous row ranges, one POSIX thread per
+    range (oracle_softmax_mt), for a multi-core reference figure."""
     from oracle import oracle
     threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    bounds = [wl.rows * k // threads for k in range(threads + 1)]
-    parts = [x[bounds[k]:bounds[k + 1]] for k in range(threads)]
     times = []
-    with ThreadPoolExecutor(threads) as pool:
-        t_all = time.perf_counter()
-        while True:
-            t0 = time.perf_counter()
-            list(pool.map(lambda part: oracle.softmax(part, wl.dtype), parts))
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() - t_all >= budget_s:
-                break
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.softmax_mt(x, wl.dtype, threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all >= budget_s:
+            break
     mean = sum(times) / len(times)
     cpu = ""
     try:

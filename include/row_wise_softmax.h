@@ -139,6 +139,34 @@ int softmax_fwd_causal_kernel(int kernel_id, const void *in, void *out, int64_t 
 int softmax_select(const void *in, const void *out, int64_t rows, int64_t cols, int64_t row_stride,
                    int dtype, int *kernel_id);
 
+/*
+ * softmax_fwd_variant -- the operation through a forced kernel variant and
+ * size, the way the width sweep of "GPU Kernels - Implementing and
+ * optimizing Softmax" (sections "CUDA scaling threads" and "Autotuning")
+ * forces a block size per width:
+ *   variant  SOFTMAX_VARIANT_PACKED, _ROW, _ONLINE or _ROW_PF;
+ *   block    packed: lanes per row (1, 2, 4, ..., 64); the others: threads per
+ *            workgroup (64 x waves).
+ * Of the compiled entries with that variant and size that take the call, it
+ * runs the one on 16-byte accesses if any, then with the fewest accesses per
+ * lane, then the fewest row groups in flight (softmax_fwd_kernel forces one
+ * exact entry instead).  Same arguments and errors as softmax_fwd, plus
+ * SOFTMAX_ERR_BAD_KERNEL when no such entry takes this width, stride or
+ * alignment, or the variant is unknown.
+ */
+int softmax_fwd_variant(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                        int variant, int block, void *stream);
+
+/*
+ * softmax_select_variant -- the variant and size (as softmax_fwd_variant
+ * takes them) that softmax_fwd picks for a contiguous tensor of `cols`
+ * columns of `dtype` on 16-byte-aligned buffers with many rows: the width
+ * dispatch by measured crossovers ("fused-softmax-roofline", the closing
+ * discussion of where the fused kernel loses).  Launches nothing.
+ * Errors: NULL_POINTER, BAD_DTYPE, BAD_SHAPE (cols < 1 or > 2^30).
+ */
+int softmax_select_variant(int64_t cols, int dtype, int *variant, int *block);
+
 /* softmax_select for softmax_fwd_causal: the causal entry it would launch. */
 int softmax_select_causal(const void *in, const void *out, int64_t rows, int64_t cols, int64_t row_stride,
                           int dtype, int *kernel_id);

@@ -8,8 +8,10 @@ double-precision implementation of the definition
 (the row softmax with max subtraction described on the pages "I Wrote My First
 GPU Kernel", section "What Fusion Actually Does", and "GPU Kernels -
 Implementing and optimizing Softmax", section "Baseline & Triton Softmax
-kernel").  Only the tests, the smoke check and the benchmark's CPU-baseline
-leg may import this module.  It never imports the GPU package, and the GPU
+kernel"), plus ``softmax_mt``, the same function run unchanged over
+contiguous row ranges on several threads for the CPU baseline's timing.
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  It never imports the GPU package, and the GPU
 package never imports it.
 """
 from __future__ import annotations
@@ -40,7 +42,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.run(
-            ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-shared", "-fPIC",
+            ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-shared", "-fPIC", "-pthread",
              "-o", tmp, _SRC, "-lm"],
             check=True,
         )
@@ -59,6 +61,11 @@ def _load():
         lib.oracle_softmax.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_void_p,
+        ]
+        lib.oracle_softmax_mt.restype = ctypes.c_int
+        lib.oracle_softmax_mt.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.oracle_softmax_causal.restype = ctypes.c_int
         lib.oracle_softmax_causal.argtypes = [
@@ -100,6 +107,25 @@ def softmax(x: np.ndarray, dtype: str, cols: int | None = None) -> np.ndarray:
     rc = lib.oracle_softmax(x.ctypes.data, code, rows, cols, stride, out.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_softmax rejected its arguments (rc={rc})")
+    return out
+
+
+def softmax_mt(x: np.ndarray, dtype: str, threads: int, cols: int | None = None) -> np.ndarray:
+    """:func:`softmax` over ``threads`` contiguous row ranges on POSIX threads
+    (the CPU baseline's all-cores timing); bit-identical to :func:`softmax`."""
+    lib = _load()
+    code = DTYPE_CODES[dtype]
+    want = np.float32 if dtype == "f32" else np.uint16
+    if x.dtype != want:
+        raise TypeError(f"oracle: {dtype} input must be held as {want.__name__}, got {x.dtype}")
+    if x.ndim != 2 or not x.flags.c_contiguous:
+        raise ValueError("oracle: input must be a 2-D C-contiguous array")
+    rows, stride = x.shape
+    cols = stride if cols is None else int(cols)
+    out = np.empty((rows, cols), dtype=np.float64)
+    rc = lib.oracle_softmax_mt(x.ctypes.data, code, rows, cols, stride, out.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_softmax_mt rejected its arguments (rc={rc})")
     return out
 
 

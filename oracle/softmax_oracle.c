@@ -40,6 +40,7 @@
  * handling relies on IEEE semantics).
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -139,6 +140,63 @@ int oracle_softmax(const void *in, int dtype, int64_t rows, int64_t cols,
             y[j] = y[j] / s;
     }
     return 0;
+}
+
+/*
+ * oracle_softmax_mt -- the same oracle over `threads` contiguous row ranges,
+ * one POSIX thread each, for timing the CPU baseline on all of a host's
+ * cores.  Each range is one unchanged call of oracle_softmax on its rows, so
+ * the result is bit-identical to the single-threaded call.  threads must be
+ * 1 ... 256 (fewer are used when there are fewer rows).
+ */
+struct oracle_range {
+    const void *in;
+    int dtype;
+    int64_t rows, cols, row_stride;
+    double *out;
+    int rc;
+};
+
+static void *oracle_range_run(void *arg)
+{
+    struct oracle_range *r = (struct oracle_range *)arg;
+    r->rc = oracle_softmax(r->in, r->dtype, r->rows, r->cols, r->row_stride, r->out);
+    return NULL;
+}
+
+int oracle_softmax_mt(const void *in, int dtype, int64_t rows, int64_t cols,
+                      int64_t row_stride, double *out, int threads)
+{
+    if (threads < 1 || threads > 256) return -1;
+    if (rows < 0 || cols < 0 || row_stride < cols) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (rows == 0 || cols == 0) return 0;
+    if (in == NULL || out == NULL) return -1;
+    if (threads > rows) threads = (int)rows;
+    const int64_t esz = dtype == ORACLE_F32 ? 4 : 2;
+    struct oracle_range r[256];
+    pthread_t tid[256];
+    int started[256] = {0};
+    for (int k = 0; k < threads; ++k) {
+        const int64_t r0 = rows * k / threads, r1 = rows * (k + 1) / threads;
+        r[k].in = (const char *)in + r0 * row_stride * esz;
+        r[k].dtype = dtype;
+        r[k].rows = r1 - r0;
+        r[k].cols = cols;
+        r[k].row_stride = row_stride;
+        r[k].out = out + r0 * cols;
+        r[k].rc = 0;
+    }
+    for (int k = 1; k < threads; ++k)
+        started[k] = pthread_create(&tid[k], NULL, oracle_range_run, &r[k]) == 0;
+    oracle_range_run(&r[0]);
+    int rc = r[0].rc;
+    for (int k = 1; k < threads; ++k) {
+        if (started[k]) pthread_join(tid[k], NULL);
+        else oracle_range_run(&r[k]); /* no thread: run the range here */
+        if (rc == 0) rc = r[k].rc;
+    }
+    return rc;
 }
 
 /*

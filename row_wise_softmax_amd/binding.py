@@ -58,6 +58,10 @@ def _load():
     lib.softmax_fwd_causal.argtypes = [vp, vp, i64, i64, i64, ctypes.c_float, i64, i32, vp]
     lib.softmax_fwd_causal_kernel.restype = i32
     lib.softmax_fwd_causal_kernel.argtypes = [i32, vp, vp, i64, i64, i64, ctypes.c_float, i64, i32, vp]
+    lib.softmax_fwd_variant.restype = i32
+    lib.softmax_fwd_variant.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.softmax_select_variant.restype = i32
+    lib.softmax_select_variant.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.softmax_select_causal.restype = i32
     lib.softmax_select_causal.argtypes = [vp, vp, i64, i64, i64, i32, ctypes.POINTER(i32)]
     lib.softmax_select.restype = i32
@@ -143,6 +147,23 @@ def softmax_select(in_ptr: int, out_ptr: int, cols: int, row_stride: int, dtype:
     fn = lib.softmax_select_causal if causal else lib.softmax_select
     _check(fn(in_ptr, out_ptr, rows, cols, row_stride, dtype, ctypes.byref(kid)), "softmax_select")
     return kid.value
+
+
+def softmax_fwd_variant(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int, dtype: int,
+                        variant: int, block: int, stream: int = 0) -> None:
+    """Raw entry point through a forced variant (0 packed, 1 row, 2 online, 3 row_pf) and size
+    (packed: lanes per row; else threads per workgroup)."""
+    lib = _load()
+    _check(lib.softmax_fwd_variant(in_ptr, out_ptr, rows, cols, row_stride, dtype, variant, block, stream),
+           "softmax_fwd_variant")
+
+
+def softmax_select_variant(cols: int, dtype: int) -> tuple[int, int]:
+    """(variant, block) softmax_fwd picks for a contiguous, aligned tensor of this width."""
+    lib = _load()
+    v, b = ctypes.c_int(-1), ctypes.c_int(-1)
+    _check(lib.softmax_select_variant(cols, dtype, ctypes.byref(v), ctypes.byref(b)), "softmax_select_variant")
+    return v.value, b.value
 
 
 def bench_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None:

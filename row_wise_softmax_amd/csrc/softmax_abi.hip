@@ -177,6 +177,29 @@ const Entry* select_entry(const void* in, const void* out, int64_t rows, int64_t
     return find(dtype, SOFTMAX_VARIANT_ONLINE, causal, 1, 64 * w, 8, 1);
 }
 
+// The plain table entry softmax_fwd_variant runs: of the entries of `variant`
+// for this dtype whose lanes per row (packed) or threads per workgroup (row,
+// row_pf, online) equal `block` and that take the call, the one on 16-byte
+// accesses if any, then with the fewest accesses per lane, then the fewest
+// row groups in flight.
+const Entry* entry_for_variant(const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype,
+                               int variant, int block) {
+    int n;
+    const Entry* t = table_of(dtype, &n);
+    const Entry* best = nullptr;
+    for (int i = 0; i < n; ++i) {
+        const Entry& e = t[i];
+        if (e.causal || e.variant != variant) continue;
+        if ((variant == SOFTMAX_VARIANT_PACKED ? e.lanes : e.block) != block) continue;
+        if (!fits(e, in, out, cols, row_stride, dtype)) continue;
+        if (best == nullptr || (e.vec > 1) > (best->vec > 1) ||
+            ((e.vec > 1) == (best->vec > 1) &&
+             (e.vpl < best->vpl || (e.vpl == best->vpl && e.groups < best->groups))))
+            best = &e;
+    }
+    return best;
+}
+
 // Shared validation.  Returns SOFTMAX_OK, or an error; *empty is set when
 // there is nothing to launch.
 int validate(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
@@ -509,6 +532,33 @@ int softmax_fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, i
 int softmax_fwd_causal_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols,
                               int64_t row_stride, float scale, int64_t diag, int dtype, void* stream) {
     return fwd_kernel(kernel_id, in, out, rows, cols, row_stride, dtype, true, scale, diag, stream);
+}
+
+int softmax_fwd_variant(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,
+                        int variant, int block, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    if (variant < SOFTMAX_VARIANT_PACKED || variant > SOFTMAX_VARIANT_ROW_PF) return SOFTMAX_ERR_BAD_KERNEL;
+    if (empty) return SOFTMAX_OK;
+    const Entry* e = entry_for_variant(in, out, cols, row_stride, dtype, variant, block);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    return launch(*e, in, out, rows, cols, row_stride, float(kLog2eD), 0, static_cast<hipStream_t>(stream));
+}
+
+int softmax_select_variant(int64_t cols, int dtype, int* variant, int* block) {
+    if (variant == nullptr || block == nullptr) return SOFTMAX_ERR_NULL_POINTER;
+    if (dtype != SOFTMAX_F32 && dtype != SOFTMAX_F16 && dtype != SOFTMAX_BF16) return SOFTMAX_ERR_BAD_DTYPE;
+    if (cols < 1 || cols > kMaxCols) return SOFTMAX_ERR_BAD_SHAPE;
+    // A contiguous tensor on 256-byte-aligned buffers with many rows (never
+    // dereferenced): the pick of softmax_fwd for this width and dtype.
+    const void* in = reinterpret_cast<const void*>(uintptr_t(1) << 40);
+    const void* out = reinterpret_cast<const void*>(uintptr_t(1) << 41);
+    const Entry* e = select_entry(in, out, int64_t(1) << 20, cols, cols, dtype, false);
+    if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
+    *variant = e->variant;
+    *block = e->variant == SOFTMAX_VARIANT_PACKED ? e->lanes : e->block;
+    return SOFTMAX_OK;
 }
 
 int softmax_select(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype,

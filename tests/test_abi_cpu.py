@@ -346,3 +346,32 @@ def test_bench_chunk_copy_argument_errors(lib):
     assert cc(A, A + 1024, 64 << 10, 4, 16, None) == 4
     assert cc(A, far, 0, 4, 16, None) == 0
     assert binding.CHUNK_COPY_SHAPES[-1] == (16, 4)
+
+
+def test_select_variant_reports_the_dispatch_pick(lib):
+    """softmax_select_variant gives the (variant, size) of softmax_fwd's pick for
+    a contiguous, aligned tensor with many rows (variant 0 packed, 1 row)."""
+    from row_wise_softmax_amd import workloads as W
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    for key in ("c3", "c4", "c5_bf16_32", "c5_bf16_1000", "c5_f32_3000", "c5_f32_16384", "c5_bf16_16384"):
+        wl = W.WORKLOADS[key]
+        code = W.dtype_code(wl.dtype)
+        k = table[binding.softmax_select(a, b, wl.cols, wl.cols, code, rows=1 << 20)]
+        want = ({"packed": 0, "row": 1, "online": 2, "row_pf": 3}[k.variant],
+                k.lanes if k.variant == "packed" else k.block)
+        assert binding.softmax_select_variant(wl.cols, code) == want, key
+    v, blk = ctypes.c_int(), ctypes.c_int()
+    assert lib.softmax_select_variant(0, 0, ctypes.byref(v), ctypes.byref(blk)) == 2
+    assert lib.softmax_select_variant(8, 9, ctypes.byref(v), ctypes.byref(blk)) == 3
+    assert lib.softmax_select_variant(8, 0, None, ctypes.byref(blk)) == 1
+
+
+def test_fwd_variant_rejects_before_any_launch(lib):
+    far = A + (1 << 40)
+    fv = lib.softmax_fwd_variant
+    assert fv(A, far, 4, 64, 64, 0, 7, 64, None) == 5       # unknown variant
+    assert fv(A, far, 4, 64, 64, 0, 0, 3, None) == 5        # no packed entry with 3 lanes per row
+    assert fv(A, far, 4, 1 << 20, 1 << 20, 0, 1, 256, None) == 5  # no row entry holds 2^20 columns
+    assert fv(A, far, 0, 64, 64, 0, 0, 16, None) == 0       # empty: nothing launched
+    assert fv(A, far, -1, 64, 64, 0, 0, 16, None) == 2

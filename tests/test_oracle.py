@@ -228,3 +228,21 @@ def test_page_traffic_and_flop_figures():
     c = fig["copy_ceiling_example"]
     gbps = W.algorithmic_bytes(c["rows"], c["cols"], c["dtype"]) / (c["fused_ms"] * 1e-3) / 1e9
     assert abs(gbps - c["fused_gbps"]) / c["fused_gbps"] < 0.01
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("threads", [1, 3, 8, 64])
+def test_threaded_oracle_is_bit_identical(oracle_mod, dtype, threads):
+    """oracle_softmax_mt runs the single-threaded function unchanged on row
+    ranges: same bits for every thread count, stride padding included."""
+    x = W.random_matrix(seed=31, rows=37, cols=250, dtype=dtype, sigma=3.0, row_stride=256)
+    one = oracle_mod.softmax(x, dtype, cols=250)
+    many = oracle_mod.softmax_mt(x, dtype, threads, cols=250)
+    assert np.array_equal(one.view(np.uint64), many.view(np.uint64))
+
+
+def test_threaded_oracle_rejects_bad_thread_counts(oracle_mod):
+    x = W.random_matrix(seed=32, rows=4, cols=8, dtype="f32")
+    for bad in (0, -1, 257):
+        with pytest.raises(ValueError):
+            oracle_mod.softmax_mt(x, "f32", bad)

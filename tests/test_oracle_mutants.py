@@ -55,7 +55,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     mutant_c = tmp_path / "mutant.c"
     mutant_c.write_text(src.replace(old, new, 1))
     lib = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-o", str(lib), str(mutant_c), "-lm"],
+    subprocess.run(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", "-o", str(lib), str(mutant_c), "-lm"],
                    check=True)
     env = dict(os.environ, ROW_SOFTMAX_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",

@@ -459,3 +459,23 @@ def test_line_shifted_rows(kid):
     check_padding_untouched(y, cols, dtype, label=k.name)
     around = out_raw.cpu().numpy()
     assert (around[:48] == 0xA5).all() and (around[48 + y.nbytes:] == 0xA5).all(), "bytes outside the output written"
+
+
+# ------------------------------------------------- forced variant and size
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant,block,cols", [(0, 8, 32), (0, 64, 512), (0, 64, 1000), (1, 256, 2048),
+                                                 (1, 512, 3000), (1, 1024, 8192), (2, 256, 70001),
+                                                 (2, 1024, 4096), (3, 256, 4096), (3, 128, 1000)])
+def test_forced_variant_and_size(dtype, variant, block, cols):
+    """softmax_fwd_variant (a variant and a lane / workgroup size, as a width sweep
+    forces them) against the oracle."""
+    import torch
+    _say(f"variant {variant} block {block} {dtype} cols={cols}")
+    x = W.random_matrix(seed=51, rows=67, cols=cols, dtype=dtype, sigma=2.0)
+    xd = to_device(x, dtype)
+    out = torch.empty_like(xd)
+    binding.softmax_fwd_variant(xd.data_ptr(), out.data_ptr(), 67, cols, cols, W.dtype_code(dtype), variant, block,
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check(to_host(out, dtype), x, dtype, O.softmax(x, dtype), label=f"variant {variant}/{block} {dtype} {cols}")
