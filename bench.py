@@ -333,10 +333,13 @@ def measure_shape(key: str, steps: int, warmup: int, with_copy: bool, with_unfus
     return d
 
 
-# Sources the fused softmax kernels are built from (attention and the unfused
-# baseline are separate kernels and do not change the softmax's traffic).
-SOFTMAX_SOURCES = ("kernel_table.hpp", "softmax_abi.hip", "softmax_kernels.hpp", "table_bf16.hip",
-                   "table_entries.inc", "table_f16.hip", "table_f32.hip")
+# The device code of the fused softmax kernels (attention and the unfused
+# baseline are separate kernels and do not change the softmax's traffic).  The
+# host side (softmax_abi.hip: validation, dispatch, launch) is left out; the
+# kernel a stored counter run measured must instead be the one the dispatch
+# picks now (stored_traffic).
+SOFTMAX_SOURCES = ("kernel_table.hpp", "softmax_kernels.hpp", "table_bf16.hip", "table_entries.inc",
+                   "table_f16.hip", "table_f32.hip")
 
 
 def _code_only(text: str) -> str:
@@ -357,8 +360,23 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str) -> dict | None:
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match these sources."""
+def kernel_signature(info) -> str:
+    """The start of the demangled name rocprofv3 reports for a table entry (KernelInfo):
+    template, element type, elements per access, then waves and accesses (row kernels) or
+    lanes, accesses and groups (packed)."""
+    elem = {0: "F32", 1: "F16", 2: "BF16"}[info.dtype]
+    tmpl = {"packed": "softmax_packed", "row": "softmax_row", "row_pf": "softmax_row_pf",
+            "online": "softmax_online"}[info.variant]
+    if info.variant == "packed":
+        args = f"{info.lanes}, {info.vecs_per_lane}, {info.groups}"
+    else:
+        args = f"{info.lanes // 64}, {info.vecs_per_lane}"
+    return f"void rws::{tmpl}<rws::{elem}, {info.vec_elems}, {args}, {'true' if info.causal else 'false'}"
+
+
+def stored_traffic(workload: str, kernel_info=None) -> dict | None:
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on this
+    device code and (when kernel_info is given) on the kernel the dispatch picks now."""
     path = os.path.join(PROFILE_DIR, f"counters_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -368,6 +386,8 @@ def stored_traffic(workload: str) -> dict | None:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("source_digest") != source_digest():
+        return None
+    if kernel_info is not None and not kv.get("kernel", "").startswith(kernel_signature(kernel_info)):
         return None
     try:
         return {"bytes": float(kv["hbm_bytes_per_dispatch"]), "source": os.path.relpath(path, ROOT)}
@@ -1306,7 +1326,8 @@ def main() -> int:
     if not args.no_cpu:
         log(f"[bench] cpu baseline: oracle on {head['workload']} for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(res, args.cpu_seconds)
-    line = result_line(head, shapes, args.steps, args.warmup, cpu, stored_traffic(head["workload"]))
+    info = next(k for k in binding.kernel_table() if k.name == head["kernel"])
+    line = result_line(head, shapes, args.steps, args.warmup, cpu, stored_traffic(head["workload"], info))
     if copy_table is not None:
         line["copy_ceiling"] = copy_table
     wide = [v for k, v in shapes.items() if k.startswith("c5_") and v["cols"] >= 2048]

@@ -54,6 +54,12 @@ def test_counter_calibration_and_digest_guard(profile_dir, tmp_path):
     text = (profile_dir / "counters_c3_8192x4096_f16.txt").read_text()
     assert f"source_digest: {bench.source_digest()}" in text
     assert "traffic_over_algorithmic: 1.00500" in text
+    # counters of another kernel than the dispatch picks now are not reported
+    from row_wise_softmax_amd import binding
+    table = {k.name: k for k in binding.kernel_table()}
+    assert bench.stored_traffic("c3_8192x4096_f16", table["row_f16_w4_v2"]) is not None
+    assert bench.stored_traffic("c3_8192x4096_f16", table["row_f16_w2_v4"]) is None
+    assert bench.stored_traffic("c3_8192x4096_f16", table["rowpf_f16_w4_v2"]) is None
     # counters taken on other kernel sources are not reported
     (profile_dir / "counters_c3_8192x4096_f16.txt").write_text(
         text.replace(bench.source_digest(), "0000000000000000"))
