@@ -114,6 +114,22 @@ int softmax_fwd_causal(const void *in, void *out, int64_t rows, int64_t cols, in
                        float scale, int64_t diag, int dtype, void *stream);
 
 /*
+ * softmax_fwd_causal_batched -- softmax_fwd_causal over a batch of score
+ * matrices stacked row-wise, such as attention scores [batch][heads][n][m]
+ * seen as (batch * heads * n) rows of m columns: row r of the call is row
+ * i = r mod rows_per_matrix of its matrix, keeps the columns j <= i + diag,
+ * and is scaled and normalised as in softmax_fwd_causal.  The mask is the one
+ * "Dissecting Memory Bandwidth & SRAM Tiling in Triton" (section "Writing the
+ * Kernel in OpenAI Triton") applies to every head's score matrix.
+ *   rows_per_matrix  rows of one matrix (>= 1); rows must be a multiple of it
+ *                    (else SOFTMAX_ERR_BAD_SHAPE).  rows_per_matrix == rows
+ *                    is softmax_fwd_causal.
+ * Other arguments, layout, ownership, aliasing and errors as softmax_fwd_causal.
+ */
+int softmax_fwd_causal_batched(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
+                               int64_t rows_per_matrix, float scale, int64_t diag, int dtype, void *stream);
+
+/*
  * softmax_fwd_kernel -- the same operation through one forced entry of the
  * compiled kernel table (for width sweeps and tests).  Same arguments and
  * errors as softmax_fwd, plus SOFTMAX_ERR_BAD_KERNEL when `kernel_id` is out of

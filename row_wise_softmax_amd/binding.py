@@ -56,6 +56,8 @@ def _load():
     lib.softmax_fwd_kernel.argtypes = [i32, vp, vp, i64, i64, i64, i32, vp]
     lib.softmax_fwd_causal.restype = i32
     lib.softmax_fwd_causal.argtypes = [vp, vp, i64, i64, i64, ctypes.c_float, i64, i32, vp]
+    lib.softmax_fwd_causal_batched.restype = i32
+    lib.softmax_fwd_causal_batched.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_float, i64, i32, vp]
     lib.softmax_fwd_causal_kernel.restype = i32
     lib.softmax_fwd_causal_kernel.argtypes = [i32, vp, vp, i64, i64, i64, ctypes.c_float, i64, i32, vp]
     lib.softmax_fwd_variant.restype = i32
@@ -130,6 +132,15 @@ def softmax_fwd_causal(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stri
     lib = _load()
     _check(lib.softmax_fwd_causal(in_ptr, out_ptr, rows, cols, row_stride, scale, diag, dtype, stream),
            "softmax_fwd_causal")
+
+
+def softmax_fwd_causal_batched(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int,
+                               rows_per_matrix: int, scale: float, diag: int, dtype: int, stream: int = 0) -> None:
+    """Raw entry point of the causal softmax over stacked score matrices (row i of each matrix
+    keeps j <= i + diag, i counted within its matrix of rows_per_matrix rows)."""
+    lib = _load()
+    _check(lib.softmax_fwd_causal_batched(in_ptr, out_ptr, rows, cols, row_stride, rows_per_matrix, scale, diag,
+                                          dtype, stream), "softmax_fwd_causal_batched")
 
 
 def softmax_fwd_causal_kernel(kernel_id: int, in_ptr: int, out_ptr: int, rows: int, cols: int,
@@ -332,17 +343,13 @@ def softmax(x, out=None, kernel_id: int | None = None, causal: bool = False, sca
 
     ``out`` (optional) must match ``x`` in shape, dtype and strides; it may be
     ``x`` itself (in place).  With ``causal=True`` row i keeps columns
-    j <= i + diag and the kept entries are multiplied by ``scale`` first; the
-    causal form takes one matrix (1-D or 2-D input) only, since the library
-    counts the row index i over the whole call.  The call is asynchronous on
-    torch's current stream.
+    j <= i + diag and the kept entries are multiplied by ``scale`` first; for
+    a tensor of rank > 2 ([..., n, m] score matrices) i counts within each
+    matrix.  The call is asynchronous on torch's current stream.
     """
     import torch
-    if causal and x.dim() > 2:
-        # Flattening [..., n, n] would number rows across matrices, so every
-        # matrix after the first would keep (almost) every column.
-        raise ValueError("softmax: causal=True takes a 1-D or 2-D tensor (one score matrix); "
-                         "call it once per matrix of a batched [..., n, n] input")
+    if causal and x.dim() > 2 and kernel_id is not None:
+        raise ValueError("softmax: a forced causal kernel takes one score matrix (1-D or 2-D input)")
     if not x.is_cuda:
         raise ValueError("softmax: input must be a GPU tensor")
     code = _torch_dtype_code(x)
@@ -354,7 +361,10 @@ def softmax(x, out=None, kernel_id: int | None = None, causal: bool = False, sca
     with torch.cuda.device(x.device):  # the library launches on the current device
         stream = torch.cuda.current_stream(x.device).cuda_stream
         if causal:
-            if kernel_id is None:
+            if x.dim() > 2:  # contiguous (checked by _as_rows): matrices of x.shape[-2] rows each
+                softmax_fwd_causal_batched(x.data_ptr(), out.data_ptr(), rows, cols, stride, x.shape[-2], scale,
+                                           diag, code, stream)
+            elif kernel_id is None:
                 softmax_fwd_causal(x.data_ptr(), out.data_ptr(), rows, cols, stride, scale, diag, code, stream)
             else:
                 softmax_fwd_causal_kernel(kernel_id, x.data_ptr(), out.data_ptr(), rows, cols, stride, scale,

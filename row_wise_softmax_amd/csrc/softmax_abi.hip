@@ -282,13 +282,14 @@ bool line_shift_fits(const Entry& e, const void* out, int64_t cols, int64_t row_
 }
 
 int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, float coef,
-           int64_t diag, hipStream_t stream) {
+           int64_t diag, hipStream_t stream, int64_t period = 0) {
     rws::Args a;
     a.in = in;
     a.out = out;
     a.rows = rows;
     a.stride = row_stride / e.vec;
     a.diag = diag;
+    a.period = period;
     a.nacc = int(cols / e.vec);
     a.cols = int(cols);
     a.coef = coef;
@@ -320,7 +321,7 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
 }
 
 int fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, bool causal,
-        float scale, int64_t diag, void* stream) {
+        float scale, int64_t diag, void* stream, int64_t period = 0) {
     bool empty;
     int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
     if (st != SOFTMAX_OK) return st;
@@ -329,7 +330,7 @@ int fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_strid
     if (empty) return SOFTMAX_OK;
     const Entry* e = select_entry(in, out, rows, cols, row_stride, dtype, causal);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
-    return launch(*e, in, out, rows, cols, row_stride, coef, diag, static_cast<hipStream_t>(stream));
+    return launch(*e, in, out, rows, cols, row_stride, coef, diag, static_cast<hipStream_t>(stream), period);
 }
 
 int fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
@@ -522,6 +523,15 @@ int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t r
 int softmax_fwd_causal(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, float scale,
                        int64_t diag, int dtype, void* stream) {
     return fwd(in, out, rows, cols, row_stride, dtype, true, scale, diag, stream);
+}
+
+int softmax_fwd_causal_batched(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,
+                               int64_t rows_per_matrix, float scale, int64_t diag, int dtype, void* stream) {
+    bool empty;
+    int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
+    if (st != SOFTMAX_OK) return st;
+    if (rows_per_matrix < 1 || rows % rows_per_matrix != 0) return SOFTMAX_ERR_BAD_SHAPE;
+    return fwd(in, out, rows, cols, row_stride, dtype, true, scale, diag, stream, rows_per_matrix);
 }
 
 int softmax_fwd_kernel(int kernel_id, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride,

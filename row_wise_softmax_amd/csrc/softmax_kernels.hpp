@@ -304,6 +304,7 @@ struct Args {
     int64_t stride;   // row stride in accesses (elements / access width)
     int64_t nblocks;  // logical workgroups; the grid may be smaller and loop
     int64_t diag;     // causal kernels: row i keeps columns j <= i + diag
+    int64_t period;   // causal kernels: rows per matrix, i counted within its matrix; 0: one matrix
     int nacc;         // accesses per row (cols / access width)
     int cols;         // elements per row
     float coef;       // scale * log2(e); log2(e) for the plain softmax
@@ -329,17 +330,20 @@ __device__ inline int line_shift(const void* row_out) {
     }
 }
 
-// Columns row `row` keeps: all of them, or j <= row + diag for the causal
-// (scaled, masked) softmax of "Dissecting Memory Bandwidth & SRAM Tiling in
-// Triton", section "Writing the Kernel in OpenAI Triton".  No sum can overflow.
+// Columns row `row` keeps: all of them, or the columns j <= i + diag for the
+// causal (scaled, masked) softmax of "Dissecting Memory Bandwidth & SRAM
+// Tiling in Triton", section "Writing the Kernel in OpenAI Triton", with i the
+// row's index within its score matrix (row mod period for a batch of
+// matrices, row itself for one).  No sum can overflow.
 template <bool Causal>
 __device__ inline int kept_cols(int64_t row, const Args& a) {
     if constexpr (!Causal) {
         return a.cols;
     } else {
+        const int64_t i = a.period > 0 ? row % a.period : row;
         if (a.diag >= a.cols) return a.cols;
-        if (a.diag < -row) return 0;
-        const int64_t k = row + a.diag + 1;
+        if (a.diag < -i) return 0;
+        const int64_t k = i + a.diag + 1;
         return k > a.cols ? a.cols : int(k);
     }
 }

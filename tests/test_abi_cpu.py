@@ -315,10 +315,21 @@ def test_row_shapes_of_accepted_views():
         binding._as_rows(torch.zeros(2, 3, 6)[:, :, :5])
 
 
-def test_causal_on_a_batch_of_matrices_is_rejected():
+def test_forced_causal_kernel_on_a_batch_of_matrices_is_rejected():
     import torch
-    with pytest.raises(ValueError, match="causal=True takes a 1-D or 2-D"):
-        binding.softmax(torch.zeros(2, 4, 4), causal=True)
+    with pytest.raises(ValueError, match="forced causal kernel takes one score matrix"):
+        binding.softmax(torch.zeros(2, 4, 4), causal=True, kernel_id=0)
+
+
+def test_batched_causal_rejects_before_any_launch(lib):
+    far = A + (1 << 40)
+    fb = lib.softmax_fwd_causal_batched
+    c = ctypes.c_float
+    assert fb(A, far, 12, 64, 64, 0, c(0.5), 0, 0, None) == 2    # no matrix height
+    assert fb(A, far, 12, 64, 64, 5, c(0.5), 0, 0, None) == 2    # 12 rows are not whole matrices of 5
+    assert fb(A, far, 12, 64, 64, 4, c(-1.0), 0, 0, None) == 7   # bad scale
+    assert fb(A, far, 0, 64, 64, 4, c(0.5), 0, 0, None) == 0     # empty
+    assert fb(A, A + 8, 12, 64, 64, 4, c(0.5), 0, 0, None) == 4  # overlap
 
 
 def test_noalloc_split_rejects_before_any_launch(lib):

@@ -115,3 +115,33 @@ def test_large_scale_and_huge_values():
     for scale in (1.0, 8.0, 1e-3):
         y = run(x, "f32", causal=True, scale=scale, diag=400)
         check(y, x, "f32", O.softmax_causal(x, "f32", scale, 400), label=f"huge scale={scale}")
+
+
+# ------------------------------------------- a batch of score matrices
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,diag", [((2, 3, 100, 100), 0), ((4, 5, 40, 40), 3), ((2, 2, 300, 320), 20),
+                                        ((1, 2, 64, 4096), 4032), ((3, 1, 1000, 1000), -5)])
+def test_batched_causal_masks_each_matrix(dtype, shape, diag):
+    """softmax_fwd_causal_batched: every matrix of [b][h][n][m] scores masked on
+    its own row index, against the oracle run matrix by matrix; the torch call
+    on the 4-D tensor gives the same bits."""
+    import torch
+
+    from gpu_util import to_device, to_host
+    b, h, n, m = shape
+    _say(f"batched causal {dtype} {shape} diag={diag}")
+    x = W.random_matrix(seed=61, rows=b * h * n, cols=m, dtype=dtype, sigma=2.0)
+    xd = to_device(x, dtype)
+    out = torch.empty_like(xd)
+    binding.softmax_fwd_causal_batched(xd.data_ptr(), out.data_ptr(), b * h * n, m, m, n, 0.5, diag,
+                                       W.dtype_code(dtype), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    y = to_host(out, dtype)
+    ref = np.concatenate([O.softmax_causal(np.ascontiguousarray(x[k * n:(k + 1) * n]), dtype, 0.5, diag)
+                          for k in range(b * h)])
+    keep = np.tile(causal_mask(n, m, diag), (b * h, 1))
+    check(y, x, dtype, ref, label=f"batched causal {dtype} {shape}", keep=keep)
+    y4 = binding.softmax(xd.view(b, h, n, m), causal=True, scale=0.5, diag=diag)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(y4.reshape(b * h * n, m), dtype), y)
