@@ -213,7 +213,9 @@ def causal_c2(steps: int, warmup: int) -> dict:
 
 
 def split_shapes(steps: int, warmup: int) -> dict:
-    """Few, wide rows: softmax_fwd (one workgroup per row) vs the split-row path."""
+    """Few, wide rows: softmax_fwd (which splits them through its output), the
+    width's one-workgroup-per-row kernel forced, and softmax_fwd_split with a
+    caller workspace."""
     import torch
     out = {}
     for key in ("wide_f32", "wide_bf16"):
@@ -221,18 +223,24 @@ def split_shapes(steps: int, warmup: int) -> dict:
         res = Resident(wl)
         nbytes = binding.split_workspace_bytes(wl.rows, wl.cols, res.code)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        one = time_launches(res.softmax, res.n, steps, warmup)
+        fwd = time_launches(res.softmax, res.n, steps, warmup)
+        variant, block = binding.softmax_select_variant(wl.cols, res.code)
+        one = time_launches(lambda i: binding.softmax_fwd_variant(res.ins[i].data_ptr(), res.outs[i].data_ptr(),
+                                                                   wl.rows, wl.cols, wl.cols, res.code, variant, block,
+                                                                   res.stream), res.n, steps, warmup)
         spl = time_launches(lambda i: binding.softmax_fwd_split(res.ins[i].data_ptr(), res.outs[i].data_ptr(), wl.rows,
                                                                  wl.cols, wl.cols, res.code, ws.data_ptr(), nbytes, 1,
                                                                  res.stream), res.n, steps, warmup)
+        rate = lambda ms: round(wl.bytes / (ms * 1e-3) / 1e9, 1)
         d = {"workload": wl.name, "rows": wl.rows, "cols": wl.cols, "dtype": wl.dtype,
-             "single_pass_kernel": kernel_name(res), "single_pass_us": round(one * 1e3, 3),
-             "single_pass_gbps": round(wl.bytes / (one * 1e-3) / 1e9, 1),
-             "split_us": round(spl * 1e3, 3), "split_gbps": round(wl.bytes / (spl * 1e-3) / 1e9, 1),
-             "note": "gbps by the metric's 2*rows*cols*size bytes; in the counter runs (profiles/counters_wide_rows.txt) "
-                     "the single-pass online kernel moved 1.00-1.04x and the split path 1.5x those bytes"}
-        log(f"[bench] {wl.name}: softmax_fwd {d['single_pass_us']} us ({d['single_pass_gbps']} GB/s)"
-            f"  split {d['split_us']} us ({d['split_gbps']} GB/s)")
+             "kernel": kernel_name(res), "us": round(fwd * 1e3, 3), "gbps": rate(fwd),
+             "one_wg_per_row": {"variant": variant, "block": block, "us": round(one * 1e3, 3), "gbps": rate(one)},
+             "split_workspace": {"us": round(spl * 1e3, 3), "gbps": rate(spl)},
+             "note": "gbps by the metric's 2*rows*cols*size bytes; softmax_fwd splits these rows with the tile pairs "
+                     "kept in its output (three kernels), softmax_fwd_split with a workspace (two); in the counter runs "
+                     "(profiles/counters_wide_rows.txt) the split moved 1.5x those bytes, one workgroup per row 1.0x"}
+        log(f"[bench] {wl.name}: softmax_fwd {d['us']} us ({d['gbps']} GB/s, {d['kernel']})"
+            f"  one wg per row {d['one_wg_per_row']['us']} us  split+workspace {d['split_workspace']['us']} us")
         out[key] = d
         del res, ws
     torch.cuda.synchronize()
@@ -275,6 +283,8 @@ def attention_shapes(steps: int, warmup: int) -> dict:
 def kernel_name(res: Resident) -> str:
     kid = binding.softmax_select(res.ins[0].data_ptr(), res.outs[0].data_ptr(), res.wl.cols, res.wl.cols,
                                  res.code, rows=res.wl.rows)
+    if kid == binding.SPLIT_KERNEL:
+        return f"split_{res.wl.dtype}_via_out"
     return binding.kernel_table()[kid].name
 
 
@@ -646,8 +656,10 @@ def summarize_trace(stats_csv):
            "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape; `copy16<4>`,"
            " `read16<4>` and `write16<4>` also at 8 MiB-1 GiB (the copy-ceiling table);",
            "- `unfused_reduce` / `unfused_elementwise`: the five-kernel unfused softmax on c3 and c4 (max, sub, exp, sum, div);",
-           "- `softmax_online` (single pass) and `softmax_split_stats` + `softmax_split_norm` (split rows):"
-           " 8 x 1048576 fp32 and 32 x 262144 bf16;",
+           "- few, wide rows (8 x 1048576 fp32, 32 x 262144 bf16): `softmax_split_stats` + `softmax_split_merge` +"
+           " `softmax_split_norm` with `Slot = true` (softmax_fwd's split, pairs kept in the output), the same two"
+           " without the merge and `Slot = false` (softmax_fwd_split, caller workspace), and the width's"
+           " one-workgroup-per-row kernel forced;",
            "- `attention_fwd_kernel<E,128,true>`: causal attention forward, batch 4, 32 heads, head dim 128"
            " (fp16 at 1024 and 4096 keys, bf16 at 4096; split by launch grid below).", "",
            "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
@@ -906,6 +918,79 @@ def chunk_copy(steps: int, warmup: int, mib: int = CHUNK_COPY_MIB, rounds: int =
     return out
 
 
+SPLIT_CROSS_ROWS = (8, 16, 32, 64, 128, 192, 256)
+SPLIT_CROSS_ROW_KIB = (64, 128, 256, 512, 1024, 2048, 4096)
+SPLIT_CROSS_MAX_BYTES = 512 << 20
+
+
+def split_crossover(steps: int, warmup: int) -> list:
+    """Few, very wide rows: for each dtype, row size and row count, the width's
+    one-workgroup-per-row kernel (softmax_fwd_variant at softmax_select_variant's
+    pick), softmax_fwd_split with a workspace (always split), and softmax_fwd
+    itself (which splits through its output where its rule says so).  Seeded
+    N(0, 1) inputs drawn on the device, rotating buffers of at least 768 MiB."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+    for dt in ("f32", "f16", "bf16"):
+        code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
+        for kib in SPLIT_CROSS_ROW_KIB:
+            cols = (kib << 10) // esz
+            variant, block = binding.softmax_select_variant(cols, code)
+            for rows in SPLIT_CROSS_ROWS:
+                nbytes = rows * cols * esz
+                if nbytes > SPLIT_CROSS_MAX_BYTES:
+                    continue
+                n = max(1, -(-(768 << 20) // (2 * nbytes)))
+                g = torch.Generator(device="cuda").manual_seed(rows * 131 + kib)
+                xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
+                ys = [torch.empty_like(x) for x in xs]
+                wsb = binding.split_workspace_bytes(rows, cols, code)
+                ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+                kid = binding.softmax_select(xs[0].data_ptr(), ys[0].data_ptr(), cols, cols, code, rows=rows)
+                runs = {
+                    "one_wg_per_row": lambda i: binding.softmax_fwd_variant(xs[i].data_ptr(), ys[i].data_ptr(), rows,
+                                                                            cols, cols, code, variant, block, stream),
+                    "split_workspace": lambda i: binding.softmax_fwd_split(xs[i].data_ptr(), ys[i].data_ptr(), rows,
+                                                                           cols, cols, code, ws.data_ptr(), wsb, 1,
+                                                                           stream),
+                    "softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols,
+                                                                 code, stream)}
+                us = {k: round(time_launches(f, n, steps, warmup, spin_s=0.02) * 1e3, 2) for k, f in runs.items()}
+                r = {"dtype": dt, "row_kib": kib, "rows": rows, "cols": cols,
+                     "softmax_fwd_path": "split via out" if kid == binding.SPLIT_KERNEL else "table", **us}
+                log(f"[bench] split crossover {dt} {kib} KiB x {rows}: {us}  ({r['softmax_fwd_path']})")
+                out.append(r)
+                del xs, ys, ws
+                torch.cuda.empty_cache()
+    return out
+
+
+def summarize_split_crossover(json_path: str) -> None:
+    """Write profiles/split_crossover.md from `bench.py --split-crossover --split-out` JSON."""
+    rows = json.load(open(json_path))
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    out = ["# Few, very wide rows: one workgroup per row against the split path, MI355X (gfx950)", "",
+           "Commands (repository root):", "",
+           f"    python3 bench.py --split-crossover --split-out {src}",
+           f"    python3 bench.py --summarize-split-crossover {src}", "",
+           "Microseconds per call over rotating buffers of at least 768 MiB, seeded N(0, 1) inputs.  `one wg/row`:",
+           "the width's one-workgroup-per-row kernel forced (softmax_fwd_variant at softmax_select_variant's pick);",
+           "`split+ws`: softmax_fwd_split with a caller workspace, always split (two kernels); `softmax_fwd`: the",
+           "library's own choice, which splits through its output (three kernels) where the path column says so.",
+           "`gain` = one wg/row / softmax_fwd.", "",
+           "| dtype | row KiB | rows | one wg/row us | split+ws us | softmax_fwd us | softmax_fwd path | gain |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['dtype']} | {r['row_kib']} | {r['rows']} | {r['one_wg_per_row']:.1f} | "
+                   f"{r['split_workspace']:.1f} | {r['softmax_fwd']:.1f} | {r['softmax_fwd_path']} | "
+                   f"{r['one_wg_per_row'] / r['softmax_fwd']:.2f} |")
+    path = os.path.join(PROFILE_DIR, "split_crossover.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def summarize_chunk_copy(json_path: str, bench_json: str | None = None) -> None:
     """Write profiles/chunk_copy_shapes.md from `bench.py --chunk-copy --chunk-out` JSON and,
     optionally, a default bench line whose c5 shapes give each row kernel's own rate."""
@@ -1130,8 +1215,9 @@ def wide_only(steps: int, warmup: int) -> dict:
 
 def summarize_wide_counters(fetch_csv, write_csv):
     """Write profiles/counters_wide_rows.txt: HBM bytes per dispatch of the
-    single-pass online kernel and of the two split-row kernels on the few-wide-
-    rows shapes, from two rocprofv3 --pmc runs of `bench.py --wide-only`."""
+    one-workgroup-per-row kernel and of the split-row kernels (with a workspace,
+    and with the pairs in the output) on the few-wide-rows shapes, from two
+    rocprofv3 --pmc runs of `bench.py --wide-only`."""
 
     def avg(f, counter):
         d = collections.defaultdict(list)
@@ -1148,7 +1234,7 @@ def summarize_wide_counters(fetch_csv, write_csv):
     rel = lambda f: os.path.relpath(os.path.abspath(f), ROOT)
     fdir, wdir = os.path.dirname(rel(fetch_csv)), os.path.dirname(rel(write_csv))
     lines = [
-        "# HBM traffic of the single-pass online kernel and of the split-row kernels on few, wide rows, MI355X (gfx950)",
+        "# HBM traffic of the one-workgroup-per-row kernel and of the split-row kernels on few, wide rows, MI355X (gfx950)",
         "# Two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), run from the repository root:",
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o w -- python3 bench.py --wide-only --steps 20 --warmup 5",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o w -- python3 bench.py --wide-only --steps 20 --warmup 5",
@@ -1158,13 +1244,13 @@ def summarize_wide_counters(fetch_csv, write_csv):
         "# least 1 GiB, so every launch's first read comes from HBM; 'x input' divides by the tensor's bytes.",
         f"source_digest: {source_digest()}", ""]
     for name in sorted(fe):
-        if not any(t in name for t in ("softmax_online", "softmax_split_stats", "softmax_split_norm")):
+        if not any(t in name for t in ("softmax_online", "softmax_row", "softmax_split_")):
             continue
         elem = "BF16" if "BF16" in name else "F32"
         key, wl = tensors[elem]
         size = wl.rows * wl.cols * (4 if elem == "F32" else 2)
         fb, wb = fe[name] * f_scale * 1024, wr.get(name, 0.0) * w_scale * 1024
-        lines.append(f"{name[:72]}  [{key} {wl.rows}x{wl.cols}]")
+        lines.append(f"{name[:96]}  [{key} {wl.rows}x{wl.cols}]")
         lines.append(f"  fetch_bytes: {fb:.0f}  ({fb / size:.3f} x input)")
         lines.append(f"  write_bytes: {wb:.0f}  ({wb / size:.3f} x input)")
     path = os.path.join(PROFILE_DIR, "counters_wide_rows.txt")
@@ -1205,6 +1291,11 @@ def main() -> int:
     ap.add_argument("--summarize-copy-sizes", nargs="+", metavar="JSON [TRACE_CSV]", default=None,
                     help="write profiles/copy_ceiling_sizes.md from a --copy-out file (or a bench JSON line) and,"
                          " optionally, the rocprofv3 kernel-trace CSV of the same run")
+    ap.add_argument("--split-crossover", action="store_true",
+                    help="time one workgroup per row, the split path and softmax_fwd on few, very wide rows")
+    ap.add_argument("--split-out", default=None, help="JSON file for --split-crossover")
+    ap.add_argument("--summarize-split-crossover", metavar="JSON", default=None,
+                    help="write profiles/split_crossover.md from --split-crossover JSON and exit")
     ap.add_argument("--chunk-copy", action="store_true",
                     help="time the chunked copies shaped like the row kernels (192 MiB) and exit")
     ap.add_argument("--chunk-out", default=None, help="with --chunk-copy: write the table as JSON here")
@@ -1224,6 +1315,9 @@ def main() -> int:
     args = ap.parse_args()
     if args.group_trace:
         group_trace(*args.group_trace)
+        return 0
+    if args.summarize_split_crossover:
+        summarize_split_crossover(args.summarize_split_crossover)
         return 0
     if args.summarize_chunk_copy:
         summarize_chunk_copy(*args.summarize_chunk_copy[:2])
@@ -1282,6 +1376,12 @@ def main() -> int:
             with open(args.copy_out, "w") as f:
                 json.dump(table, f, indent=1)
         print(json.dumps(table), flush=True)
+        return 0
+    if args.split_crossover:
+        table = split_crossover(args.steps, args.warmup)
+        if args.split_out:
+            with open(args.split_out, "w") as f:
+                json.dump(table, f, indent=1)
         return 0
     if args.chunk_copy:
         table = chunk_copy(args.steps, args.warmup)

@@ -23,9 +23,12 @@
  *
  * Ownership: the caller owns both device buffers (and any workspace).  The
  * library allocates no device memory, keeps no pointer after returning, never
- * synchronises the host and never pre-fills `out` (it writes every out[i, j < cols] exactly once;
- * "I Wrote My First GPU Kernel", section "The Honest Part", on the cost of
- * zero-filling an output the kernel overwrites anyway).
+ * synchronises the host and never pre-fills `out` ("I Wrote My First GPU
+ * Kernel", section "The Honest Part", on the cost of zero-filling an output
+ * the kernel overwrites anyway).  It writes every out[i, j < cols] once, with
+ * one exception: softmax_fwd's split of few, very wide rows (below) keeps
+ * partial results in the first 8 bytes of every 16 KiB tile of `out` between
+ * its kernels before writing the final values there.
  *
  * Aliasing: in == out (exactly in place) is allowed; any other overlap of the
  * two extents is rejected with SOFTMAX_ERR_OVERLAP.
@@ -86,6 +89,15 @@ extern "C" {
  * where the fused kernel loses) and to tune block shape per width rather than
  * by one formula ("GPU Kernels - Implementing and optimizing Softmax",
  * sections "CUDA scaling threads" and "Autotuning").
+ * Few, very wide rows, out of place on the 16-byte path, take the split path
+ * of softmax_fwd_split below without a workspace: each tile's (max, sum) pair
+ * is kept in the first 8 bytes of that tile's own output, and a third kernel
+ * merges each row's pairs between the other two.  One workgroup per row would
+ * keep only `rows` of the 256 compute units busy.  The measured lines: fp32
+ * rows of >= 2 MiB up to 192 rows, >= 1 MiB up to 128, >= 512 KiB up to 64,
+ * >= 256 KiB up to 16; fp16 / bf16 rows of >= 2 MiB up to 256 rows, >= 1 MiB
+ * up to 192, >= 256 KiB up to 128, >= 128 KiB up to 64.  Results are
+ * bit-identical to softmax_fwd_split's.
  */
 int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
                 int dtype, void *stream);
@@ -149,9 +161,11 @@ int softmax_fwd_causal_kernel(int kernel_id, const void *in, void *out, int64_t 
 
 /*
  * softmax_select -- the kernel id softmax_fwd would launch for these
- * arguments, written to *kernel_id.  Validates like softmax_fwd (rows only
- * matters for validation and launch shape); launches nothing.
+ * arguments, written to *kernel_id, or SOFTMAX_KERNEL_SPLIT when softmax_fwd
+ * takes the split path (few, very wide rows).  Validates like softmax_fwd;
+ * launches nothing.
  */
+#define SOFTMAX_KERNEL_SPLIT (-1)
 int softmax_select(const void *in, const void *out, int64_t rows, int64_t cols, int64_t row_stride,
                    int dtype, int *kernel_id);
 

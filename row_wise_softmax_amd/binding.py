@@ -150,9 +150,15 @@ def softmax_fwd_causal_kernel(kernel_id: int, in_ptr: int, out_ptr: int, rows: i
                                          dtype, stream), "softmax_fwd_causal_kernel")
 
 
+# softmax_select's answer when softmax_fwd splits few, very wide rows over
+# several workgroups (SOFTMAX_KERNEL_SPLIT): not an id of the kernel table.
+SPLIT_KERNEL = -1
+
+
 def softmax_select(in_ptr: int, out_ptr: int, cols: int, row_stride: int, dtype: int,
                    rows: int = 1, causal: bool = False) -> int:
-    """The kernel id the library's width dispatch picks for this call."""
+    """The kernel id the library's width dispatch picks for this call, or
+    SPLIT_KERNEL for softmax_fwd's split of few, very wide rows."""
     lib = _load()
     kid = ctypes.c_int(-1)
     fn = lib.softmax_select_causal if causal else lib.softmax_select

@@ -320,6 +320,11 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     return SOFTMAX_OK;
 }
 
+bool splits_through_out(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
+                        int dtype);
+int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, float* part,
+                 hipStream_t stream);
+
 int fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, bool causal,
         float scale, int64_t diag, void* stream, int64_t period = 0) {
     bool empty;
@@ -328,6 +333,8 @@ int fwd(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_strid
     float coef = float(kLog2eD);
     if (causal && !coef_of(scale, &coef)) return SOFTMAX_ERR_BAD_SCALE;
     if (empty) return SOFTMAX_OK;
+    if (!causal && splits_through_out(in, out, rows, cols, row_stride, dtype))
+        return launch_split(in, out, rows, cols, row_stride, dtype, nullptr, static_cast<hipStream_t>(stream));
     const Entry* e = select_entry(in, out, rows, cols, row_stride, dtype, causal);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
     return launch(*e, in, out, rows, cols, row_stride, coef, diag, static_cast<hipStream_t>(stream), period);
@@ -353,6 +360,10 @@ int select_id(const void* in, const void* out, int64_t rows, int64_t cols, int64
     bool empty;
     int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
     if (st != SOFTMAX_OK) return st;
+    if (!causal && !empty && splits_through_out(in, out, rows, cols, row_stride, dtype)) {
+        *kernel_id = SOFTMAX_KERNEL_SPLIT;
+        return SOFTMAX_OK;
+    }
     const Entry* e =
         select_entry(in, out, rows, cols > 0 ? cols : 1, row_stride > 0 ? row_stride : 1, dtype, causal);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;
@@ -370,6 +381,11 @@ constexpr int64_t kSplitMaxRows = 1024;  // below this many rows, split when ask
 struct SplitPair {
     const void* stats;
     const void* norm;
+    // 16-byte path only: the same two with each tile's pair in its own output
+    // slot, and the merge launched between them (softmax_fwd's own split)
+    const void* stats_slot;
+    const void* merge;
+    const void* norm_slot;
     int vec;
     int tile;  // accesses per tile
 };
@@ -378,10 +394,15 @@ template <class E>
 SplitPair split_kernels(bool vec) {
     constexpr int kN = 16 / E::kBytes;
     if (vec)
-        return {(const void*)&rws::softmax_split_stats<E, kN, kSplitW, kSplitVecV>,
-                (const void*)&rws::softmax_split_norm<E, kN, kSplitW, kSplitVecV>, kN, kSplitW * 64 * kSplitVecV};
-    return {(const void*)&rws::softmax_split_stats<E, 1, kSplitW, kSplitScalarV>,
-            (const void*)&rws::softmax_split_norm<E, 1, kSplitW, kSplitScalarV>, 1, kSplitW * 64 * kSplitScalarV};
+        return {(const void*)&rws::softmax_split_stats<E, kN, kSplitW, kSplitVecV, false>,
+                (const void*)&rws::softmax_split_norm<E, kN, kSplitW, kSplitVecV, false>,
+                (const void*)&rws::softmax_split_stats<E, kN, kSplitW, kSplitVecV, true>,
+                (const void*)&rws::softmax_split_merge<E, kN, kSplitW, kSplitVecV>,
+                (const void*)&rws::softmax_split_norm<E, kN, kSplitW, kSplitVecV, true>, kN,
+                kSplitW * 64 * kSplitVecV};
+    return {(const void*)&rws::softmax_split_stats<E, 1, kSplitW, kSplitScalarV, false>,
+            (const void*)&rws::softmax_split_norm<E, 1, kSplitW, kSplitScalarV, false>, nullptr, nullptr, nullptr, 1,
+            kSplitW * 64 * kSplitScalarV};
 }
 
 SplitPair split_for(int dtype, bool vec) {
@@ -407,6 +428,9 @@ int64_t split_workspace(int64_t rows, int64_t cols, int dtype) {
     return ((rows * tiles * 8 + 255) / 256) * 256;
 }
 
+// The split path's kernels in order.  With a workspace (`part`): stats, norm.
+// Without one (part == nullptr, the 16-byte path, out != in): stats and norm
+// keeping the pairs in the output's tile slots, with the per-row merge between.
 int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, float* part,
                  hipStream_t stream) {
     const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
@@ -421,14 +445,52 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
     a.work = rows * a.tiles;
     a.coef = float(kLog2eD);
     const int64_t grid = a.work < kMaxGrid ? a.work : kMaxGrid;
+    const int64_t row_grid = rows < kMaxGrid ? rows : kMaxGrid;
+    struct Step {
+        const void* fn;
+        int64_t grid;
+    };
+    const Step with_part[] = {{k.stats, grid}, {k.norm, grid}};
+    const Step in_slots[] = {{k.stats_slot, grid}, {k.merge, row_grid}, {k.norm_slot, grid}};
+    const Step* steps = part != nullptr ? with_part : in_slots;
+    const int nsteps = part != nullptr ? 2 : 3;
+    if (part == nullptr && (k.stats_slot == nullptr || in == out)) return SOFTMAX_ERR_BAD_KERNEL;
     void* args[] = {&a};
-    for (const void* fn : {k.stats, k.norm}) {
-        if (hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(kSplitW * 64), args, 0, stream) != hipSuccess) {
+    for (int i = 0; i < nsteps; ++i) {
+        if (hipLaunchKernel(steps[i].fn, dim3(unsigned(steps[i].grid)), dim3(kSplitW * 64), args, 0, stream) !=
+            hipSuccess) {
             (void)hipGetLastError();
             return SOFTMAX_ERR_HIP;
         }
     }
     return SOFTMAX_OK;
+}
+
+// softmax_fwd's own split, through the output's tile slots: out of place, on
+// the 16-byte path, when a row has at least `min_row_bytes` and there are at
+// most `max_rows` rows (first matching line, widest first).  One workgroup per
+// row keeps at most `rows` compute units busy, and on such rows each runs at a
+// rate set by its element count; the split reads every element twice and adds
+// a launch of 2-4 us.  Measured for fp32, fp16 and bf16 at 8 .. 256 rows of
+// 64 KiB .. 4 MiB against one workgroup per row; each line is where the split
+// gained at least 5% (e.g. fp32 4 MiB rows: 9.7x at 8 rows, 1.5x at 128; bf16
+// 512 KiB rows: 3.3x at 8, 1.2x at 128).
+struct SlotSplitRule {
+    int64_t min_row_bytes;
+    int64_t max_rows;
+};
+constexpr SlotSplitRule kSlotSplitF32[] = {
+    {int64_t(2) << 20, 192}, {int64_t(1) << 20, 128}, {int64_t(512) << 10, 64}, {int64_t(256) << 10, 16}};
+constexpr SlotSplitRule kSlotSplit16[] = {
+    {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(256) << 10, 128}, {int64_t(128) << 10, 64}};
+
+bool splits_through_out(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
+                        int dtype) {
+    if (in == out || !aligned16(in, out, cols, row_stride, dtype)) return false;
+    const int64_t row_bytes = cols * elem_bytes(dtype);
+    for (const SlotSplitRule& r : dtype == SOFTMAX_F32 ? kSlotSplitF32 : kSlotSplit16)
+        if (row_bytes >= r.min_row_bytes) return rows <= r.max_rows;
+    return false;
 }
 
 // ---- the split path without a caller workspace

@@ -669,10 +669,18 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
 // Traffic: two reads and one write per element; kernel 1 reads with the
 // default cache policy so that kernel 2's re-read can hit L2 or the Infinity
 // Cache.  No workgroup waits for another, so the grid may be any size.
+//
+// With Slot = true there is no workspace: each tile's pair goes to the first
+// 8 bytes of the tile's own output (every tile holds at least one 16-byte
+// access).  A kernel launched between the two, softmax_split_merge, merges
+// each row's pairs in the same fixed order and writes the row's merged pair
+// back to every slot of the row.  Kernel 2 then reads only its own tile's
+// slot, before any thread of its workgroup overwrites it, and reaches the
+// bits of the workspace path.  This needs an output distinct from the input.
 struct SplitArgs {
     const void* in;
     void* out;
-    float* part;     // 2 floats (max, sum) per (row, tile), row-major
+    float* part;     // 2 floats (max, sum) per (row, tile), row-major; unused with Slot
     int64_t rows;
     int64_t stride;  // row stride in accesses
     int64_t work;    // rows * tiles
@@ -681,7 +689,20 @@ struct SplitArgs {
     float coef;      // log2(e)
 };
 
-template <class E, int N, int W, int V>
+// Where tile `tile` of row `row` keeps its (max, sum) pair: the workspace, or
+// (Slot) the first 8 bytes of the tile's own output.
+template <class E, int N, int W, int V, bool Slot>
+__device__ inline f32x2* pair_at(const SplitArgs& a, int64_t row, int tile) {
+    if constexpr (Slot) {
+        typedef typename Access<E, N>::raw raw;
+        raw* out = static_cast<raw*>(a.out);
+        return reinterpret_cast<f32x2*>(out + row * a.stride + int64_t(tile) * (W * kWave * V));
+    } else {
+        return reinterpret_cast<f32x2*>(a.part + 2 * (row * a.tiles + tile));
+    }
+}
+
+template <class E, int N, int W, int V, bool Slot>
 __global__ void __launch_bounds__(W * kWave) softmax_split_stats(SplitArgs a) {
     typedef typename Access<E, N>::raw raw;
     constexpr int kThreads = W * kWave;
@@ -726,13 +747,48 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_stats(SplitArgs a) {
 #pragma unroll
             for (int w = 1; w < W; ++w) s += red_s[w];
             f32x2 pr = {m, s};
-            *reinterpret_cast<f32x2*>(a.part + 2 * b) = pr;
+            *pair_at<E, N, W, V, Slot>(a, row, int(b - row * a.tiles)) = pr;
         }
         __syncthreads();  // red_m / red_s are rewritten for the next tile
     }
 }
 
+// Slot only: merge each row's tile pairs (thread t takes tiles t, t + 64W, ...
+// in order, then the wave and workgroup reductions in a fixed order -- the
+// order softmax_split_norm merges in on the workspace path) and write the
+// merged pair to every slot of the row.  Each slot is read and later written
+// by the same thread.
 template <class E, int N, int W, int V>
+__global__ void __launch_bounds__(W * kWave) softmax_split_merge(SplitArgs a) {
+    constexpr int kThreads = W * kWave;
+    __shared__ float red_m[W];
+    __shared__ float red_s[W];
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        float m = -INFINITY, s = 0.0f;
+        for (int j = t; j < a.tiles; j += kThreads) {
+            const f32x2 pr = *pair_at<E, N, W, V, true>(a, row, j);
+            merge_pair(m, s, pr.x, pr.y, a.coef);
+        }
+        wave_reduce_pair(m, s, a.coef);
+        if (lane == 0) {
+            red_m[wave] = m;
+            red_s[wave] = s;
+        }
+        __syncthreads();
+        m = red_m[0];
+        s = red_s[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+        const f32x2 merged = {m, s};
+        for (int j = t; j < a.tiles; j += kThreads) *pair_at<E, N, W, V, true>(a, row, j) = merged;
+        __syncthreads();  // red_m / red_s are rewritten for the next row
+    }
+}
+
+template <class E, int N, int W, int V, bool Slot>
 __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
     typedef typename Access<E, N>::raw raw;
     constexpr int kThreads = W * kWave;
@@ -751,24 +807,33 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
         float x[V][N];
 #pragma unroll
         for (int v = 0; v < V; ++v) load_access<E, N, false>(p + v * kThreads, base + v * kThreads + t, a.nacc, 0, x[v]);
-        // Merge the row's tile pairs: thread t takes tiles t, t + 64W, ... in
-        // order, then the wave and workgroup reductions run in a fixed order.
-        float m = -INFINITY, s = 0.0f;
-        const float* part = a.part + 2 * row * a.tiles;
-        for (int j = t; j < a.tiles; j += kThreads) {
-            const f32x2 pr = *reinterpret_cast<const f32x2*>(part + 2 * j);
-            merge_pair(m, s, pr.x, pr.y, a.coef);
-        }
-        wave_reduce_pair(m, s, a.coef);
-        if (lane == 0) {
-            red_m[wave] = m;
-            red_s[wave] = s;
-        }
-        __syncthreads();
-        m = red_m[0];
-        s = red_s[0];
+        float m, s;
+        if constexpr (Slot) {
+            // the row's merged pair, already in this tile's slot
+            const f32x2 pr = *pair_at<E, N, W, V, true>(a, row, int(b - row * a.tiles));
+            m = pr.x;
+            s = pr.y;
+            __syncthreads();  // every thread has read the slot before the tile's first access is rewritten
+        } else {
+            // Merge the row's tile pairs: thread t takes tiles t, t + 64W, ... in
+            // order, then the wave and workgroup reductions run in a fixed order.
+            m = -INFINITY;
+            s = 0.0f;
+            for (int j = t; j < a.tiles; j += kThreads) {
+                const f32x2 pr = *pair_at<E, N, W, V, false>(a, row, j);
+                merge_pair(m, s, pr.x, pr.y, a.coef);
+            }
+            wave_reduce_pair(m, s, a.coef);
+            if (lane == 0) {
+                red_m[wave] = m;
+                red_s[wave] = s;
+            }
+            __syncthreads();
+            m = red_m[0];
+            s = red_s[0];
 #pragma unroll
-        for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+            for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+        }
         const float mu = m == -INFINITY ? 0.0f : m;  // all -inf row: every term exp(-inf) = 0
         const float r = recip_sum(s);
         raw* q = out + row * a.stride + base + t;

@@ -144,10 +144,13 @@ def test_kernel_table_is_consistent(lib):
 @pytest.mark.parametrize("causal", [False, True])
 def test_dispatch_always_picks_a_fitting_kernel(lib, dtype, cols, causal):
     kid = binding.softmax_select(A, B, cols, cols, dtype, rows=4, causal=causal)
+    esz = 4 if dtype == 0 else 2
+    if kid == binding.SPLIT_KERNEL:  # few, very wide rows out of place: softmax_fwd's own split
+        assert not causal and cols * esz >= 128 << 10
+        kid = binding.softmax_select(A, A, cols, cols, dtype, rows=4)  # in place takes the table
     assert binding.kernel_fits(kid, A, B, cols, cols, dtype)
     info = binding.kernel_table()[kid]
     assert info.causal == causal
-    esz = 4 if dtype == 0 else 2
     if (cols * esz) % 16 == 0:
         assert info.vec_elems * esz == 16, "aligned rows must take 16-byte accesses"
     # misaligned pointers fall back to the scalar path
@@ -277,6 +280,36 @@ def test_few_rows_take_the_persistent_twin(lib):
     assert pick(8192, 2, 2048) == "rowpf_bf16_w8_v2" and pick(8192, 2, 2049) == "row_bf16_w8_v2"
     assert pick(2048, 0, 2048, causal=True) == "causal_rowpf_f32_w4_v2"
     assert pick(16384, 0, 16) == "row_f32_w4_v16"  # rows past the register-resident two-access shapes keep theirs
+
+
+def test_few_very_wide_rows_split_through_the_output(lib):
+    """softmax_fwd splits few, very wide rows out of place on the 16-byte path,
+    by the measured (row bytes, most rows) lines; anything else takes the
+    kernel table."""
+    a, b = 1 << 40, 1 << 41
+    S = binding.SPLIT_KERNEL
+
+    def sel(cols, code, rows, x=a, y=b, stride=None, causal=False):
+        return binding.softmax_select(x, y, cols, stride or cols, code, rows=rows, causal=causal)
+
+    # fp32: >= 2 MiB rows up to 192 rows, >= 1 MiB up to 128, >= 512 KiB up to 64, >= 256 KiB up to 16
+    assert sel(1 << 20, 0, 192) == S and sel(1 << 20, 0, 193) != S
+    assert sel(1 << 18, 0, 128) == S and sel(1 << 18, 0, 129) != S
+    assert sel(1 << 17, 0, 1) == S and sel(1 << 17, 0, 64) == S and sel(1 << 17, 0, 65) != S
+    assert sel(1 << 16, 0, 16) == S and sel(1 << 16, 0, 17) != S
+    assert sel((1 << 16) - 4, 0, 8) != S
+    # fp16 / bf16: >= 2 MiB up to 256, >= 1 MiB up to 192, >= 256 KiB up to 128, >= 128 KiB up to 64
+    for code in (1, 2):
+        assert sel(1 << 20, code, 256) == S and sel(1 << 20, code, 257) != S
+        assert sel(1 << 19, code, 192) == S and sel(1 << 19, code, 193) != S
+        assert sel(1 << 17, code, 128) == S and sel(1 << 17, code, 129) != S
+        assert sel(1 << 16, code, 64) == S and sel(1 << 16, code, 65) != S
+        assert sel((1 << 16) - 8, code, 8) != S
+    assert sel((1 << 17) + 4, 0, 3, stride=(1 << 17) + 8) == S          # ragged last tile, padded stride
+    assert sel(1 << 17, 0, 8, y=a) != S                                 # in place
+    assert sel(1 << 17, 0, 8, x=a + 4, y=b + 4) != S                    # not on the 16-byte path
+    assert sel(1 << 17, 0, 8, stride=(1 << 17) + 1) != S                # row pitch not a 16-byte multiple
+    assert sel(1 << 17, 0, 8, causal=True) != S                         # the causal form never splits
 
 
 def test_fp32_ragged_rule_follows_the_row_count(lib):

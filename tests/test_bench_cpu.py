@@ -247,3 +247,19 @@ def test_trace_reduction_and_per_grid_softmax_rows(profile_dir, tmp_path):
     text = (profile_dir / "kernel_trace_bench.md").read_text()
     assert "| `softmax_row<F16, 8, 4, 2, false, false>` | 8192 | 256 | c3 | 2 | 22500 | 22000 |" in text
     assert "| f16 | 1024 | 1024 | 1 | 48000 | 48000 |" in text
+
+
+def test_split_crossover_summary(profile_dir, tmp_path):
+    """The gain column is the one-workgroup-per-row time over softmax_fwd's, and
+    each line names the path softmax_fwd took."""
+    rows = [{"dtype": "f32", "row_kib": 4096, "rows": 8, "cols": 1 << 20, "softmax_fwd_path": "split via out",
+             "one_wg_per_row": 180.0, "split_workspace": 15.0, "softmax_fwd": 18.0},
+            {"dtype": "bf16", "row_kib": 64, "rows": 256, "cols": 32768, "softmax_fwd_path": "table",
+             "one_wg_per_row": 12.0, "split_workspace": 15.0, "softmax_fwd": 12.0}]
+    src = tmp_path / "cross.json"
+    src.write_text(json.dumps(rows))
+    bench.summarize_split_crossover(str(src))
+    text = (profile_dir / "split_crossover.md").read_text()
+    assert "| f32 | 4096 | 8 | 180.0 | 15.0 | 18.0 | split via out | 10.00 |" in text
+    assert "| bf16 | 64 | 256 | 12.0 | 15.0 | 12.0 | table | 1.00 |" in text
+    assert "--split-crossover --split-out" in text

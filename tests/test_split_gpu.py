@@ -127,3 +127,74 @@ def test_split_random_calls(case):
     check(y, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"split random #{case}")
     if not inplace:
         check_padding_untouched(y, cols, dtype, label=f"split random #{case}")
+
+
+# --------------------- softmax_fwd's own split: the tile pairs kept in the output
+
+def _bits(y, dtype):
+    return y.view(np.uint32) if dtype == "f32" else y
+
+
+def _run_fwd(x, dtype, cols, inplace=False):
+    """softmax_fwd on host array x (rows x row_stride), output prefilled with a
+    sentinel; returns (raw output, what softmax_select reported for the call)."""
+    import torch
+    rows, stride = x.shape
+    code = W.dtype_code(dtype)
+    xd = to_device(x, dtype)
+    out = xd if inplace else to_device(np.full_like(x, sentinel(dtype)), dtype)
+    kid = binding.softmax_select(xd.data_ptr(), out.data_ptr(), cols, stride, code, rows=rows)
+    binding.softmax_fwd(xd.data_ptr(), out.data_ptr(), rows, cols, stride, code,
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return to_host(out, dtype), kid
+
+
+@pytest.mark.parametrize("dtype,rows,cols,stride", [
+    ("f32", 1, 1 << 17, None), ("f32", 5, (1 << 17) + 4, (1 << 17) + 8), ("f32", 64, 1 << 17, None),
+    ("f32", 16, 1 << 16, None), ("f32", 3, 1 << 20, None), ("f16", 2, 1 << 18, None),
+    ("bf16", 9, (1 << 18) + 8, (1 << 18) + 16), ("bf16", 128, 1 << 17, None), ("bf16", 32, 1 << 16, None)])
+def test_fwd_splits_few_very_wide_rows(dtype, rows, cols, stride):
+    """softmax_fwd on few, very wide rows out of place: the split path with each
+    tile's (max, sum) in its own output slot.  Every row against the oracle, the
+    same bits as softmax_fwd_split's workspace path, padding untouched."""
+    from gpu_util import check_every_row
+    stride = stride or cols
+    print(f"[gpu-case] fwd split {dtype} rows={rows} cols={cols} stride={stride}", file=sys.stderr, flush=True)
+    x = W.random_matrix(seed=76, rows=rows, cols=cols, dtype=dtype, sigma=3.0, row_stride=stride)
+    y, kid = _run_fwd(x, dtype, cols)
+    assert kid == binding.SPLIT_KERNEL
+    check_padding_untouched(y, cols, dtype, label="fwd split")
+    yc = np.ascontiguousarray(y[:, :cols])
+    check_every_row(yc, np.ascontiguousarray(x[:, :cols]), dtype, label=f"fwd split {dtype} {rows}x{cols}")
+    ys = _run_split(x, dtype, cols=cols, force=1)
+    assert np.array_equal(_bits(yc, dtype), _bits(np.ascontiguousarray(ys[:, :cols]), dtype))
+
+
+def test_fwd_split_masked_and_extreme_rows():
+    """Whole -inf rows, rows whose first three quarters (whole tiles) are -inf,
+    and huge entries, through softmax_fwd's own split."""
+    rows, cols = 6, 1 << 17
+    x64 = np.random.default_rng(77).standard_normal((rows, cols)) * 2
+    x64[0, :] = -np.inf
+    x64[1, : 3 * cols // 4] = -np.inf
+    x64[2, 100000] = 3.0e38
+    x64[3, :] = -3.0e38
+    x64[4, 7] = 1e9
+    x64[5, -1] = 50.0
+    x = W.cast(x64, "f32")
+    y, kid = _run_fwd(x, "f32", cols)
+    assert kid == binding.SPLIT_KERNEL
+    check(y, x, "f32", O.softmax(x, "f32"), label="fwd split extremes")
+    assert np.all(decode(y, "f32")[0] == 0.0)
+
+
+@pytest.mark.parametrize("rows", [4, 129])
+def test_fwd_few_very_wide_rows_in_place_or_past_the_rule(rows):
+    # 512 KiB bf16 rows: split up to 128 rows out of place
+    """In place, or with more rows than the rule takes, the same widths run the
+    kernel table's one-workgroup-per-row kernels."""
+    x = W.random_matrix(seed=78, rows=rows, cols=1 << 18, dtype="bf16")
+    y, kid = _run_fwd(x, "bf16", 1 << 18, inplace=(rows == 4))
+    assert kid != binding.SPLIT_KERNEL
+    check(y, x, "bf16", O.softmax(x, "bf16"), label=f"fwd wide rows={rows}")
