@@ -2,7 +2,9 @@
 
 They allocate nothing, never synchronise and issue no memset, so a caller may
 record them in a graph.  One graph here holds a plain softmax, a scaled causal
-softmax, a split-row softmax (caller workspace) and an attention forward.  It
+softmax, the same over a batch of score matrices, a split-row softmax (caller
+workspace), softmax_fwd's own split of few, very wide rows (three kernels, the
+partials kept in the output) and an attention forward.  It
 is replayed three times on fresh inputs written between replays by ordinary
 eager work, and after every replay each output must equal, bit for bit, the
 same call made eagerly on the same inputs (every kernel here is
@@ -31,12 +33,16 @@ def _gpu():
 
 
 def _calls(bufs, stream):
-    """The four library calls, from the buffers in `bufs`, on `stream`."""
+    """The library calls, from the buffers in `bufs`, on `stream`."""
     r, c = bufs["shape"]
     f16 = W.dtype_code("f16")
     binding.softmax_fwd(bufs["x"].data_ptr(), bufs["y"].data_ptr(), r, c, c, f16, stream)
     binding.softmax_fwd_causal(bufs["s"].data_ptr(), bufs["ys"].data_ptr(), 256, 256, 256, 0.125, 0,
                                W.dtype_code("f32"), stream)
+    binding.softmax_fwd_causal_batched(bufs["sb"].data_ptr(), bufs["ysb"].data_ptr(), 6 * 64, 64, 64, 64, 0.5, 2,
+                                       W.dtype_code("f32"), stream)
+    vr, vc = bufs["vshape"]
+    binding.softmax_fwd(bufs["wide"].data_ptr(), bufs["ywide"].data_ptr(), vr, vc, vc, W.dtype_code("bf16"), stream)
     wr, wc = bufs["wshape"]
     binding.softmax_fwd_split(bufs["w"].data_ptr(), bufs["yw"].data_ptr(), wr, wc, wc, W.dtype_code("f32"),
                               bufs["ws"].data_ptr(), bufs["ws"].numel(), 1, stream)
@@ -50,6 +56,8 @@ def _inputs(seed):
     return {
         "x": W.cast(3.0 * rng.standard_normal((300, 4096)), "f16"),
         "s": W.cast(rng.standard_normal((256, 256)), "f32"),
+        "sb": W.cast(rng.standard_normal((6 * 64, 64)), "f32"),
+        "wide": W.cast(2.0 * rng.standard_normal((8, 1 << 18)), "bf16"),
         "w": W.cast(2.0 * rng.standard_normal((3, 70000)), "f32"),
         "q": W.cast(rng.standard_normal((1, 4, 200, 128)), "f16"),
         "k": W.cast(rng.standard_normal((1, 4, 200, 128)), "f16"),
@@ -70,14 +78,19 @@ def test_captured_graph_replays_match_eager_calls():
     host = _inputs(101)
     dev = {key: torch.empty(arr.shape, dtype=torch.float16 if arr.dtype == np.uint16 else torch.float32,
                             device="cuda") for key, arr in host.items()}
-    bufs = dict(dev, shape=(300, 4096), wshape=(3, 70000), ashape=(1, 4, 200, 128))
+    dev["wide"] = torch.empty(host["wide"].shape, dtype=torch.bfloat16, device="cuda")
+    bufs = dict(dev, shape=(300, 4096), wshape=(3, 70000), vshape=(8, 1 << 18), ashape=(1, 4, 200, 128))
     bufs["y"] = torch.empty_like(dev["x"])
     bufs["ys"] = torch.empty_like(dev["s"])
+    bufs["ysb"] = torch.empty_like(dev["sb"])
+    bufs["ywide"] = torch.empty_like(dev["wide"])
+    assert binding.softmax_select(dev["wide"].data_ptr(), bufs["ywide"].data_ptr(), 1 << 18, 1 << 18,
+                                  W.dtype_code("bf16"), rows=8) == binding.SPLIT_KERNEL
     bufs["yw"] = torch.empty_like(dev["w"])
     bufs["o"] = torch.empty_like(dev["q"])
     nbytes = binding.split_workspace_bytes(3, 70000, W.dtype_code("f32"))
     bufs["ws"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
-    outs = ("y", "ys", "yw", "o")
+    outs = ("y", "ys", "ysb", "ywide", "yw", "o")
 
     _upload(dev, host)
     side = torch.cuda.Stream()
@@ -87,7 +100,8 @@ def test_captured_graph_replays_match_eager_calls():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
-    print("[gpu-case] graph capture of softmax, causal, split and attention", file=sys.stderr, flush=True)
+    print("[gpu-case] graph capture of softmax, causal, batched causal, split and attention", file=sys.stderr,
+          flush=True)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         _calls(bufs, torch.cuda.current_stream().cuda_stream)
@@ -120,6 +134,13 @@ def test_captured_graph_replays_match_eager_calls():
             ys = to_host(got["ys"], "f32")
             keep = np.arange(256)[None, :] <= np.arange(256)[:, None]
             check(ys, host["s"], "f32", O.softmax_causal(host["s"], "f32", 0.125, 0), label="graph causal", keep=keep)
+            ysb = to_host(got["ysb"], "f32")
+            ref = np.concatenate([O.softmax_causal(np.ascontiguousarray(host["sb"][k * 64:(k + 1) * 64]), "f32", 0.5, 2)
+                                  for k in range(6)])
+            keep = np.tile(np.arange(64)[None, :] <= np.arange(64)[:, None] + 2, (6, 1))
+            check(ysb, host["sb"], "f32", ref, label="graph batched causal", keep=keep)
+            ywide = to_host(got["ywide"], "bf16")
+            check(ywide, host["wide"], "bf16", O.softmax(host["wide"], "bf16"), label="graph fwd split")
             yw = to_host(got["yw"], "f32")
             check(yw, host["w"], "f32", O.softmax(host["w"], "f32"), label="graph split")
             o = decode(to_host(got["o"], "f16"), "f16")
