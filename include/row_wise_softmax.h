@@ -279,7 +279,9 @@ int softmax_bench_chunk_copy(const void *src, void *dst, int64_t bytes, int wave
  * rule ("Dissecting Memory Bandwidth & SRAM Tiling in Triton", section "The
  * Mathematical Remedy: Online Softmax Tiling") -- the same fixed merge order
  * in every workgroup of the row -- and re-reads its tile to write it
- * normalised.  This is the two-pass answer to a reduction that spans
+ * normalised.  Rows of more than 4096 tiles (64 MiB on the 16-byte path) get
+ * the merge, in the same order, from a kernel of its own launched between
+ * the two, so that it is done once per row.  This is the two-pass answer to a reduction that spans
  * workgroups ("Kernel Fusion", section "What fusion cannot fix").  Traffic is
  * two reads and one write per element; the re-read may hit L2 or the
  * Infinity Cache.  Results are those of softmax_fwd up to rounding.

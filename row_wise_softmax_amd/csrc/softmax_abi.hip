@@ -378,31 +378,48 @@ constexpr int kSplitVecV = 4;     // 16-byte accesses per thread per tile
 constexpr int kSplitScalarV = 8;  // elements per thread per tile (any alignment)
 constexpr int64_t kSplitMaxRows = 1024;  // below this many rows, split when asked to choose
 
+// Above this many tiles per row the workspace path merges each row's pairs
+// once in a kernel of its own instead of in every workgroup of the norm
+// kernel (tiles^2 pair reads per row).  Measured on one fp32 row: 2^24
+// columns (4096 tiles) take 33 us with the merge in the norm kernel; with the
+// merge kernel, 2^26 columns (16384 tiles) take 128 us instead of 242 and
+// 2^28 columns (65536 tiles) 530 us instead of 2350.
+constexpr int64_t kSplitMergeKernelTiles = 4096;
+
 struct SplitPair {
     const void* stats;
-    const void* norm;
-    // 16-byte path only: the same two with each tile's pair in its own output
-    // slot, and the merge launched between them (softmax_fwd's own split)
+    const void* norm;         // merges the row's pairs itself
+    const void* merge;        // workspace pairs merged once per row ...
+    const void* norm_merged;  // ... and read back by the norm kernel
+    // 16-byte path only: stats, merge and norm with each tile's pair in its
+    // own output slot (softmax_fwd's own split)
     const void* stats_slot;
-    const void* merge;
+    const void* merge_slot;
     const void* norm_slot;
     int vec;
     int tile;  // accesses per tile
 };
 
+template <class E, int N, int V>
+SplitPair split_kernels_of() {
+    constexpr int W = kSplitW;
+    SplitPair k = {(const void*)&rws::softmax_split_stats<E, N, W, V, false>,
+                   (const void*)&rws::softmax_split_norm<E, N, W, V, false, false>,
+                   (const void*)&rws::softmax_split_merge<E, N, W, V, false>,
+                   (const void*)&rws::softmax_split_norm<E, N, W, V, false, true>,
+                   nullptr, nullptr, nullptr, N, W * 64 * V};
+    if constexpr (N > 1) {
+        k.stats_slot = (const void*)&rws::softmax_split_stats<E, N, W, V, true>;
+        k.merge_slot = (const void*)&rws::softmax_split_merge<E, N, W, V, true>;
+        k.norm_slot = (const void*)&rws::softmax_split_norm<E, N, W, V, true, true>;
+    }
+    return k;
+}
+
 template <class E>
 SplitPair split_kernels(bool vec) {
     constexpr int kN = 16 / E::kBytes;
-    if (vec)
-        return {(const void*)&rws::softmax_split_stats<E, kN, kSplitW, kSplitVecV, false>,
-                (const void*)&rws::softmax_split_norm<E, kN, kSplitW, kSplitVecV, false>,
-                (const void*)&rws::softmax_split_stats<E, kN, kSplitW, kSplitVecV, true>,
-                (const void*)&rws::softmax_split_merge<E, kN, kSplitW, kSplitVecV>,
-                (const void*)&rws::softmax_split_norm<E, kN, kSplitW, kSplitVecV, true>, kN,
-                kSplitW * 64 * kSplitVecV};
-    return {(const void*)&rws::softmax_split_stats<E, 1, kSplitW, kSplitScalarV, false>,
-            (const void*)&rws::softmax_split_norm<E, 1, kSplitW, kSplitScalarV, false>, nullptr, nullptr, nullptr, 1,
-            kSplitW * 64 * kSplitScalarV};
+    return vec ? split_kernels_of<E, kN, kSplitVecV>() : split_kernels_of<E, 1, kSplitScalarV>();
 }
 
 SplitPair split_for(int dtype, bool vec) {
@@ -428,9 +445,10 @@ int64_t split_workspace(int64_t rows, int64_t cols, int dtype) {
     return ((rows * tiles * 8 + 255) / 256) * 256;
 }
 
-// The split path's kernels in order.  With a workspace (`part`): stats, norm.
-// Without one (part == nullptr, the 16-byte path, out != in): stats and norm
-// keeping the pairs in the output's tile slots, with the per-row merge between.
+// The split path's kernels in order.  With a workspace (`part`): stats, norm,
+// with the per-row merge between them for rows of many tiles.  Without one
+// (part == nullptr, the 16-byte path, out != in): stats, merge and norm
+// keeping the pairs in the output's tile slots.
 int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, float* part,
                  hipStream_t stream) {
     const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
@@ -451,9 +469,11 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
         int64_t grid;
     };
     const Step with_part[] = {{k.stats, grid}, {k.norm, grid}};
-    const Step in_slots[] = {{k.stats_slot, grid}, {k.merge, row_grid}, {k.norm_slot, grid}};
-    const Step* steps = part != nullptr ? with_part : in_slots;
-    const int nsteps = part != nullptr ? 2 : 3;
+    const Step with_part_merged[] = {{k.stats, grid}, {k.merge, row_grid}, {k.norm_merged, grid}};
+    const Step in_slots[] = {{k.stats_slot, grid}, {k.merge_slot, row_grid}, {k.norm_slot, grid}};
+    const bool merge_kernel = a.tiles > kSplitMergeKernelTiles;
+    const Step* steps = part == nullptr ? in_slots : merge_kernel ? with_part_merged : with_part;
+    const int nsteps = part != nullptr && !merge_kernel ? 2 : 3;
     if (part == nullptr && (k.stats_slot == nullptr || in == out)) return SOFTMAX_ERR_BAD_KERNEL;
     void* args[] = {&a};
     for (int i = 0; i < nsteps; ++i) {

@@ -670,13 +670,17 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
 // default cache policy so that kernel 2's re-read can hit L2 or the Infinity
 // Cache.  No workgroup waits for another, so the grid may be any size.
 //
+// Rows of many tiles would have every workgroup of kernel 2 read all of the
+// row's pairs (tiles^2 reads per row), so for them a kernel launched between
+// the two, softmax_split_merge, merges each row's pairs once, in the same
+// fixed order, and writes the merged pair back to every tile's entry; kernel 2
+// (Merged = true) then reads only its own tile's entry.  The bits are the same.
+//
 // With Slot = true there is no workspace: each tile's pair goes to the first
 // 8 bytes of the tile's own output (every tile holds at least one 16-byte
-// access).  A kernel launched between the two, softmax_split_merge, merges
-// each row's pairs in the same fixed order and writes the row's merged pair
-// back to every slot of the row.  Kernel 2 then reads only its own tile's
-// slot, before any thread of its workgroup overwrites it, and reaches the
-// bits of the workspace path.  This needs an output distinct from the input.
+// access), the merge kernel always runs, and kernel 2 reads its own tile's
+// slot before any thread of its workgroup overwrites it.  This needs an
+// output distinct from the input.
 struct SplitArgs {
     const void* in;
     void* out;
@@ -753,43 +757,66 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_stats(SplitArgs a) {
     }
 }
 
-// Slot only: merge each row's tile pairs (thread t takes tiles t, t + 64W, ...
-// in order, then the wave and workgroup reductions in a fixed order -- the
-// order softmax_split_norm merges in on the workspace path) and write the
-// merged pair to every slot of the row.  Each slot is read and later written
+// Merge row `row`'s tile pairs in one fixed order: thread t takes tiles t,
+// t + 64W, ... in order (loading eight at a time, so that a row of many tiles
+// costs few round trips), then the wave and the workgroup reductions.  Every
+// caller merges in this order, so all of them reach the same bits.  Every
+// thread ends with the row's pair; red_m / red_s stay in use until the
+// caller's next barrier.
+template <class E, int N, int W, int V, bool Slot>
+__device__ inline void merge_row(const SplitArgs& a, int64_t row, float* red_m, float* red_s, float& m, float& s) {
+    constexpr int kThreads = W * kWave;
+    constexpr int kBatch = 8;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    m = -INFINITY;
+    s = 0.0f;
+    int j = t;
+    for (; j + (kBatch - 1) * kThreads < a.tiles; j += kBatch * kThreads) {
+        f32x2 pr[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) pr[u] = *pair_at<E, N, W, V, Slot>(a, row, j + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) merge_pair(m, s, pr[u].x, pr[u].y, a.coef);
+    }
+    for (; j < a.tiles; j += kThreads) {
+        const f32x2 pr = *pair_at<E, N, W, V, Slot>(a, row, j);
+        merge_pair(m, s, pr.x, pr.y, a.coef);
+    }
+    wave_reduce_pair(m, s, a.coef);
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_s[wave] = s;
+    }
+    __syncthreads();
+    m = red_m[0];
+    s = red_s[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+}
+
+// Merge each row's tile pairs once (merge_row) and write the merged pair back
+// to every tile's entry of the row.  Each entry is read, and later written,
 // by the same thread.
-template <class E, int N, int W, int V>
+template <class E, int N, int W, int V, bool Slot>
 __global__ void __launch_bounds__(W * kWave) softmax_split_merge(SplitArgs a) {
     constexpr int kThreads = W * kWave;
     __shared__ float red_m[W];
     __shared__ float red_s[W];
     const int t = threadIdx.x;
-    const int lane = t & (kWave - 1);
-    const int wave = t / kWave;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        float m = -INFINITY, s = 0.0f;
-        for (int j = t; j < a.tiles; j += kThreads) {
-            const f32x2 pr = *pair_at<E, N, W, V, true>(a, row, j);
-            merge_pair(m, s, pr.x, pr.y, a.coef);
-        }
-        wave_reduce_pair(m, s, a.coef);
-        if (lane == 0) {
-            red_m[wave] = m;
-            red_s[wave] = s;
-        }
-        __syncthreads();
-        m = red_m[0];
-        s = red_s[0];
-#pragma unroll
-        for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+        float m, s;
+        merge_row<E, N, W, V, Slot>(a, row, red_m, red_s, m, s);
         const f32x2 merged = {m, s};
-        for (int j = t; j < a.tiles; j += kThreads) *pair_at<E, N, W, V, true>(a, row, j) = merged;
+        for (int j = t; j < a.tiles; j += kThreads) *pair_at<E, N, W, V, Slot>(a, row, j) = merged;
         __syncthreads();  // red_m / red_s are rewritten for the next row
     }
 }
 
-template <class E, int N, int W, int V, bool Slot>
+template <class E, int N, int W, int V, bool Slot, bool Merged>
 __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
+    static_assert(Merged || !Slot, "the slots are merged by softmax_split_merge");
     typedef typename Access<E, N>::raw raw;
     constexpr int kThreads = W * kWave;
     constexpr int kTile = kThreads * V;
@@ -798,8 +825,6 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
     const raw* in = static_cast<const raw*>(a.in);
     raw* out = static_cast<raw*>(a.out);
     const int t = threadIdx.x;
-    const int lane = t & (kWave - 1);
-    const int wave = t / kWave;
     for (int64_t b = blockIdx.x; b < a.work; b += gridDim.x) {
         const int64_t row = b / a.tiles;
         const int base = int(b - row * a.tiles) * kTile;
@@ -808,31 +833,14 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
 #pragma unroll
         for (int v = 0; v < V; ++v) load_access<E, N, false>(p + v * kThreads, base + v * kThreads + t, a.nacc, 0, x[v]);
         float m, s;
-        if constexpr (Slot) {
-            // the row's merged pair, already in this tile's slot
-            const f32x2 pr = *pair_at<E, N, W, V, true>(a, row, int(b - row * a.tiles));
+        if constexpr (Merged) {
+            // the row's merged pair, already in this tile's entry
+            const f32x2 pr = *pair_at<E, N, W, V, Slot>(a, row, int(b - row * a.tiles));
             m = pr.x;
             s = pr.y;
-            __syncthreads();  // every thread has read the slot before the tile's first access is rewritten
+            if constexpr (Slot) __syncthreads();  // all have read the slot before the tile's first access is rewritten
         } else {
-            // Merge the row's tile pairs: thread t takes tiles t, t + 64W, ... in
-            // order, then the wave and workgroup reductions run in a fixed order.
-            m = -INFINITY;
-            s = 0.0f;
-            for (int j = t; j < a.tiles; j += kThreads) {
-                const f32x2 pr = *pair_at<E, N, W, V, false>(a, row, j);
-                merge_pair(m, s, pr.x, pr.y, a.coef);
-            }
-            wave_reduce_pair(m, s, a.coef);
-            if (lane == 0) {
-                red_m[wave] = m;
-                red_s[wave] = s;
-            }
-            __syncthreads();
-            m = red_m[0];
-            s = red_s[0];
-#pragma unroll
-            for (int w = 1; w < W; ++w) merge_pair(m, s, red_m[w], red_s[w], a.coef);
+            merge_row<E, N, W, V, false>(a, row, red_m, red_s, m, s);
         }
         const float mu = m == -INFINITY ? 0.0f : m;  // all -inf row: every term exp(-inf) = 0
         const float r = recip_sum(s);

@@ -21,9 +21,10 @@ def _gpu():
     binding._load()
 
 
-def _run_split(x, dtype, cols=None, force=1, inplace=False, offset=0):
-    """Run softmax_fwd_split on host array x (rows x row_stride); offset shifts both
-    pointers by that many elements (to reach the any-alignment path)."""
+def _run_split(x, dtype, cols=None, force=1, inplace=False, offset=0, noalloc=False):
+    """Run softmax_fwd_split (or, with noalloc, softmax_fwd_split_noalloc) on host
+    array x (rows x row_stride); offset shifts both pointers by that many
+    elements (to reach the any-alignment path)."""
     import torch
     rows, stride = x.shape
     cols = stride if cols is None else cols
@@ -37,8 +38,13 @@ def _run_split(x, dtype, cols=None, force=1, inplace=False, offset=0):
     nbytes = binding.split_workspace_bytes(rows, cols, code)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
     esz = 4 if dtype == "f32" else 2
-    binding.softmax_fwd_split(xd.data_ptr() + offset * esz, out.data_ptr() + offset * esz, rows, cols, stride,
-                              code, ws.data_ptr(), nbytes, force, torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    if noalloc:
+        binding.softmax_fwd_split_noalloc(xd.data_ptr() + offset * esz, out.data_ptr() + offset * esz, rows, cols,
+                                          stride, code, force, stream)
+    else:
+        binding.softmax_fwd_split(xd.data_ptr() + offset * esz, out.data_ptr() + offset * esz, rows, cols, stride,
+                                  code, ws.data_ptr(), nbytes, force, stream)
     torch.cuda.synchronize()
     return to_host(out, dtype)[offset:].reshape(rows, stride)
 
@@ -198,3 +204,25 @@ def test_fwd_few_very_wide_rows_in_place_or_past_the_rule(rows):
     y, kid = _run_fwd(x, "bf16", 1 << 18, inplace=(rows == 4))
     assert kid != binding.SPLIT_KERNEL
     check(y, x, "bf16", O.softmax(x, "bf16"), label=f"fwd wide rows={rows}")
+
+
+@pytest.mark.parametrize("dtype,rows,cols,offset", [
+    ("f32", 1, 4097 * 4096 + 4, 0),      # 16-byte path: 4098 tiles
+    ("bf16", 2, (1 << 25) + 8192, 0),    # 4097 tiles a row
+    ("f32", 1, (1 << 23) + 3, 1)])       # element path: 4097 tiles of 2048 elements
+def test_split_rows_of_many_tiles(dtype, rows, cols, offset):
+    """Rows of more than 4096 tiles: the workspace path merges each row's pairs in a
+    kernel of its own.  Against the oracle, with the same bits from softmax_fwd_split,
+    softmax_fwd_split_noalloc and (16-byte path) softmax_fwd."""
+    print(f"[gpu-case] split many tiles {dtype} rows={rows} cols={cols} offset={offset}", file=sys.stderr,
+          flush=True)
+    x = W.random_matrix(seed=80, rows=rows, cols=cols, dtype=dtype, sigma=2.0)
+    x[0, : cols // 3] = W.neg_inf(dtype)
+    y = _run_split(x, dtype, offset=offset)
+    check(y, x, dtype, O.softmax(x, dtype), label=f"split many tiles {dtype}")
+    yn = _run_split(x, dtype, offset=offset, noalloc=True)
+    assert np.array_equal(_bits(yn, dtype), _bits(y, dtype))
+    if offset == 0:
+        yf, kid = _run_fwd(x, dtype, cols)
+        assert kid == binding.SPLIT_KERNEL
+        assert np.array_equal(_bits(yf, dtype), _bits(y, dtype))
