@@ -270,11 +270,17 @@ def attention_shapes(steps: int, warmup: int) -> dict:
         reps = max(3, min(steps, 20 if n <= 8192 else 5))
         ms = time_launches(launch, 1, reps, max(1, min(warmup, 3)))
         flops = 4.0 * b * h * d * (n * (n + 1) / 2)  # two products over the kept (causal) keys
+        nbytes = 4.0 * b * h * n * d * 2  # Q, K, V read once and O written once
         tf = flops / (ms * 1e-3) / 1e12
+        bound_us = max(flops / 2.5e15, nbytes / (PEAK_GBPS * 1e9)) * 1e6  # the slower of MFMA and HBM at peak
         key = f"attention_{dt}_b{b}_h{h}_n{n}_d{d}_causal"
         out[key] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / 2500.0, 4),
-                    "note": "flops = 4*b*h*d*n(n+1)/2 (kept keys only); peak = 2.5 PFLOP/s dense fp16/bf16 MFMA"}
-        log(f"[bench] {key}: {out[key]['us']} us  {out[key]['tflops']} TFLOP/s ({100 * out[key]['frac_of_mfma_peak']:.1f}% of MFMA peak)")
+                    "bound": "mfma" if flops / 2.5e15 >= nbytes / (PEAK_GBPS * 1e9) else "hbm",
+                    "roofline_us": round(bound_us, 1), "frac_of_roofline": round(bound_us / (ms * 1e3), 4),
+                    "note": "flops = 4*b*h*d*n(n+1)/2 (kept keys only); bytes = 8*b*h*n*d (Q, K, V in, O out); "
+                            "roofline = max(flops / 2.5 PFLOP/s dense fp16/bf16 MFMA, bytes / 8 TB/s)"}
+        log(f"[bench] {key}: {out[key]['us']} us  {out[key]['tflops']} TFLOP/s ({100 * out[key]['frac_of_mfma_peak']:.1f}% of MFMA"
+            f" peak; {out[key]['bound']}-bound roofline {out[key]['roofline_us']} us, {100 * out[key]['frac_of_roofline']:.1f}%)")
         del qkv, o
     torch.cuda.synchronize()
     return out
