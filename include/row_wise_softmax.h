@@ -134,8 +134,8 @@ int softmax_fwd_causal(const void *in, void *out, int64_t rows, int64_t cols, in
  * "Dissecting Memory Bandwidth & SRAM Tiling in Triton" (section "Writing the
  * Kernel in OpenAI Triton") applies to every head's score matrix.
  *   rows_per_matrix  rows of one matrix (>= 1); rows must be a multiple of it
- *                    (else SOFTMAX_ERR_BAD_SHAPE).  rows_per_matrix == rows
- *                    is softmax_fwd_causal.
+ *                    (else SOFTMAX_ERR_BAD_SHAPE; not checked for an empty
+ *                    call).  rows_per_matrix == rows is softmax_fwd_causal.
  * Other arguments, layout, ownership, aliasing and errors as softmax_fwd_causal.
  */
 int softmax_fwd_causal_batched(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,

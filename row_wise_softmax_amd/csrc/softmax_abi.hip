@@ -612,7 +612,7 @@ int softmax_fwd_causal_batched(const void* in, void* out, int64_t rows, int64_t 
     bool empty;
     int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
     if (st != SOFTMAX_OK) return st;
-    if (rows_per_matrix < 1 || rows % rows_per_matrix != 0) return SOFTMAX_ERR_BAD_SHAPE;
+    if (!empty && (rows_per_matrix < 1 || rows % rows_per_matrix != 0)) return SOFTMAX_ERR_BAD_SHAPE;
     return fwd(in, out, rows, cols, row_stride, dtype, true, scale, diag, stream, rows_per_matrix);
 }
 

@@ -362,6 +362,8 @@ def test_batched_causal_rejects_before_any_launch(lib):
     assert fb(A, far, 12, 64, 64, 5, c(0.5), 0, 0, None) == 2    # 12 rows are not whole matrices of 5
     assert fb(A, far, 12, 64, 64, 4, c(-1.0), 0, 0, None) == 7   # bad scale
     assert fb(A, far, 0, 64, 64, 4, c(0.5), 0, 0, None) == 0     # empty
+    assert fb(A, far, 0, 64, 64, 0, c(0.5), 0, 0, None) == 0     # empty, from a [..., 0, m] batch
+    assert fb(A, far, 0, 64, 64, 0, c(-1.0), 0, 0, None) == 7    # the scale is checked even then
     assert fb(A, A + 8, 12, 64, 64, 4, c(0.5), 0, 0, None) == 4  # overlap
 
 

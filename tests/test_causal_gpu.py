@@ -145,3 +145,13 @@ def test_batched_causal_masks_each_matrix(dtype, shape, diag):
     y4 = binding.softmax(xd.view(b, h, n, m), causal=True, scale=0.5, diag=diag)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(y4.reshape(b * h * n, m), dtype), y)
+
+
+def test_batched_causal_empty_shapes():
+    """Empty [..., n, m] batches (no matrix, no rows, no columns) launch nothing and return."""
+    import torch
+    for shape in ((2, 0, 5), (0, 3, 4, 4), (2, 3, 4, 0)):
+        x = torch.empty(shape, device="cuda")
+        y = binding.softmax(x, causal=True, scale=0.5)
+        torch.cuda.synchronize()
+        assert y.shape == x.shape
