@@ -528,8 +528,8 @@ def sweep(steps: int, warmup: int, keys: list | None = None) -> list:
             results = []
             spin_up(res.softmax, res.n, SPIN_S)  # once per width; the kernels then follow each other closely
             for k in table:
-                if k.causal:
-                    continue  # the sweep times the plain softmax
+                if k.causal or "any_" in k.name:
+                    continue  # the sweep times the plain softmax on the aligned kernels
                 if not binding.kernel_fits(k.kid, res.ins[0].data_ptr(), res.outs[0].data_ptr(), wl.cols,
                                            wl.cols, res.code):
                     continue
@@ -573,7 +573,9 @@ def summarize_sweep(sweep_json: str) -> None:
     src = os.path.relpath(os.path.abspath(sweep_json), ROOT)
     keys = [r["key"] for r in rows if "key" in r]
     c5 = all(k.startswith("c5_") for k in keys)
+    vocab = all(k.startswith("vocab_") for k in keys)
     title = ("every plain table kernel at every c5 width" if c5 else
+             "every plain table kernel at vocabulary-sized widths, 24576 to 151936 columns" if vocab else
              "every plain table kernel at the exact shapes " + ", ".join(keys))
     cmd = f"    python3 bench.py --sweep --sweep-out {src}" if c5 else \
         f"    python3 bench.py --sweep --sweep-keys {','.join(keys)} --sweep-out {src}"
@@ -581,7 +583,7 @@ def summarize_sweep(sweep_json: str) -> None:
            "Commands (repository root):", "",
            cmd,
            f"    python3 bench.py --summarize-sweep {src}", "",
-           ("About 200 MB of input per tensor" if c5 else "The workloads' exact shapes") +
+           ("About 200 MB of input per tensor" if c5 or vocab else "The workloads' exact shapes") +
            ", rotating buffer sets of at least 1 GiB, 0.3 s spin-up per shape; GB/s by",
            "the metric's 2·rows·cols·size bytes.  `pick` is the kernel the width dispatch chooses, `best` the fastest",
            "kernel measured; the last column lists the next four.", "",
@@ -598,7 +600,8 @@ def summarize_sweep(sweep_json: str) -> None:
             out.append(f"- {r['crossover']}: the packed kernel (several rows per wave) wins up to "
                        f"{r['packed_wins_up_to_cols']} columns; one workgroup per row wins from "
                        f"{r['row_wins_from_cols']} columns.")
-    path = os.path.join(PROFILE_DIR, "sweep_c5_widths.md" if c5 else "sweep_fixed_shapes.md")
+    path = os.path.join(PROFILE_DIR, "sweep_c5_widths.md" if c5 else
+                        "sweep_vocab_widths.md" if vocab else "sweep_fixed_shapes.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
     print(path)
@@ -997,6 +1000,86 @@ def summarize_split_crossover(json_path: str) -> None:
     print("\n".join(out))
 
 
+ODD_WIDTHS = {"f32": (1001, 1025, 2049, 3001, 4097, 8193, 16385, 32001, 50257),
+              "bf16": (1001, 2049, 4097, 8193, 16385, 32001, 50257)}
+
+
+def odd_widths(steps: int, warmup: int) -> list:
+    """Widths that are not a multiple of 16 bytes, at about 200 MB per tensor:
+    softmax_fwd (the any-alignment kernels), the scalar path forced (what such
+    widths ran on before), and the aligned width just below (the same row count,
+    on the aligned kernels).  Seeded N(0, 1) inputs drawn on the device,
+    rotating buffers of at least 1 GiB, the best of three timings each."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    table = binding.kernel_table()
+    out = []
+    for dt, widths in ODD_WIDTHS.items():
+        code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
+        vec = 16 // esz
+        for cols in widths:
+            rows = max(64, int(200e6 // (cols * esz)))
+            nbytes = rows * cols * esz
+            n = n_buffers(2 * nbytes)
+            g = torch.Generator(device="cuda").manual_seed(cols)
+            xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
+            ys = [torch.empty_like(x) for x in xs]
+            kid = binding.softmax_select(xs[0].data_ptr(), ys[0].data_ptr(), cols, cols, code, rows=rows)
+            # the scalar kernel softmax_fwd runs for input and output at different offsets in their chunks
+            block = 64 * (1 if cols <= 512 else 4 if cols <= 8192 else 16)
+            scalar = next(k.kid for k in table if k.dtype == code and k.variant == "online" and k.vec_elems == 1
+                          and not k.causal and k.block == block)
+            al = cols // vec * vec  # the aligned width below, as a view of the same buffers (pitch = cols)
+            runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols,
+                                                                 code, stream),
+                    "scalar": lambda i: binding.softmax_fwd_kernel(scalar, xs[i].data_ptr(), ys[i].data_ptr(), rows,
+                                                                   cols, cols, code, stream)}
+            xa = [torch.randn((rows, al), generator=g, device="cuda").to(tdt) for _ in range(n)]
+            ya = [torch.empty_like(x) for x in xa]
+            runs["aligned_below"] = lambda i: binding.softmax_fwd(xa[i].data_ptr(), ya[i].data_ptr(), rows, al, al,
+                                                                  code, stream)
+            best = {k: 0.0 for k in runs}
+            for _ in range(3):
+                for k, f in runs.items():
+                    ms = time_launches(f, n, steps, warmup, spin_s=0.05)
+                    b = (nbytes if k != "aligned_below" else rows * al * esz) * 2
+                    best[k] = max(best[k], b / (ms * 1e-3) / 1e9)
+            r = {"dtype": dt, "rows": rows, "cols": cols, "aligned_cols": al,
+                 "kernel": table[kid].name if kid >= 0 else "split", **{k: round(v, 1) for k, v in best.items()}}
+            log(f"[bench] odd width {dt} {rows}x{cols}: {r}")
+            out.append(r)
+            del xs, ys, xa, ya
+            torch.cuda.empty_cache()
+    return out
+
+
+def summarize_odd_widths(json_path: str) -> None:
+    """Write profiles/odd_widths.md from `bench.py --odd-widths --odd-out` JSON."""
+    rows = json.load(open(json_path))
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    out = ["# Widths that are not a multiple of 16 bytes, MI355X (gfx950)", "",
+           "Commands (repository root):", "",
+           f"    python3 bench.py --odd-widths --odd-out {src}",
+           f"    python3 bench.py --summarize-odd-widths {src}", "",
+           "About 200 MB per tensor, contiguous (so consecutive rows start at every offset within a 16-byte chunk),",
+           "seeded N(0, 1) inputs, rotating buffers of at least 1 GiB, best of three timings; GB/s by the metric's",
+           "2·rows·cols·size bytes.  `softmax_fwd`: the library's pick (the any-alignment kernels); `scalar`: the",
+           "element-by-element online kernel, forced -- what softmax_fwd runs when input and output sit at",
+           "different offsets in their 16-byte chunks, and what every such width ran on before the any-alignment",
+           "kernels; `aligned below`: softmax_fwd on the same row count at the largest 16-byte-multiple width below.",
+           "",
+           "| dtype | rows | cols | pick | softmax_fwd GB/s | scalar GB/s | gain | aligned below (cols) GB/s | / aligned |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['dtype']} | {r['rows']} | {r['cols']} | {r['kernel']} | {r['softmax_fwd']:.0f} | "
+                   f"{r['scalar']:.0f} | {r['softmax_fwd'] / r['scalar']:.2f}x | {r['aligned_below']:.0f} "
+                   f"({r['aligned_cols']}) | {r['softmax_fwd'] / r['aligned_below']:.3f} |")
+    path = os.path.join(PROFILE_DIR, "odd_widths.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def summarize_chunk_copy(json_path: str, bench_json: str | None = None) -> None:
     """Write profiles/chunk_copy_shapes.md from `bench.py --chunk-copy --chunk-out` JSON and,
     optionally, a default bench line whose c5 shapes give each row kernel's own rate."""
@@ -1297,6 +1380,11 @@ def main() -> int:
     ap.add_argument("--summarize-copy-sizes", nargs="+", metavar="JSON [TRACE_CSV]", default=None,
                     help="write profiles/copy_ceiling_sizes.md from a --copy-out file (or a bench JSON line) and,"
                          " optionally, the rocprofv3 kernel-trace CSV of the same run")
+    ap.add_argument("--odd-widths", action="store_true",
+                    help="time widths that are not a multiple of 16 bytes: the pick, the scalar path, the aligned width")
+    ap.add_argument("--odd-out", default=None, help="JSON file for --odd-widths")
+    ap.add_argument("--summarize-odd-widths", metavar="JSON", default=None,
+                    help="write profiles/odd_widths.md from --odd-widths JSON and exit")
     ap.add_argument("--split-crossover", action="store_true",
                     help="time one workgroup per row, the split path and softmax_fwd on few, very wide rows")
     ap.add_argument("--split-out", default=None, help="JSON file for --split-crossover")
@@ -1321,6 +1409,9 @@ def main() -> int:
     args = ap.parse_args()
     if args.group_trace:
         group_trace(*args.group_trace)
+        return 0
+    if args.summarize_odd_widths:
+        summarize_odd_widths(args.summarize_odd_widths)
         return 0
     if args.summarize_split_crossover:
         summarize_split_crossover(args.summarize_split_crossover)
@@ -1382,6 +1473,12 @@ def main() -> int:
             with open(args.copy_out, "w") as f:
                 json.dump(table, f, indent=1)
         print(json.dumps(table), flush=True)
+        return 0
+    if args.odd_widths:
+        table = odd_widths(args.steps, args.warmup)
+        if args.odd_out:
+            with open(args.odd_out, "w") as f:
+                json.dump(table, f, indent=1)
         return 0
     if args.split_crossover:
         table = split_crossover(args.steps, args.warmup)

@@ -77,9 +77,16 @@ extern "C" {
 /*
  * softmax_fwd -- the fused row softmax, with the library's width dispatch.
  *   in, out     device pointers to rows x row_stride elements of `dtype`
- *               (the last row needs only `cols`); 16-byte-aligned pointers and
- *               16-byte-multiple row pitches take the vector path, anything
- *               else a scalar path of the same results.
+ *               (the last row needs only `cols`), element-aligned.  Rows move
+ *               in 16-byte accesses whatever the width, pitch and offset as
+ *               long as in and out sit at the same offset within their
+ *               16-byte chunks (two tensors of one layout from one
+ *               allocator): rows that start and end on 16-byte boundaries on
+ *               the aligned kernels, others on the any-alignment kernels,
+ *               which read a row's chunks whole (masking the neighbouring
+ *               rows' elements) and write the chunks it shares with its
+ *               neighbours element by element.  In and out at different
+ *               offsets take a scalar path of the same results.
  *   rows, cols  matrix shape; the softmax runs along each row.
  *   row_stride  elements between the starts of consecutive rows (>= cols).
  *   dtype       SOFTMAX_F32, SOFTMAX_F16 or SOFTMAX_BF16.

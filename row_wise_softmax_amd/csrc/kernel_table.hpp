@@ -17,6 +17,7 @@ struct Entry {
     int dtype;    // SOFTMAX_F32 / F16 / BF16
     int variant;  // SOFTMAX_VARIANT_*
     bool causal;  // scaled, causally masked softmax (softmax_fwd_causal)
+    bool any;     // 16-byte accesses for rows at any element offset (in and out at one offset mod 16)
     int vec;      // elements per access
     int lanes;    // packed: lanes per row; row/online: threads per row
     int vpl;      // accesses per lane per row (online: per chunk)

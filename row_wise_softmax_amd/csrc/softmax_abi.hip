@@ -64,15 +64,27 @@ int id_of(const Entry* e) {
     return -1;
 }
 
-// Widest row an entry holds: lanes (or threads) x accesses each x elements per access.
+// Widest row an entry holds: lanes (or threads) x accesses each x elements per
+// access; an any-alignment entry gives up vec - 1 of them to the row's offset
+// in its first chunk.
 int64_t max_cols_of(const Entry& e) {
     if (e.variant == SOFTMAX_VARIANT_ONLINE) return -1;
-    return int64_t(e.lanes) * e.vpl * e.vec;
+    return int64_t(e.lanes) * e.vpl * e.vec - (e.any ? e.vec - 1 : 0);
+}
+
+// Whether rows of this call can take the any-alignment kernels: element-
+// aligned pointers at the same offset in their 16-byte chunks, so that each
+// chunk of the input row maps onto one chunk of the output row.
+bool any16(const void* in, const void* out, int dtype) {
+    const uintptr_t esz = uintptr_t(elem_bytes(dtype));
+    return uintptr_t(in) % esz == 0 && uintptr_t(out) % esz == 0 && (uintptr_t(in) - uintptr_t(out)) % 16 == 0;
 }
 
 bool fits(const Entry& e, const void* in, const void* out, int64_t cols, int64_t row_stride, int dtype) {
     if (e.dtype != dtype) return false;
-    if (e.vec > 1) {
+    if (e.any) {
+        if (!any16(in, out, dtype)) return false;
+    } else if (e.vec > 1) {
         const uintptr_t acc = uintptr_t(e.vec) * elem_bytes(dtype);
         if (uintptr_t(in) % acc || uintptr_t(out) % acc) return false;
         if ((uint64_t(row_stride) * elem_bytes(dtype)) % acc) return false;
@@ -82,13 +94,13 @@ bool fits(const Entry& e, const void* in, const void* out, int64_t cols, int64_t
     return mc < 0 || cols <= mc;
 }
 
-const Entry* find(int dtype, int variant, bool causal, int vec, int lanes, int vpl, int groups) {
+const Entry* find(int dtype, int variant, bool causal, int vec, int lanes, int vpl, int groups, bool any = false) {
     int n;
     const Entry* t = table_of(dtype, &n);
     for (int i = 0; i < n; ++i) {
         const Entry& e = t[i];
-        if (e.variant == variant && e.causal == causal && e.vec == vec && e.lanes == lanes && e.vpl == vpl &&
-            e.groups == groups)
+        if (e.variant == variant && e.causal == causal && e.any == any && e.vec == vec && e.lanes == lanes &&
+            e.vpl == vpl && e.groups == groups)
             return &e;
     }
     return nullptr;
@@ -116,63 +128,115 @@ int pow2_at_least(int64_t v) {
 // 16-byte accesses per row the fastest shape keeps about two loads in flight
 // per lane and spreads the row over as many lanes as that takes (ragged rows
 // of 129..255 accesses excepted, see below); wider rows do best on four waves
-// with more loads each.  `nacc` is the row length in 16-byte accesses.  The
-// causal table holds the same picks.
+// with more loads each.  `nacc` is the row length in 16-byte accesses (for
+// rows at any element offset, the most chunks a row can touch).  The causal
+// table, and the any-alignment entries (any = true), hold the same picks.
+const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t nacc) {
+    const int vec16 = 16 / elem_bytes(dtype);
+    const Entry* e = nullptr;
+    if (nacc <= 64) {
+        // several rows per wave: L lanes per row, two row groups in flight
+        e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, pow2_at_least(nacc), 1, 2, any);
+    } else if (nacc <= 128) {
+        e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1, any);
+    } else if (nacc <= 2048) {
+        // ragged rows of 129..255 accesses: four waves of one access each
+        // (1000 fp32 columns: 6226 GB/s, against 5915 for two waves of two;
+        // at exactly 256 accesses the two-wave shape stays ahead).  fp32
+        // tensors of 8192 rows or more take two accesses per lane on the
+        // same four waves, half the slots idle: 0.5-5% faster at 520, 600,
+        // 700, 800 and 1000 columns with 8 K-49 K rows, but up to 4%
+        // slower with 1 K rows, and 15-25% slower for bf16 at any count.
+        if (nacc < 256) {
+            const int v = dtype == SOFTMAX_F32 && rows >= 8192 ? 2 : 1;
+            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, v, 1, any);
+        }
+        // otherwise one workgroup per row, two accesses per lane, up to 16
+        // waves (2048 accesses, 16384 bf16 columns: 6150 GB/s on sixteen
+        // waves against 5600 on four waves of eight; 8192 fp32 columns:
+        // 6220 against 6117)
+        const int w2 = pow2_at_least((nacc + 127) / 128);
+        // A row at any offset can touch one chunk more than its width needs,
+        // which past a power of two would double the waves and leave half
+        // of them idle (4097 bf16 columns: 4120 GB/s on eight waves of two);
+        // half the waves with three accesses each hold it instead.
+        if (e == nullptr && any && w2 >= 4 && nacc <= (w2 / 2) * 64 * 3)
+            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * (w2 / 2), 3, 1, any);
+        if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * w2, 2, 1, any);
+        // Few rows: when the whole job fills the chip's wave slots at most
+        // twice, every workgroup of a round starts, loads and computes
+        // together, and HBM idles while a round computes.  The row kernel's
+        // persistent twin (same shape, grid = resident workgroups, the next
+        // row's loads issued before the current row's reductions) keeps
+        // loads in flight: 1-5% faster at one round or less, 2-21% at two
+        // (4096 x 4096 bf16: 5044 -> 5973 GB/s; 2048 x 2048 fp32: 5080 ->
+        // 5170).  From four rounds on the plain kernel is 1-7% ahead.
+        if (e != nullptr && rows * (e->lanes / 64) <= kFewRowWaves) {
+            const Entry* pf = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, e->lanes, e->vpl, 1, any);
+            if (pf != nullptr) e = pf;
+        }
+    } else if (elem_bytes(dtype) == 2) {
+        // 16-bit rows past 2048 chunks (16384 columns) hold 8 values per
+        // chunk, so four or eight waves of 16 accesses need 128 registers of
+        // them per lane; sixteen waves do better (bf16, about 200 MB tensors:
+        // 24576 columns 5670 GB/s on sixteen waves of four against 3513 on
+        // four of sixteen; 32000: 5618 against 4025; 65536: 4965 on sixteen
+        // of eight against 4243 on eight of sixteen).  Rows that leave more
+        // than a tenth of sixteen waves of eight idle take the online kernel
+        // (50304 columns: 4831 GB/s on sixteen waves of two chunks, against
+        // 3509 on eight waves of sixteen).
+        // Rows at any offset carry the boundary masks, which cost the
+        // sixteen-wave shapes of four or more accesses their second
+        // workgroup per CU; they take sixteen waves of three up to 3072
+        // chunks, eight waves of eight up to 4096 (32001 bf16 columns: 5039
+        // GB/s against 4326 on sixteen of four) and sixteen waves of eight
+        // up to 8192 (50257 columns: 4211 against 3663 online).
+        if (any) {
+            if (nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, true);
+            else if (nacc <= 4096) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 8, 8, 1, true);
+            else if (nacc <= 8192) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, true);
+        } else if (nacc <= 4096) {
+            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 4, 1, false);
+        } else if (nacc <= 8192 && nacc * 10 >= 8192 * 9) {
+            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, false);
+        }
+        if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, any ? 4 : 2, 1, any);
+        if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, 4, 1, any);
+    } else {
+        // wider rows: four waves with more accesses each (16384 fp32
+        // columns: 5825 GB/s, against 5625 on eight waves and 5613 on
+        // sixteen); where the table has no such shape, 8 or 16 waves
+        const int v4 = pow2_at_least((nacc + 255) / 256);
+        for (int w = 4; w <= 16 && e == nullptr; w *= 2) {
+            const int v = v4 * 4 / w;
+            if (v >= 1) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * w, v, 1, any);
+        }
+        // A row at any offset just past a power of two would leave a quarter
+        // or more of that shape's slots idle: sixteen waves with as few
+        // accesses each as hold it instead (16385 bf16 columns, 2049 chunks:
+        // 3609 GB/s on eight waves of eight, 5183 on sixteen of three)
+        if (any && (e == nullptr || nacc * 4 < int64_t(e->lanes) * e->vpl * 3) && nacc <= 8 * 1024) {
+            const int v = int((nacc + 1023) / 1024);
+            const Entry* w16 = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, v == 7 ? 8 : v, 1, any);
+            if (w16 != nullptr) e = w16;
+        }
+        if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, 4, 1, any);
+    }
+    return e;
+}
+
 const Entry* select_entry(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
                           int dtype, bool causal) {
     const int vec16 = 16 / elem_bytes(dtype);
     if (aligned16(in, out, cols, row_stride, dtype)) {
-        const int64_t nacc = cols / vec16;
-        const Entry* e = nullptr;
-        if (nacc <= 64) {
-            // several rows per wave: L lanes per row, two row groups in flight
-            e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, pow2_at_least(nacc), 1, 2);
-        } else if (nacc <= 128) {
-            e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1);
-        } else if (nacc <= 2048) {
-            // ragged rows of 129..255 accesses: four waves of one access each
-            // (1000 fp32 columns: 6226 GB/s, against 5915 for two waves of two;
-            // at exactly 256 accesses the two-wave shape stays ahead).  fp32
-            // tensors of 8192 rows or more take two accesses per lane on the
-            // same four waves, half the slots idle: 0.5-5% faster at 520, 600,
-            // 700, 800 and 1000 columns with 8 K-49 K rows, but up to 4%
-            // slower with 1 K rows, and 15-25% slower for bf16 at any count.
-            if (nacc < 256) {
-                const int v = dtype == SOFTMAX_F32 && rows >= 8192 ? 2 : 1;
-                e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, v, 1);
-            }
-            // otherwise one workgroup per row, two accesses per lane, up to 16
-            // waves (2048 accesses, 16384 bf16 columns: 6150 GB/s on sixteen
-            // waves against 5600 on four waves of eight; 8192 fp32 columns:
-            // 6220 against 6117)
-            if (e == nullptr)
-                e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * pow2_at_least((nacc + 127) / 128), 2, 1);
-            // Few rows: when the whole job fills the chip's wave slots at most
-            // twice, every workgroup of a round starts, loads and computes
-            // together, and HBM idles while a round computes.  The row kernel's
-            // persistent twin (same shape, grid = resident workgroups, the next
-            // row's loads issued before the current row's reductions) keeps
-            // loads in flight: 1-5% faster at one round or less, 2-21% at two
-            // (4096 x 4096 bf16: 5044 -> 5973 GB/s; 2048 x 2048 fp32: 5080 ->
-            // 5170).  From four rounds on the plain kernel is 1-7% ahead.
-            if (e != nullptr && rows * (e->lanes / 64) <= kFewRowWaves) {
-                const Entry* pf = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, e->lanes, e->vpl, 1);
-                if (pf != nullptr) e = pf;
-            }
-        } else {
-            // wider rows: four waves with more accesses each (16384 fp32
-            // columns: 5825 GB/s, against 5625 on eight waves and 5613 on
-            // sixteen); where the table has no such shape, 8 or 16 waves
-            const int v4 = pow2_at_least((nacc + 255) / 256);
-            for (int w = 4; w <= 16 && e == nullptr; w *= 2) {
-                const int v = v4 * 4 / w;
-                if (v >= 1) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * w, v, 1);
-            }
-            if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, 4, 1);
-        }
+        const Entry* e = pick_16byte(dtype, causal, false, rows, cols / vec16);
+        if (e && fits(*e, in, out, cols, row_stride, dtype)) return e;
+    } else if (any16(in, out, dtype)) {
+        // rows at any element offset: the same rule on the chunks a row can touch
+        const Entry* e = pick_16byte(dtype, causal, true, rows, (cols + 2 * vec16 - 2) / vec16);
         if (e && fits(*e, in, out, cols, row_stride, dtype)) return e;
     }
-    // Any alignment: scalar accesses, streamed twice.
+    // Pointers at different offsets in their 16-byte chunks: scalar accesses, streamed twice.
     const int w = cols <= 64 * 8 ? 1 : (cols <= 4 * 64 * 8 * 4 ? 4 : 16);
     return find(dtype, SOFTMAX_VARIANT_ONLINE, causal, 1, 64 * w, 8, 1);
 }
@@ -194,7 +258,9 @@ const Entry* entry_for_variant(const void* in, const void* out, int64_t cols, in
         if (!fits(e, in, out, cols, row_stride, dtype)) continue;
         if (best == nullptr || (e.vec > 1) > (best->vec > 1) ||
             ((e.vec > 1) == (best->vec > 1) &&
-             (e.vpl < best->vpl || (e.vpl == best->vpl && e.groups < best->groups))))
+             (!e.any > !best->any ||
+              (e.any == best->any &&
+               (e.vpl < best->vpl || (e.vpl == best->vpl && e.groups < best->groups))))))
             best = &e;
     }
     return best;
@@ -271,14 +337,17 @@ bool line_shift_fits(const Entry& e, const void* out, int64_t cols, int64_t row_
     if (e.variant != SOFTMAX_VARIANT_ROW && e.variant != SOFTMAX_VARIANT_ROW_PF) return false;
     const int64_t esz = elem_bytes(e.dtype);
     if (e.vec * esz != 16) return false;
-    const int64_t base = int64_t((uintptr_t(out) >> 4) & 7), pitch = ((row_stride * esz) >> 4) & 7;
+    // row r's first chunk is line (out + r * pitch bytes) / 16 mod 8 of its
+    // 128-byte line, which repeats with a period dividing 128 rows
+    const uint64_t pitch = uint64_t(row_stride) * uint64_t(esz);
     int64_t most = 0;
-    for (int64_t r = 0; r < 8; ++r) {
-        const int64_t sh = (base + r * pitch) & 7;
+    for (uint64_t r = 0; r < 128; ++r) {
+        const int64_t sh = int64_t(((uintptr_t(out) + r * pitch) >> 4) & 7);
         most = sh > most ? sh : most;
     }
+    const int64_t chunks = e.any ? (cols + 2 * e.vec - 2) / e.vec : cols / e.vec;
     const int64_t slots = int64_t(e.lanes) * e.vpl;
-    return most > 0 && slots >= cols / e.vec + most;
+    return most > 0 && slots >= chunks + most;
 }
 
 int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, float coef,
@@ -290,7 +359,8 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     a.stride = row_stride / e.vec;
     a.diag = diag;
     a.period = period;
-    a.nacc = int(cols / e.vec);
+    a.pitch = row_stride * elem_bytes(e.dtype);
+    a.nacc = int(e.any ? (cols + 2 * e.vec - 2) / e.vec : cols / e.vec);
     a.cols = int(cols);
     a.coef = coef;
     int block;

@@ -166,6 +166,13 @@ __device__ inline void store_elems(typename Access<E, N>::raw* p, const float* f
     }
 }
 
+// Store one element at p (one of an access's N, element-aligned).
+template <class E>
+__device__ inline void store_elem(void* p, float f) {
+    if constexpr (E::kBytes == 4) st<true>(static_cast<unsigned*>(p), __builtin_bit_cast(unsigned, f));
+    else st<true>(static_cast<unsigned short*>(p), narrow_half<E>(f));
+}
+
 // ------------------------------------------------------- cross-lane steps
 
 __device__ inline float as_f(int v) { return __builtin_bit_cast(float, v); }
@@ -305,6 +312,7 @@ struct Args {
     int64_t nblocks;  // logical workgroups; the grid may be smaller and loop
     int64_t diag;     // causal kernels: row i keeps columns j <= i + diag
     int64_t period;   // causal kernels: rows per matrix, i counted within its matrix; 0: one matrix
+    int64_t pitch;    // bytes between row starts (any-alignment kernels)
     int nacc;         // accesses per row (cols / access width)
     int cols;         // elements per row
     float coef;       // scale * log2(e); log2(e) for the plain softmax
@@ -378,18 +386,106 @@ __device__ inline void load_access(const typename Access<E, N>::raw* p, int idx,
     }
 }
 
+// ------------------------------------------------ rows at any element offset
+//
+// When a row's start is not on a 16-byte boundary (a width that is not a
+// multiple of 16 bytes, an odd row pitch, a pointer inside a chunk), the
+// any-alignment kernels (Any = true) still move it in aligned 16-byte
+// accesses: the chunks that hold any of its elements, counted from the chunk
+// holding its first element, at chunk-relative element index lo.  The row
+// covers chunk-relative elements [lo, lo + cols).  A chunk is read whole: it
+// lies in one page with elements of the row, so the neighbouring rows' bytes
+// it also holds are safe to read, and they are masked to -inf.  It is
+// written whole when all its elements are the row's, element by element in
+// the (at most two) chunks it shares with the neighbouring rows, so those
+// rows' bytes are never written.  Input and output sit at the same offset in
+// their chunks (the host checks), so one lo serves both.
+template <class E, int N>
+struct RowPos {
+    const typename Access<E, N>::raw* in;
+    typename Access<E, N>::raw* out;
+    int lo;  // chunk-relative index of the row's first element (0 for aligned rows)
+};
+
+template <class E, int N, bool Any>
+__device__ inline RowPos<E, N> row_pos(const Args& a, int64_t row) {
+    typedef typename Access<E, N>::raw raw;
+    if constexpr (!Any) {
+        return {static_cast<const raw*>(a.in) + row * a.stride, static_cast<raw*>(a.out) + row * a.stride, 0};
+    } else {
+        const uintptr_t off = uintptr_t(row) * uintptr_t(a.pitch);
+        const uintptr_t ia = reinterpret_cast<uintptr_t>(a.in) + off;
+        const uintptr_t sub = ia & 15;
+        return {reinterpret_cast<const raw*>(ia - sub),
+                reinterpret_cast<raw*>(reinterpret_cast<uintptr_t>(a.out) + off - sub), int(sub) / E::kBytes};
+    }
+}
+
+// Chunks a row touches: the aligned kernels' accesses per row, or (Any) the
+// chunks over [lo, lo + cols).
+template <class E, int N, bool Any>
+__device__ inline int row_chunks(const Args& a, int lo) {
+    if constexpr (!Any) return a.nacc;
+    else return (lo + a.cols + N - 1) / N;
+}
+
+// Load chunk `idx` of an any-alignment row whose loaded elements are [lo, hi)
+// (hi = lo + kept columns); a chunk holding none of them is not read, and f
+// is then left as it was.  mask_any, run once every access of the row is
+// loaded, sets what lies outside [lo, hi) to -inf: masking right after each
+// load would make each load wait for the one before.
+template <class E, int N, bool Keep = false>
+__device__ inline void load_any(const typename Access<E, N>::raw* p, int idx, int lo, int hi, float* f) {
+    const int first = idx * N;
+    if (idx >= 0 && first < hi && first + N > lo) load_elems<E, N, Keep>(p, f);
+}
+
+template <int N>
+__device__ inline void mask_any(int idx, int lo, int hi, float* f) {
+    const int first = idx * N;
+    if (first >= lo && first + N <= hi) return;  // the whole chunk is the row's: most lanes
+#pragma unroll
+    for (int e = 0; e < N; ++e) f[e] = first + e >= lo && first + e < hi ? f[e] : -INFINITY;
+}
+
+// Store the elements of chunk `idx` that lie in [lo, hi) (hi = lo + cols).
+template <class E, int N>
+__device__ inline void store_any(typename Access<E, N>::raw* q, int idx, int lo, int hi, const float* f) {
+    const int first = idx * N;
+    if (idx < 0 || first >= hi || first + N <= lo) return;
+    if (first >= lo && first + N <= hi) {
+        store_elems<E, N>(q, f);
+        return;
+    }
+    unsigned char* b = reinterpret_cast<unsigned char*>(q);
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        if (first + e >= lo && first + e < hi) store_elem<E>(b + e * E::kBytes, f[e]);
+}
+
+// The load of one access of a row: load_access for aligned rows, load_any for
+// the rest (its loaded elements [lo, lo + kept); mask_one after all loads).
+template <class E, int N, bool Causal, bool Any, bool Keep = false>
+__device__ inline void load_one(const typename Access<E, N>::raw* p, int idx, int nacc, int lo, int kept, float* f) {
+    if constexpr (Any) load_any<E, N, Keep>(p, idx, lo, lo + kept, f);
+    else load_access<E, N, Causal, Keep>(p, idx, nacc, kept, f);
+}
+
+template <int N, bool Any>
+__device__ inline void mask_one(int idx, int lo, int kept, float* f) {
+    if constexpr (Any) mask_any<N>(idx, lo, lo + kept, f);
+}
+
 // ------------------------------------------------------------ packed kernel
 //
 // Lane l of a group of L lanes owns accesses l, l + L, l + 2L, ... of its row,
 // so one load instruction of a wave reads 64 consecutive 16-byte chunks: the
 // rows of a group are adjacent when the row stride equals the width.
-template <class E, int N, int L, int V, int G, bool Causal>
+template <class E, int N, int L, int V, int G, bool Causal, bool Any = false>
 __global__ void __launch_bounds__(256) softmax_packed(Args a) {
     typedef typename Access<E, N>::raw raw;
     constexpr int kRowsPerGroup = kWave / L;
     constexpr int kRowsPerWave = kRowsPerGroup * G;
-    const raw* in = static_cast<const raw*>(a.in);
-    raw* out = static_cast<raw*>(a.out);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int waves = blockDim.x / kWave;
@@ -399,14 +495,26 @@ __global__ void __launch_bounds__(256) softmax_packed(Args a) {
     for (int64_t b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
         const int64_t row0 = (b * waves + wave) * kRowsPerWave + sub;
         float x[G][V][N];
+        RowPos<E, N> pos[G];  // (aligned rows: recomputed at the store)
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t row = row0 + g * kRowsPerGroup;
             const bool live = row < a.rows;
             const int kept = live ? kept_cols<Causal>(row, a) : 0;
-            const raw* p = in + row * a.stride + l;
+            pos[g] = row_pos<E, N, Any>(a, row);  // a row past the last is never dereferenced
+            const raw* p = pos[g].in + l;
 #pragma unroll
-            for (int v = 0; v < V; ++v) load_access<E, N, Causal>(p + v * L, v * L + l, live ? a.nacc : 0, kept, x[g][v]);
+            for (int v = 0; v < V; ++v)
+                load_one<E, N, Causal, Any>(p + v * L, v * L + l, live ? a.nacc : 0, pos[g].lo, kept, x[g][v]);
+        }
+        if constexpr (Any) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int64_t row = row0 + g * kRowsPerGroup;
+                const int kept = row < a.rows ? kept_cols<Causal>(row, a) : 0;
+#pragma unroll
+                for (int v = 0; v < V; ++v) mask_one<N, Any>(v * L + l, pos[g].lo, kept, x[g][v]);
+            }
         }
         float mx[G], r[G];
 #pragma unroll
@@ -427,10 +535,16 @@ __global__ void __launch_bounds__(256) softmax_packed(Args a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t row = row0 + g * kRowsPerGroup;
-            raw* p = out + row * a.stride + l;
+            raw* p = (Any ? pos[g].out : static_cast<raw*>(a.out) + row * a.stride) + l;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                if (row < a.rows && v * L + l < a.nacc) {
+                if constexpr (Any) {
+                    if (row < a.rows) {
+#pragma unroll
+                        for (int e = 0; e < N; ++e) x[g][v][e] *= r[g];
+                        store_any<E, N>(p + v * L, v * L + l, pos[g].lo, pos[g].lo + a.cols, x[g][v]);
+                    }
+                } else if (row < a.rows && v * L + l < a.nacc) {
 #pragma unroll
                     for (int e = 0; e < N; ++e) x[g][v][e] *= r[g];
                     store_elems<E, N>(p + v * L, x[g][v]);
@@ -460,11 +574,13 @@ __device__ inline int first_access(int t, int s) {
 
 // Thread loads accesses i0, i0 + 64, ..., i0 + 64 (V - 1) of the row (i0 from
 // first_access); p addresses access i0.
-template <class E, int N, int W, int V, bool Causal>
-__device__ inline void load_row(const typename Access<E, N>::raw* p, int i0, int nacc, int kept,
+template <class E, int N, int W, int V, bool Causal, bool Any = false>
+__device__ inline void load_row(const typename Access<E, N>::raw* p, int i0, int nacc, int lo, int kept,
                                 float (&x)[V][N]) {
 #pragma unroll
-    for (int v = 0; v < V; ++v) load_access<E, N, Causal>(p + v * kWave, v * kWave + i0, nacc, kept, x[v]);
+    for (int v = 0; v < V; ++v) load_one<E, N, Causal, Any>(p + v * kWave, v * kWave + i0, nacc, lo, kept, x[v]);
+#pragma unroll
+    for (int v = 0; v < V; ++v) mask_one<N, Any>(v * kWave + i0, lo, kept, x[v]);
 }
 
 // Max, exponentials, sum and the normalised store of one row held in x.
@@ -472,9 +588,9 @@ __device__ inline void load_row(const typename Access<E, N>::raw* p, int i0, int
 // rows in turn: every thread reads red_max before the second barrier and
 // red_sum before the next call's first barrier, so the slots can be reused
 // without a third barrier.
-template <class E, int N, int W, int V>
+template <class E, int N, int W, int V, bool Any = false>
 __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* q, int t, int i0, int nacc,
-                                  float coef, float* red_max, float* red_sum) {
+                                  float coef, float* red_max, float* red_sum, int lo = 0, int cols = 0) {
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
     float m = x[0][0];
@@ -506,7 +622,11 @@ __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* 
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int idx = v * kWave + i0;
-        if (idx >= 0 && idx < nacc) {
+        if constexpr (Any) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) x[v][e] *= r;
+            store_any<E, N>(q + v * kWave, idx, lo, lo + cols, x[v]);
+        } else if (idx >= 0 && idx < nacc) {
 #pragma unroll
             for (int e = 0; e < N; ++e) x[v][e] *= r;
             store_elems<E, N>(q + v * kWave, x[v]);
@@ -514,19 +634,17 @@ __device__ inline void finish_row(float (&x)[V][N], typename Access<E, N>::raw* 
     }
 }
 
-template <class E, int N, int W, int V, bool Causal, bool Shift = false>
+template <class E, int N, int W, int V, bool Causal, bool Shift = false, bool Any = false>
 __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
-    typedef typename Access<E, N>::raw raw;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
-    const raw* in = static_cast<const raw*>(a.in);
-    raw* out = static_cast<raw*>(a.out);
     const int t = threadIdx.x;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         float x[V][N];
-        const int i0 = first_access<V>(t, line_shift<E, N, Shift>(out + row * a.stride));
-        load_row<E, N, W, V, Causal>(in + row * a.stride + i0, i0, a.nacc, kept_cols<Causal>(row, a), x);
-        finish_row<E, N, W, V>(x, out + row * a.stride + i0, t, i0, a.nacc, a.coef, red_max, red_sum);
+        const RowPos<E, N> pos = row_pos<E, N, Any>(a, row);
+        const int i0 = first_access<V>(t, line_shift<E, N, Shift>(pos.out));
+        load_row<E, N, W, V, Causal, Any>(pos.in + i0, i0, a.nacc, pos.lo, kept_cols<Causal>(row, a), x);
+        finish_row<E, N, W, V, Any>(x, pos.out + i0, t, i0, a.nacc, a.coef, red_max, red_sum, pos.lo, a.cols);
     }
 }
 
@@ -537,19 +655,17 @@ __global__ void __launch_bounds__(W * kWave) softmax_row(Args a) {
 // before the current row is reduced, so its HBM reads overlap the current
 // row's reductions, exponentials and stores.  The grid is sized to the
 // number of workgroups the chip holds at once.
-template <class E, int N, int W, int V, bool Causal, bool Shift = false>
+template <class E, int N, int W, int V, bool Causal, bool Shift = false, bool Any = false>
 __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
-    typedef typename Access<E, N>::raw raw;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
-    const raw* in = static_cast<const raw*>(a.in);
-    raw* out = static_cast<raw*>(a.out);
     const int t = threadIdx.x;
     int64_t row = blockIdx.x;
     if (row >= a.rows) return;  // uniform per workgroup: no barrier is skipped by part of it
     float nx[V][N];
-    int ni0 = first_access<V>(t, line_shift<E, N, Shift>(out + row * a.stride));
-    load_row<E, N, W, V, Causal>(in + row * a.stride + ni0, ni0, a.nacc, kept_cols<Causal>(row, a), nx);
+    RowPos<E, N> npos = row_pos<E, N, Any>(a, row);
+    int ni0 = first_access<V>(t, line_shift<E, N, Shift>(npos.out));
+    load_row<E, N, W, V, Causal, Any>(npos.in + ni0, ni0, a.nacc, npos.lo, kept_cols<Causal>(row, a), nx);
     for (; row < a.rows; row += gridDim.x) {
         float x[V][N];
 #pragma unroll
@@ -557,12 +673,14 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
 #pragma unroll
             for (int e = 0; e < N; ++e) x[v][e] = nx[v][e];
         const int i0 = ni0;
+        const RowPos<E, N> pos = npos;
         const int64_t next = row + gridDim.x;
         if (next < a.rows) {
-            ni0 = first_access<V>(t, line_shift<E, N, Shift>(out + next * a.stride));
-            load_row<E, N, W, V, Causal>(in + next * a.stride + ni0, ni0, a.nacc, kept_cols<Causal>(next, a), nx);
+            npos = row_pos<E, N, Any>(a, next);
+            ni0 = first_access<V>(t, line_shift<E, N, Shift>(npos.out));
+            load_row<E, N, W, V, Causal, Any>(npos.in + ni0, ni0, a.nacc, npos.lo, kept_cols<Causal>(next, a), nx);
         }
-        finish_row<E, N, W, V>(x, out + row * a.stride + i0, t, i0, a.nacc, a.coef, red_max, red_sum);
+        finish_row<E, N, W, V, Any>(x, pos.out + i0, t, i0, a.nacc, a.coef, red_max, red_sum, pos.lo, a.cols);
     }
 }
 
@@ -580,32 +698,35 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
 // Exponentials here are 2^((x - m) c), two operations: each lane's sum is
 // relative to that lane's own max, and the subtraction keeps the terms of
 // different lanes and both passes consistent without a shared frame.
-template <class E, int N, int W, int V, bool Causal>
+template <class E, int N, int W, int V, bool Causal, bool Any = false>
 __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
     typedef typename Access<E, N>::raw raw;
     constexpr int kThreads = W * kWave;
     constexpr int kChunk = kThreads * V;
     __shared__ float red_m[W];
     __shared__ float red_s[W];
-    const raw* in = static_cast<const raw*>(a.in);
-    raw* out = static_cast<raw*>(a.out);
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
     const float coef = a.coef;
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const raw* p = in + row * a.stride + t;
+        const RowPos<E, N> pos = row_pos<E, N, Any>(a, row);
+        const raw* p = pos.in + t;
         const int kept = kept_cols<Causal>(row, a);
         // accesses that hold at least one kept column
-        const int nread = Causal ? (kept + N - 1) / N : a.nacc;
+        const int nread = Causal || Any ? (pos.lo + kept + N - 1) / N : a.nacc;
+        const int nacc = row_chunks<E, N, Any>(a, pos.lo);
         float lm = -INFINITY;  // lane running max; -inf: nothing finite seen yet
         float ls = 0.0f;       // lane sum of e^(c (x - lm))
         for (int c = 0; c < nread; c += kChunk) {
             float x[V][N];
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                load_access<E, N, Causal, true>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, kept, x[v]);
+                load_one<E, N, Causal, Any, true>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, pos.lo, kept,
+                                                  x[v]);
+#pragma unroll
+            for (int v = 0; v < V; ++v) mask_one<N, Any>(c + v * kThreads + t, pos.lo, kept, x[v]);
             float cm = x[0][0];
 #pragma unroll
             for (int v = 0; v < V; ++v)
@@ -636,15 +757,22 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
         const float m = lm == -INFINITY ? 0.0f : lm;  // all -inf row: every term exp(-inf) = 0
         const float r = recip_sum(ls);
 
-        raw* q = out + row * a.stride + t;
-        for (int c = 0; c < a.nacc; c += kChunk) {
+        raw* q = pos.out + t;
+        for (int c = 0; c < nacc; c += kChunk) {
             float x[V][N];
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                load_access<E, N, Causal>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, kept, x[v]);
+                load_one<E, N, Causal, Any>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, pos.lo, kept, x[v]);
+#pragma unroll
+            for (int v = 0; v < V; ++v) mask_one<N, Any>(c + v * kThreads + t, pos.lo, kept, x[v]);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                if (c + v * kThreads + t < a.nacc) {
+                const int idx = c + v * kThreads + t;
+                if constexpr (Any) {
+#pragma unroll
+                    for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m, coef) * r;
+                    store_any<E, N>(q + c + v * kThreads, idx, pos.lo, pos.lo + a.cols, x[v]);
+                } else if (idx < a.nacc) {
 #pragma unroll
                     for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m, coef) * r;
                     store_elems<E, N>(q + c + v * kThreads, x[v]);

@@ -40,6 +40,9 @@ import numpy as np
 DTYPES = {"f32": (0, 4), "f16": (1, 2), "bf16": (2, 2)}
 
 SWEEP_WIDTHS = (32, 64, 128, 256, 512, 1000, 1024, 2048, 3000, 4096, 8192, 16384)
+# Rows past the sweep's widest, as wide as a vocabulary's logits (about 200 MB per tensor too).
+VOCAB_WIDTHS = {"bf16": (24576, 32000, 32768, 50304, 65536, 128256, 151936),
+                "f32": (24576, 32000, 32768, 50304, 65536, 128256)}
 SWEEP_BYTES = 200_000_000  # decimal bytes of input per sweep tensor
 
 _CHUNK_ELEMS = 1 << 20  # rows are drawn in slices of about this many elements
@@ -191,6 +194,10 @@ def _build_registry() -> dict:
             key = f"c5_{dt}_{w}"
             reg[key] = Workload(f"c5_sweep_{sweep_rows(w, dt)}x{w}_{dt}", sweep_rows(w, dt), w, dt,
                                 "normal", (5, w, dtype_code(dt)), {"sigma": 2.0})
+    for dt, widths in VOCAB_WIDTHS.items():
+        for w in widths:
+            reg[f"vocab_{dt}_{w}"] = Workload(f"vocab_{sweep_rows(w, dt)}x{w}_{dt}", sweep_rows(w, dt), w, dt,
+                                              "normal", (7, w, dtype_code(dt)), {"sigma": 2.0})
     return reg
 
 

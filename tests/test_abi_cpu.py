@@ -128,6 +128,8 @@ def test_kernel_table_is_consistent(lib):
         assert k.dtype in (0, 1, 2)
         if k.variant == "online":
             assert k.max_cols == -1
+        elif "any_" in k.name:  # rows at any element offset give vec - 1 slots to the offset
+            assert k.max_cols == k.lanes * k.vecs_per_lane * k.vec_elems - (k.vec_elems - 1)
         else:
             assert k.max_cols == k.lanes * k.vecs_per_lane * k.vec_elems
         if k.vec_elems > 1:
@@ -151,12 +153,19 @@ def test_dispatch_always_picks_a_fitting_kernel(lib, dtype, cols, causal):
     assert binding.kernel_fits(kid, A, B, cols, cols, dtype)
     info = binding.kernel_table()[kid]
     assert info.causal == causal
-    if (cols * esz) % 16 == 0:
-        assert info.vec_elems * esz == 16, "aligned rows must take 16-byte accesses"
-    # misaligned pointers fall back to the scalar path
+    # 16-byte accesses whatever the width: aligned rows on the aligned kernels,
+    # other widths on the any-alignment ones
+    assert info.vec_elems * esz == 16
+    assert ("any_" in info.name) == ((cols * esz) % 16 != 0)
+    # pointers one 16-bit element past a chunk boundary, at the same offset:
+    # element-aligned for 16-bit types (any-alignment kernels), not for fp32 (scalar)
     kid2 = binding.softmax_select(A + 2, B + 2, cols, cols, dtype, rows=4, causal=causal)
-    assert binding.kernel_table()[kid2].vec_elems == 1
-    assert binding.kernel_table()[kid2].causal == causal
+    k2 = binding.kernel_table()[kid2]
+    assert k2.causal == causal
+    assert (k2.vec_elems == 1) if esz == 4 else ("any_" in k2.name and k2.vec_elems == 8)
+    # input and output at different offsets in their chunks: the scalar path
+    kid3 = binding.softmax_select(A + 4, B + 8, cols, cols, dtype, rows=4, causal=causal)
+    assert binding.kernel_table()[kid3].vec_elems == 1
 
 
 @pytest.mark.parametrize("dtype", [0, 1, 2])
@@ -310,6 +319,45 @@ def test_few_very_wide_rows_split_through_the_output(lib):
     assert sel(1 << 17, 0, 8, x=a + 4, y=b + 4) != S                    # not on the 16-byte path
     assert sel(1 << 17, 0, 8, stride=(1 << 17) + 1) != S                # row pitch not a 16-byte multiple
     assert sel(1 << 17, 0, 8, causal=True) != S                         # the causal form never splits
+
+
+def test_any_alignment_dispatch(lib):
+    """Rows at any element offset take the any-alignment entries of the width rule
+    on the chunks a row can touch, ceil((cols + vec - 1) / vec); just past a power of
+    two, half the waves with three accesses each, and sixteen waves for wide rows
+    that would leave a quarter of the slots idle."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+
+    def pick(cols, code, rows=50000, x=a, y=b, causal=False):
+        return table[binding.softmax_select(x, y, cols, cols, code, rows=rows, causal=causal)].name
+
+    assert pick(1001, 2) == "any_packed_bf16_l64_v2_g1" and pick(33, 2) == "any_packed_bf16_l8_v1_g2"
+    assert pick(1001, 0) == "any_row_f32_w4_v2"
+    assert pick(4089, 2) == "any_row_bf16_w4_v2"      # 512 chunks: the aligned shape
+    assert pick(4097, 2) == "any_row_bf16_w4_v3"      # 513 chunks
+    assert pick(2049, 0) == "any_row_f32_w4_v3" and pick(4097, 0) == "any_row_f32_w8_v3"
+    assert pick(16385, 2) == "any_row_bf16_w16_v3" and pick(32001, 2) == "any_row_bf16_w8_v8"
+    assert pick(50257, 2) == "any_row_bf16_w16_v8"
+    assert pick(4097, 2, rows=64) == "any_rowpf_bf16_w4_v3"  # few rows: the persistent twin
+    assert pick(4097, 2, causal=True) == "causal_any_row_bf16_w4_v3"
+    assert pick(4096, 2, x=a + 2, y=b + 2) == "any_row_bf16_w4_v3"  # aligned width, pointers inside a chunk
+    assert pick(4096, 2) == "row_bf16_w4_v2"
+
+
+def test_wide_16bit_rows_take_sixteen_waves(lib):
+    """16-bit rows past 16384 columns: sixteen waves of four (up to 4096 chunks) or
+    eight (at least nine tenths of 8192 chunks) accesses, else the online kernel;
+    fp32 keeps four or eight waves of sixteen."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=2000,
+                                                                        causal=causal)].name
+    assert pick(24576, 2) == "row_bf16_w16_v4" and pick(32000, 1) == "row_f16_w16_v4"
+    assert pick(65536, 2) == "row_bf16_w16_v8" and pick(50304, 2) == "online_bf16_vec_w16_v2"
+    assert pick(32000, 2, causal=True) == "causal_row_bf16_w16_v4"
+    assert pick(16384, 2) == "row_bf16_w16_v2"  # 2048 chunks: the two-access rule
+    assert pick(32000, 0) == "row_f32_w8_v16" and pick(16384, 0) == "row_f32_w4_v16"
 
 
 def test_fp32_ragged_rule_follows_the_row_count(lib):

@@ -263,3 +263,14 @@ def test_split_crossover_summary(profile_dir, tmp_path):
     assert "| f32 | 4096 | 8 | 180.0 | 15.0 | 18.0 | split via out | 10.00 |" in text
     assert "| bf16 | 64 | 256 | 12.0 | 15.0 | 12.0 | table | 1.00 |" in text
     assert "--split-crossover --split-out" in text
+
+
+def test_odd_width_summary(profile_dir, tmp_path):
+    """Gains are softmax_fwd over the scalar path and over the aligned width below."""
+    rows = [{"dtype": "bf16", "rows": 24408, "cols": 4097, "aligned_cols": 4096, "kernel": "any_row_bf16_w4_v3",
+             "softmax_fwd": 5800.0, "scalar": 1700.0, "aligned_below": 5900.0}]
+    src = tmp_path / "odd.json"
+    src.write_text(json.dumps(rows))
+    bench.summarize_odd_widths(str(src))
+    text = (profile_dir / "odd_widths.md").read_text()
+    assert "| bf16 | 24408 | 4097 | any_row_bf16_w4_v3 | 5800 | 1700 | 3.41x | 5900 (4096) | 0.983 |" in text

@@ -63,13 +63,17 @@ def test_c2_causal_first_rows():
         assert np.all(y[i, i + 1:] == 0.0)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("width", list(W.SWEEP_WIDTHS))
-def test_sweep_full_size_every_row(dtype, width):
-    """Full-size sweep inputs (about 200 MB each) in the benchmark's launch
-    shape, compared with the oracle element by element over every row, plus
-    the value range and the row sums."""
-    wl = W.WORKLOADS[f"c5_{dtype}_{width}"]
+_FULL_KEYS = [f"c5_{dt}_{w}" for w in W.SWEEP_WIDTHS for dt in ("bf16", "f32")] + \
+             [f"vocab_{dt}_{w}" for dt, ws in W.VOCAB_WIDTHS.items() for w in ws]
+
+
+@pytest.mark.parametrize("key", _FULL_KEYS)
+def test_sweep_full_size_every_row(key):
+    """Full-size sweep and vocabulary-width inputs (about 200 MB each) in the
+    benchmark's launch shape, compared with the oracle element by element over
+    every row, plus the value range and the row sums."""
+    wl = W.WORKLOADS[key]
+    dtype = wl.dtype
     _say(f"sweep {wl.name}")
     x = wl.generate()
     y = run(x, dtype, prefill_out=False)
@@ -77,8 +81,8 @@ def test_sweep_full_size_every_row(dtype, width):
     yd = decode(y, dtype)
     assert np.all(yd >= 0.0) and np.all(yd <= 1.0)
     # fp32 row sums are held to 1e-5 inside check_every_row.  bf16: each output
-    # carries a relative rounding error of at most 2^-9, so the sum is within
-    # 2^-9 of 1 (2x margin).
+    # carries a relative rounding error of at most its unit roundoff 2^-8 (8
+    # significant bits, round to nearest), so the sum is within 2^-8 of 1.
     if dtype == "bf16":
         assert np.max(np.abs(yd.sum(axis=1) - 1.0)) <= 2.0 ** -8
     _say(f"sweep {wl.name} rows {wl.rows} max abs err {err:.3e}")
@@ -128,23 +132,35 @@ def test_in_place(dtype, cols):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_misaligned_pointer_takes_scalar_path(dtype):
+@pytest.mark.parametrize("out_shift", [1, 2])
+def test_misaligned_pointers(dtype, out_shift):
+    """Rows one element past a 16-byte boundary.  With the output at the same
+    offset (out_shift 1) the any-alignment kernels run; at another offset
+    (out_shift 2) the scalar path does."""
     import torch
-    _say(f"misaligned {dtype}")
+    _say(f"misaligned {dtype} out_shift={out_shift}")
     cols = 1000
     x = W.random_matrix(seed=25, rows=11, cols=cols + 1, dtype=dtype)
     xd = to_device(x, dtype)[:, 1:]            # starts one element past a 16-byte boundary
-    out_full = torch.empty((11, cols + 1), dtype=xd.dtype, device="cuda")
-    out = out_full[:, 1:]
+    out_full = torch.full((11 * (cols + 1) + 2,), float("nan"), dtype=xd.dtype, device="cuda")
+    out = out_full[out_shift:out_shift + 11 * (cols + 1)].view(11, cols + 1)[:, :cols]
     code = W.dtype_code(dtype)
     kid = binding.softmax_select(xd.data_ptr(), out.data_ptr(), cols, cols + 1, code, rows=11)
-    assert binding.kernel_table()[kid].vec_elems == 1
+    k = binding.kernel_table()[kid]
+    assert ("any_" in k.name) if out_shift == 1 else (k.vec_elems == 1)
     binding.softmax_fwd(xd.data_ptr(), out.data_ptr(), 11, cols, cols + 1, code,
                         torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    y = to_host(out_full, dtype)[:, 1:]
+    y = to_host(out, dtype)
     xs = np.ascontiguousarray(x[:, 1:])
     check(np.ascontiguousarray(y), xs, dtype, O.softmax(xs, dtype), label="misaligned")
+    # the gaps between rows, and the elements around the output, stay untouched
+    full = to_host(out_full, dtype).reshape(-1)
+    wrote = np.zeros(full.size, dtype=bool)
+    for r in range(11):
+        wrote[out_shift + r * (cols + 1): out_shift + r * (cols + 1) + cols] = True
+    rest = full[~wrote]
+    assert np.isnan(decode(rest, dtype)).all(), "an element outside the rows was written"
 
 
 def test_empty_inputs_launch_nothing():
@@ -217,6 +233,12 @@ _DT = {0: "f32", 1: "f16", 2: "bf16"}
 
 def _widths_for(k):
     n = k.vec_elems
+    if "any_" in k.name:  # odd widths: consecutive rows start at every offset within a chunk
+        if k.max_cols > 0:
+            m = k.max_cols
+            return sorted({w for w in (m, m - 2, (m // 2) | 1, 1, 3) if 1 <= w <= m})
+        chunk = k.lanes * k.vecs_per_lane * n
+        return sorted({1, chunk + 1, 2 * chunk + 3 * n + 1})
     if k.max_cols > 0:
         m = k.max_cols
         ws = {m, max(n, m - n), max(n, (m // 2 // n) * n + n), n}
