@@ -653,14 +653,14 @@ def summarize_trace(stats_csv):
            "bench.py launches each kernel and shape untimed for 0.3 s (clock spin-up), then 50 warm-up + 200 timed"
            " launches, over rotating buffer sets of at least 1 GiB; the averages below cover all of them.",
            "Kernels, by template arguments `<element, elements per access, waves per row, accesses per lane, causal,"
-           " line shift>`:",
+           " line shift, any alignment>`:",
            "",
-           "- `softmax_row_pf<F32,4,4,1,false,true>`: c1 128x1000 fp32 (4000-byte rows, line-shifted; few rows:"
+           "- `softmax_row_pf<F32,4,4,1,false,true,false>`: c1 128x1000 fp32 (4000-byte rows, line-shifted; few rows:"
            " the persistent twin);",
-           "- `softmax_row_pf<F32,4,4,2,false,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
-           "- `softmax_row_pf<F32,4,4,2,true,false>`: c2 with the mask and 1/8 scale fused (raw scores in);",
-           "- `softmax_row<F16,8,4,2,false,false>`: c3 8192x4096 fp16 (the headline);",
-           "- `softmax_row<F32,4,8,2,false,false>`: c4 4096x4096 fp32;",
+           "- `softmax_row_pf<F32,4,4,2,false,false,false>`: c2 2048x2048 fp32 (mask written in as -inf);",
+           "- `softmax_row_pf<F32,4,4,2,true,false,false>`: c2 with the mask and 1/8 scale fused (raw scores in);",
+           "- `softmax_row<F16,8,4,2,false,false,false>`: c3 8192x4096 fp16 (the headline);",
+           "- `softmax_row<F32,4,8,2,false,false,false>`: c4 4096x4096 fp32;",
            "- `softmax_packed<...>` and `softmax_row<...>` at the 24 width-sweep tensors (c5), each once per width;",
            "- `copy16<4>` and `__amd_rocclr_copyBuffer`: the same-size copy references, for every shape; `copy16<4>`,"
            " `read16<4>` and `write16<4>` also at 8 MiB-1 GiB (the copy-ceiling table);",
