@@ -1000,6 +1000,80 @@ def summarize_split_crossover(json_path: str) -> None:
     print("\n".join(out))
 
 
+RAGGED_WIDTHS = {"f32": (600, 900, 960, 1000, 1020), "bf16": (1200, 1800, 2000, 2040)}
+RAGGED_ROWS = (2048, 4096, 8192, 16384, 65536)
+RAGGED_SHAPES = ("row_{}_w4_v1", "rowpf_{}_w4_v1", "row_{}_w2_v2", "rowpf_{}_w2_v2", "row_{}_w4_v2")
+
+
+def ragged_rows(steps: int, warmup: int) -> list:
+    """Ragged widths of 129..255 16-byte accesses (aligned, contiguous) at
+    2 K-64 K rows: softmax_fwd and each candidate row shape forced (four waves
+    of one access, two of two, four of two; plain and persistent).  Seeded
+    N(0, 1) inputs drawn on the device, rotating buffers of at least 1 GiB,
+    the best of three interleaved timings each."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    table = binding.kernel_table()
+    ids = {k.name: k.kid for k in table}
+    out = []
+    for dt, widths in RAGGED_WIDTHS.items():
+        code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
+        for cols in widths:
+            for rows in RAGGED_ROWS:
+                nbytes = rows * cols * esz
+                n = n_buffers(2 * nbytes)
+                g = torch.Generator(device="cuda").manual_seed(cols * 7 + rows)
+                xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
+                ys = [torch.empty_like(x) for x in xs]
+                kid = binding.softmax_select(xs[0].data_ptr(), ys[0].data_ptr(), cols, cols, code, rows=rows)
+                runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols,
+                                                                     cols, code, stream)}
+                for shape in RAGGED_SHAPES:
+                    k = ids[shape.format(dt)]
+                    runs[shape.format(dt)] = (lambda k: lambda i: binding.softmax_fwd_kernel(
+                        k, xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols, code, stream))(k)
+                best = {k: 0.0 for k in runs}
+                for _ in range(3):
+                    for k, f in runs.items():
+                        ms = time_launches(f, n, steps, warmup, spin_s=0.02)
+                        best[k] = max(best[k], 2 * nbytes / (ms * 1e-3) / 1e9)
+                r = {"dtype": dt, "rows": rows, "cols": cols, "accesses": cols * esz // 16,
+                     "kernel": table[kid].name, **{k: round(v, 1) for k, v in best.items()}}
+                log(f"[bench] ragged {dt} {rows}x{cols}: {r}")
+                out.append(r)
+                del xs, ys
+                torch.cuda.empty_cache()
+    return out
+
+
+def summarize_ragged_rows(json_path: str) -> None:
+    """Write profiles/ragged_widths_rows.md from `bench.py --ragged-rows --ragged-out` JSON."""
+    rows = json.load(open(json_path))
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    heads = [s.format("dt").replace("_dt_", " ").replace("_", "") for s in RAGGED_SHAPES]
+    out = ["# Ragged widths (129..255 16-byte accesses) across row counts, MI355X (gfx950)", "",
+           "Commands (repository root):", "",
+           f"    python3 bench.py --ragged-rows --ragged-out {src}",
+           f"    python3 bench.py --summarize-ragged-rows {src}", "",
+           "Contiguous tensors of widths a multiple of 16 bytes, seeded N(0, 1) inputs, rotating buffers of at",
+           "least 1 GiB, best of three interleaved timings; GB/s by the metric's 2·rows·cols·size bytes.  The",
+           "shape columns force one kernel (`w4v1`: four waves of one 16-byte access per lane, `w2v2`: two",
+           "waves of two, `w4v2`: four waves of two; `rowpf`: the persistent twin).  `pick / best`: softmax_fwd",
+           "against the fastest column of its line.", "",
+           "| dtype | cols | accesses | rows | pick | softmax_fwd | " + " | ".join(heads) + " | pick / best |",
+           "|---|---|---|---|---|---|" + "---|" * len(heads) + "---|"]
+    for r in rows:
+        vals = [r[s.format(r["dtype"])] for s in RAGGED_SHAPES]
+        best = max(vals + [r["softmax_fwd"]])
+        out.append(f"| {r['dtype']} | {r['cols']} | {r['accesses']} | {r['rows']} | {r['kernel']} | "
+                   f"{r['softmax_fwd']:.0f} | " + " | ".join(f"{v:.0f}" for v in vals) +
+                   f" | {r['softmax_fwd'] / best:.3f} |")
+    path = os.path.join(PROFILE_DIR, "ragged_widths_rows.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 ODD_WIDTHS = {"f32": (1001, 1025, 2049, 3001, 4097, 8193, 16385, 32001, 50257),
               "bf16": (1001, 2049, 4097, 8193, 16385, 32001, 50257)}
 
@@ -1385,6 +1459,11 @@ def main() -> int:
     ap.add_argument("--odd-out", default=None, help="JSON file for --odd-widths")
     ap.add_argument("--summarize-odd-widths", metavar="JSON", default=None,
                     help="write profiles/odd_widths.md from --odd-widths JSON and exit")
+    ap.add_argument("--ragged-rows", action="store_true",
+                    help="time ragged widths (129..255 accesses) at 2 K-64 K rows: the pick and each candidate shape")
+    ap.add_argument("--ragged-out", default=None, help="JSON file for --ragged-rows")
+    ap.add_argument("--summarize-ragged-rows", metavar="JSON", default=None,
+                    help="write profiles/ragged_widths_rows.md from --ragged-rows JSON and exit")
     ap.add_argument("--split-crossover", action="store_true",
                     help="time one workgroup per row, the split path and softmax_fwd on few, very wide rows")
     ap.add_argument("--split-out", default=None, help="JSON file for --split-crossover")
@@ -1415,6 +1494,9 @@ def main() -> int:
         return 0
     if args.summarize_split_crossover:
         summarize_split_crossover(args.summarize_split_crossover)
+        return 0
+    if args.summarize_ragged_rows:
+        summarize_ragged_rows(args.summarize_ragged_rows)
         return 0
     if args.summarize_chunk_copy:
         summarize_chunk_copy(*args.summarize_chunk_copy[:2])
@@ -1478,6 +1560,12 @@ def main() -> int:
         table = odd_widths(args.steps, args.warmup)
         if args.odd_out:
             with open(args.odd_out, "w") as f:
+                json.dump(table, f, indent=1)
+        return 0
+    if args.ragged_rows:
+        table = ragged_rows(args.steps, args.warmup)
+        if args.ragged_out:
+            with open(args.ragged_out, "w") as f:
                 json.dump(table, f, indent=1)
         return 0
     if args.split_crossover:

@@ -126,9 +126,9 @@ int pow2_at_least(int64_t v) {
 // The width dispatch rule, set from the width sweep (bench.py --sweep, bf16
 // and fp32, widths 32 ... 16384 at about 200 MB per tensor): up to 2048
 // 16-byte accesses per row the fastest shape keeps about two loads in flight
-// per lane and spreads the row over as many lanes as that takes (ragged rows
-// of 129..255 accesses excepted, see below); wider rows do best on four waves
-// with more loads each.  `nacc` is the row length in 16-byte accesses (for
+// per lane and spreads the row over as many lanes as that takes (with a few
+// measured exceptions for ragged rows of 129..255 accesses, see below);
+// wider rows do best on four waves with more loads each.  `nacc` is the row length in 16-byte accesses (for
 // rows at any element offset, the most chunks a row can touch).  The causal
 // table, and the any-alignment entries (any = true), hold the same picks.
 const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t nacc) {
@@ -140,16 +140,27 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
     } else if (nacc <= 128) {
         e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1, any);
     } else if (nacc <= 2048) {
-        // ragged rows of 129..255 accesses: four waves of one access each
-        // (1000 fp32 columns: 6226 GB/s, against 5915 for two waves of two;
-        // at exactly 256 accesses the two-wave shape stays ahead).  fp32
-        // tensors of 8192 rows or more take two accesses per lane on the
-        // same four waves, half the slots idle: 0.5-5% faster at 520, 600,
-        // 700, 800 and 1000 columns with 8 K-49 K rows, but up to 4%
-        // slower with 1 K rows, and 15-25% slower for bf16 at any count.
+        // Ragged rows of 129..255 accesses take the general two-wave shape
+        // below (bf16 1200 columns x 64 K rows: 5650 GB/s, against 4590 on
+        // four waves of one; fp32 600 columns: 6026 against 4934 on four
+        // waves of two), with three exceptions measured across 2 K-64 K
+        // rows.  fp32 rows of 240 accesses or more (960 columns), from 8192
+        // rows on: four waves of two, half the slots idle (1000 columns x
+        // 64 K rows: 6409 against 6287).  16-bit rows below 4096 rows,
+        // where two waves per row fill less than one round of the chip's
+        // wave slots: four waves of one, twice the waves in flight (bf16
+        // 2048 x 1200: 2119 against 2045).  16-bit rows of more than 250
+        // accesses past 8192 rows: four waves of one, whose 512 slots hold
+        // the line shift that 256 cannot (bf16 2040 columns x 64 K rows:
+        // 5921 against 5466).
         if (nacc < 256) {
-            const int v = dtype == SOFTMAX_F32 && rows >= 8192 ? 2 : 1;
-            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, v, 1, any);
+            int v = 0;
+            if (dtype == SOFTMAX_F32) {
+                if (nacc >= 240 && rows >= 8192) v = 2;
+            } else if (rows < 4096 || (nacc > 250 && rows > 8192)) {
+                v = 1;
+            }
+            if (v > 0) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, v, 1, any);
         }
         // otherwise one workgroup per row, two accesses per lane, up to 16
         // waves (2048 accesses, 16384 bf16 columns: 6150 GB/s on sixteen

@@ -255,7 +255,7 @@ def test_attention_argument_errors(lib):
 # those workloads' row counts (the "pick" column of the measured sweep); a
 # change to the rule must change this table knowingly.
 _PICKS = {
-    "c1": "rowpf_f32_w4_v1", "c2": "rowpf_f32_w4_v2", "c3": "row_f16_w4_v2", "c4": "row_f32_w8_v2",
+    "c1": "rowpf_f32_w2_v2", "c2": "rowpf_f32_w4_v2", "c3": "row_f16_w4_v2", "c4": "row_f32_w8_v2",
     "c5_bf16_32": "packed_bf16_l4_v1_g2", "c5_bf16_64": "packed_bf16_l8_v1_g2", "c5_bf16_128": "packed_bf16_l16_v1_g2",
     "c5_bf16_256": "packed_bf16_l32_v1_g2", "c5_bf16_512": "packed_bf16_l64_v1_g2",
     "c5_bf16_1000": "packed_bf16_l64_v2_g1", "c5_bf16_1024": "packed_bf16_l64_v2_g1", "c5_bf16_2048": "row_bf16_w2_v2",
@@ -360,14 +360,22 @@ def test_wide_16bit_rows_take_sixteen_waves(lib):
     assert pick(32000, 0) == "row_f32_w8_v16" and pick(16384, 0) == "row_f32_w4_v16"
 
 
-def test_fp32_ragged_rule_follows_the_row_count(lib):
-    """Ragged fp32 rows of 129..255 accesses: one access per lane below 8192
-    rows, two from 8192 rows on; bf16 keeps one at any count."""
+def test_ragged_rule_follows_the_row_count(lib):
+    """Ragged rows of 129..255 accesses: two waves of two accesses, except fp32
+    rows of 240 accesses or more from 8192 rows on (four waves of two), and
+    16-bit rows below 4096 rows or of more than 250 accesses past 8192 rows
+    (four waves of one); up to 8192 rows the two-wave shape runs as its
+    persistent twin."""
     a, b = 1 << 40, 1 << 41
     names = lambda cols, code, rows: binding.kernel_table()[binding.softmax_select(a, b, cols, cols, code,
                                                                                       rows=rows)].name
-    assert names(1000, 0, 8191) == "row_f32_w4_v1" and names(1000, 0, 8192) == "row_f32_w4_v2"
-    assert names(2000, 2, 8191) == "row_bf16_w4_v1" and names(2000, 2, 100000) == "row_bf16_w4_v1"
+    assert names(1000, 0, 8191) == "rowpf_f32_w2_v2" and names(1000, 0, 8192) == "row_f32_w4_v2"
+    assert names(956, 0, 100000) == "row_f32_w2_v2"  # 239 accesses
+    assert names(1000, 0, 4096) == "rowpf_f32_w2_v2" and names(600, 0, 100000) == "row_f32_w2_v2"
+    assert names(2000, 2, 4095) == "rowpf_bf16_w4_v1" and names(2000, 2, 4096) == "rowpf_bf16_w2_v2"
+    assert names(2000, 2, 100000) == "row_bf16_w2_v2" and names(2008, 2, 100000) == "row_bf16_w4_v1"
+    assert names(2008, 2, 8192) == "rowpf_bf16_w2_v2" and names(2008, 1, 8193) == "row_f16_w4_v1"
+    assert names(2048, 2, 100000) == "row_bf16_w2_v2"  # 256 accesses: the general rule
 
 
 # ----------------------------------------------- torch-level argument checks

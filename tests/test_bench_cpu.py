@@ -274,3 +274,17 @@ def test_odd_width_summary(profile_dir, tmp_path):
     bench.summarize_odd_widths(str(src))
     text = (profile_dir / "odd_widths.md").read_text()
     assert "| bf16 | 24408 | 4097 | any_row_bf16_w4_v3 | 5800 | 1700 | 3.41x | 5900 (4096) | 0.983 |" in text
+
+
+def test_ragged_rows_summary(profile_dir, tmp_path):
+    """One line per (width, rows): the pick, every forced shape, and the pick
+    against the fastest of them."""
+    r = {"dtype": "bf16", "rows": 65536, "cols": 2040, "accesses": 255, "kernel": "row_bf16_w4_v1",
+         "softmax_fwd": 5900.0, "row_bf16_w4_v1": 5910.0, "rowpf_bf16_w4_v1": 4960.0, "row_bf16_w2_v2": 5466.0,
+         "rowpf_bf16_w2_v2": 4793.0, "row_bf16_w4_v2": 5166.0}
+    src = tmp_path / "ragged.json"
+    src.write_text(json.dumps([r]))
+    bench.summarize_ragged_rows(str(src))
+    text = (profile_dir / "ragged_widths_rows.md").read_text()
+    assert "| row w4v1 | rowpf w4v1 | row w2v2 | rowpf w2v2 | row w4v2 | pick / best |" in text
+    assert "| bf16 | 2040 | 255 | 65536 | row_bf16_w4_v1 | 5900 | 5910 | 4960 | 5466 | 4793 | 5166 | 0.998 |" in text
