@@ -1074,6 +1074,80 @@ def summarize_ragged_rows(json_path: str) -> None:
     print("\n".join(out))
 
 
+FEW_ROWS_WIDTHS = {"f32": (1024, 2048, 4096, 8192), "bf16": (2048, 4096, 8192, 16384)}
+FEW_ROWS = (256, 512, 1024, 2048, 4096)
+
+
+def few_rows(steps: int, warmup: int) -> list:
+    """Jobs of few rows (256-4096) at aligned widths of 4-32 KiB: softmax_fwd
+    and every persistent row shape (the twin family) whose slots hold the row
+    at most twice over, each forced.  Seeded N(0, 1) inputs drawn on the device,
+    rotating buffers of at least 1 GiB, the best of three interleaved timings."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    table = binding.kernel_table()
+    out = []
+    for dt, widths in FEW_ROWS_WIDTHS.items():
+        code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
+        for cols in widths:
+            for rows in FEW_ROWS:
+                nbytes = rows * cols * esz
+                n = n_buffers(2 * nbytes)
+                g = torch.Generator(device="cuda").manual_seed(cols * 11 + rows)
+                xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
+                ys = [torch.empty_like(x) for x in xs]
+                x0, y0 = xs[0].data_ptr(), ys[0].data_ptr()
+                kid = binding.softmax_select(x0, y0, cols, cols, code, rows=rows)
+                runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols,
+                                                                     cols, code, stream)}
+                for k in table:
+                    if (k.dtype == code and k.variant == "row_pf" and not k.causal and not k.name.startswith("any_")
+                            and k.max_cols <= 2 * cols and binding.kernel_fits(k.kid, x0, y0, cols, cols, code)):
+                        runs[k.name] = (lambda kk: lambda i: binding.softmax_fwd_kernel(
+                            kk, xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols, code, stream))(k.kid)
+                best = {k: 0.0 for k in runs}
+                for _ in range(3):
+                    for k, f in runs.items():
+                        ms = time_launches(f, n, steps, warmup, spin_s=0.02)
+                        best[k] = max(best[k], 2 * nbytes / (ms * 1e-3) / 1e9)
+                r = {"dtype": dt, "rows": rows, "cols": cols, "kernel": table[kid].name,
+                     "gbps": {k: round(v, 1) for k, v in best.items()}}
+                log(f"[bench] few rows {dt} {rows}x{cols}: {r}")
+                out.append(r)
+                del xs, ys
+                torch.cuda.empty_cache()
+    return out
+
+
+def summarize_few_rows(json_path: str) -> None:
+    """Write profiles/few_rows_shapes.md from `bench.py --few-rows --few-out` JSON."""
+    rows = json.load(open(json_path))
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    out = ["# Few rows: the persistent row shapes at 256-4096 rows, MI355X (gfx950)", "",
+           "Commands (repository root):", "",
+           f"    python3 bench.py --few-rows --few-out {src}",
+           f"    python3 bench.py --summarize-few-rows {src}", "",
+           "Contiguous tensors, seeded N(0, 1) inputs, rotating buffers of at least 1 GiB, best of three interleaved",
+           "timings; GB/s by the metric's 2·rows·cols·size bytes.  Each persistent row shape (`rowpf_<dtype>_w<W>_v<V>`:",
+           "W waves per row, V 16-byte accesses per lane, grid = resident workgroups) whose slots hold the row at most",
+           "twice over is forced; `pick / best` is softmax_fwd against the fastest of them (or itself).", "",
+           "| dtype | cols | rows | pick | softmax_fwd GB/s | best shape | best GB/s | pick / best | next three |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        g = dict(r["gbps"])
+        pick = g.pop("softmax_fwd")
+        ranked = sorted(g.items(), key=lambda kv: -kv[1])
+        bname, bval = ranked[0] if ranked else ("-", 0.0)
+        top = max(bval, pick)
+        nxt = ", ".join(f"{k.split('_', 2)[2]} {v:.0f}" for k, v in ranked[1:4])
+        out.append(f"| {r['dtype']} | {r['cols']} | {r['rows']} | {r['kernel']} | {pick:.0f} | {bname} | {bval:.0f} | "
+                   f"{pick / top:.3f} | {nxt} |")
+    path = os.path.join(PROFILE_DIR, "few_rows_shapes.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 ODD_WIDTHS = {"f32": (1001, 1025, 2049, 3001, 4097, 8193, 16385, 32001, 50257),
               "bf16": (1001, 2049, 4097, 8193, 16385, 32001, 50257)}
 
@@ -1459,6 +1533,11 @@ def main() -> int:
     ap.add_argument("--odd-out", default=None, help="JSON file for --odd-widths")
     ap.add_argument("--summarize-odd-widths", metavar="JSON", default=None,
                     help="write profiles/odd_widths.md from --odd-widths JSON and exit")
+    ap.add_argument("--few-rows", action="store_true",
+                    help="time jobs of 256-4096 rows: softmax_fwd and every persistent row shape that fits")
+    ap.add_argument("--few-out", default=None, help="JSON file for --few-rows")
+    ap.add_argument("--summarize-few-rows", metavar="JSON", default=None,
+                    help="write profiles/few_rows_shapes.md from --few-rows JSON and exit")
     ap.add_argument("--ragged-rows", action="store_true",
                     help="time ragged widths (129..255 accesses) at 2 K-64 K rows: the pick and each candidate shape")
     ap.add_argument("--ragged-out", default=None, help="JSON file for --ragged-rows")
@@ -1494,6 +1573,9 @@ def main() -> int:
         return 0
     if args.summarize_split_crossover:
         summarize_split_crossover(args.summarize_split_crossover)
+        return 0
+    if args.summarize_few_rows:
+        summarize_few_rows(args.summarize_few_rows)
         return 0
     if args.summarize_ragged_rows:
         summarize_ragged_rows(args.summarize_ragged_rows)
@@ -1560,6 +1642,12 @@ def main() -> int:
         table = odd_widths(args.steps, args.warmup)
         if args.odd_out:
             with open(args.odd_out, "w") as f:
+                json.dump(table, f, indent=1)
+        return 0
+    if args.few_rows:
+        table = few_rows(args.steps, args.warmup)
+        if args.few_out:
+            with open(args.few_out, "w") as f:
                 json.dump(table, f, indent=1)
         return 0
     if args.ragged_rows:

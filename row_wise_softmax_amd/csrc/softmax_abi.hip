@@ -114,8 +114,9 @@ bool aligned16(const void* in, const void* out, int64_t cols, int64_t row_stride
            (cols * esz) % 16 == 0;
 }
 
-// Two rounds of the chip's wave slots: 256 CUs x 4 SIMDs x 8 waves, twice.
-constexpr int64_t kFewRowWaves = 2 * 256 * 4 * 8;
+// One round of the chip's wave slots (256 CUs x 4 SIMDs x 8 waves), and two.
+constexpr int64_t kOneRoundWaves = 256 * 4 * 8;
+constexpr int64_t kFewRowWaves = 2 * kOneRoundWaves;
 
 int pow2_at_least(int64_t v) {
     int p = 1;
@@ -146,18 +147,16 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // waves of two), with three exceptions measured across 2 K-64 K
         // rows.  fp32 rows of 240 accesses or more (960 columns), from 8192
         // rows on: four waves of two, half the slots idle (1000 columns x
-        // 64 K rows: 6409 against 6287).  16-bit rows below 4096 rows,
-        // where two waves per row fill less than one round of the chip's
-        // wave slots: four waves of one, twice the waves in flight (bf16
-        // 2048 x 1200: 2119 against 2045).  16-bit rows of more than 250
+        // 64 K rows: 6409 against 6287).  16-bit rows of more than 250
         // accesses past 8192 rows: four waves of one, whose 512 slots hold
         // the line shift that 256 cannot (bf16 2040 columns x 64 K rows:
-        // 5921 against 5466).
+        // 5921 against 5466).  (16-bit jobs of few rows take four waves of
+        // one by the one-round rule below.)
         if (nacc < 256) {
             int v = 0;
             if (dtype == SOFTMAX_F32) {
                 if (nacc >= 240 && rows >= 8192) v = 2;
-            } else if (rows < 4096 || (nacc > 250 && rows > 8192)) {
+            } else if (nacc > 250 && rows > 8192) {
                 v = 1;
             }
             if (v > 0) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 4, v, 1, any);
@@ -185,6 +184,15 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         if (e != nullptr && rows * (e->lanes / 64) <= kFewRowWaves) {
             const Entry* pf = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, e->lanes, e->vpl, 1, any);
             if (pf != nullptr) e = pf;
+        }
+        // 16-bit jobs that twice the waves, one access each, still hold in
+        // one round: the twin on those, for twice the rows' loads issued at
+        // once (bf16, 256-2048 rows of 2048-8192 columns: 0.5-13% faster;
+        // 512 x 2048: 1048 -> 1188 GB/s).  At two rounds it is 9-16% slower.
+        if (e != nullptr && e->variant == SOFTMAX_VARIANT_ROW_PF && elem_bytes(dtype) == 2 && e->vpl == 2 &&
+            rows * (2 * e->lanes / 64) <= kOneRoundWaves) {
+            const Entry* one = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, 2 * e->lanes, 1, 1, any);
+            if (one != nullptr) e = one;
         }
     } else if (elem_bytes(dtype) == 2) {
         // 16-bit rows past 2048 chunks (16384 columns) hold 8 values per

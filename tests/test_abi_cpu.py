@@ -291,6 +291,24 @@ def test_few_rows_take_the_persistent_twin(lib):
     assert pick(16384, 0, 16) == "row_f32_w4_v16"  # rows past the register-resident two-access shapes keep theirs
 
 
+def test_few_16bit_rows_take_one_access_on_twice_the_waves(lib):
+    """16-bit jobs whose rows, on twice the twin's waves, fit one round of the
+    8192 wave slots take the persistent shape of one access per lane, plain and
+    causal; fp32 keeps the twin."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
+                                                                               causal=causal)].name
+    assert pick(2048, 2, 2048) == "rowpf_bf16_w4_v1" and pick(2048, 2, 2049) == "rowpf_bf16_w2_v2"
+    assert pick(4096, 1, 1024) == "rowpf_f16_w8_v1" and pick(4096, 1, 1025) == "rowpf_f16_w4_v2"
+    assert pick(8192, 2, 512) == "rowpf_bf16_w16_v1" and pick(8192, 2, 513) == "rowpf_bf16_w8_v2"
+    assert pick(16384, 2, 256) == "rowpf_bf16_w16_v2"      # no thirty-two-wave shape
+    assert pick(2048, 0, 512) == "rowpf_f32_w4_v2"         # fp32 keeps the twin
+    assert pick(2048, 2, 2048, causal=True) == "causal_rowpf_bf16_w4_v1"
+    assert pick(4096, 2, 1024, causal=True) == "causal_rowpf_bf16_w8_v1"
+    assert pick(4097, 2, 64) == "any_rowpf_bf16_w4_v3"    # three accesses: the twin as it is
+
+
 def test_few_very_wide_rows_split_through_the_output(lib):
     """softmax_fwd splits few, very wide rows out of place on the 16-byte path,
     by the measured (row bytes, most rows) lines; anything else takes the
@@ -363,16 +381,16 @@ def test_wide_16bit_rows_take_sixteen_waves(lib):
 def test_ragged_rule_follows_the_row_count(lib):
     """Ragged rows of 129..255 accesses: two waves of two accesses, except fp32
     rows of 240 accesses or more from 8192 rows on (four waves of two), and
-    16-bit rows below 4096 rows or of more than 250 accesses past 8192 rows
-    (four waves of one); up to 8192 rows the two-wave shape runs as its
-    persistent twin."""
+    16-bit rows of more than 250 accesses past 8192 rows (four waves of one);
+    up to 8192 rows the two-wave shape runs as its persistent twin, and 16-bit
+    jobs of at most 2048 rows take four waves of one (the one-round rule)."""
     a, b = 1 << 40, 1 << 41
     names = lambda cols, code, rows: binding.kernel_table()[binding.softmax_select(a, b, cols, cols, code,
                                                                                       rows=rows)].name
     assert names(1000, 0, 8191) == "rowpf_f32_w2_v2" and names(1000, 0, 8192) == "row_f32_w4_v2"
     assert names(956, 0, 100000) == "row_f32_w2_v2"  # 239 accesses
     assert names(1000, 0, 4096) == "rowpf_f32_w2_v2" and names(600, 0, 100000) == "row_f32_w2_v2"
-    assert names(2000, 2, 4095) == "rowpf_bf16_w4_v1" and names(2000, 2, 4096) == "rowpf_bf16_w2_v2"
+    assert names(2000, 2, 2048) == "rowpf_bf16_w4_v1" and names(2000, 2, 2049) == "rowpf_bf16_w2_v2"
     assert names(2000, 2, 100000) == "row_bf16_w2_v2" and names(2008, 2, 100000) == "row_bf16_w4_v1"
     assert names(2008, 2, 8192) == "rowpf_bf16_w2_v2" and names(2008, 1, 8193) == "row_f16_w4_v1"
     assert names(2048, 2, 100000) == "row_bf16_w2_v2"  # 256 accesses: the general rule

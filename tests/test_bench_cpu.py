@@ -288,3 +288,16 @@ def test_ragged_rows_summary(profile_dir, tmp_path):
     text = (profile_dir / "ragged_widths_rows.md").read_text()
     assert "| row w4v1 | rowpf w4v1 | row w2v2 | rowpf w2v2 | row w4v2 | pick / best |" in text
     assert "| bf16 | 2040 | 255 | 65536 | row_bf16_w4_v1 | 5900 | 5910 | 4960 | 5466 | 4793 | 5166 | 0.998 |" in text
+
+
+def test_few_rows_summary(profile_dir, tmp_path):
+    """The best forced persistent shape, softmax_fwd against it, and the next three."""
+    r = {"dtype": "bf16", "rows": 512, "cols": 2048, "kernel": "rowpf_bf16_w4_v1",
+         "gbps": {"softmax_fwd": 1180.0, "rowpf_bf16_w4_v1": 1188.0, "rowpf_bf16_w2_v2": 1048.0,
+                  "rowpf_bf16_w8_v1": 1148.0, "rowpf_bf16_w4_v2": 1031.0, "rowpf_bf16_w1_v4": 878.0}}
+    src = tmp_path / "few.json"
+    src.write_text(json.dumps([r]))
+    bench.summarize_few_rows(str(src))
+    text = (profile_dir / "few_rows_shapes.md").read_text()
+    assert ("| bf16 | 2048 | 512 | rowpf_bf16_w4_v1 | 1180 | rowpf_bf16_w4_v1 | 1188 | 0.993 | "
+            "w8_v1 1148, w2_v2 1048, w4_v2 1031 |") in text
