@@ -320,30 +320,33 @@ bool coef_of(float scale, float* coef) {
     return *coef > 0.0f;
 }
 
-// Workgroups of entry `e` the current device holds at once (occupancy per CU
-// x CU count), cached per device and kernel.  Used to size persistent grids.
+// Workgroups of entry `e`'s kernel `fn` (its plain or its line-shifted
+// instantiation, whose register counts, and so occupancy, can differ) the
+// current device holds at once (occupancy per CU x CU count), cached per
+// device, kernel and instantiation.  Used to size persistent grids.
 constexpr int kMaxDevices = 64;
 constexpr int kMaxKernels = 1024;
-std::atomic<int> g_resident[kMaxDevices][kMaxKernels];  // 0 = not yet known
+std::atomic<int> g_resident[kMaxDevices][2][kMaxKernels];  // 0 = not yet known
 
-int64_t resident_workgroups(const Entry& e, int block) {
+int64_t resident_workgroups(const Entry& e, const void* fn, int block) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = -1;
     const int id = id_of(&e);
+    const int shifted = fn == e.fn ? 0 : 1;
     const bool cacheable = dev >= 0 && dev < kMaxDevices && id >= 0 && id < kMaxKernels;
     if (cacheable) {
-        const int known = g_resident[dev][id].load(std::memory_order_relaxed);
+        const int known = g_resident[dev][shifted][id].load(std::memory_order_relaxed);
         if (known > 0) return known;
     }
     int per_cu = 0, cus = 0;
-    if (dev < 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, e.fn, block, 0) != hipSuccess ||
+    if (dev < 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
         cus <= 0) {
         (void)hipGetLastError();
         return 256 * 4;  // a safe default: the kernel loops over whatever rows remain
     }
     const int n = per_cu * cus;
-    if (cacheable) g_resident[dev][id].store(n, std::memory_order_relaxed);
+    if (cacheable) g_resident[dev][shifted][id].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -382,6 +385,7 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     a.nacc = int(e.any ? (cols + 2 * e.vec - 2) / e.vec : cols / e.vec);
     a.cols = int(cols);
     a.coef = coef;
+    const void* fn = (e.fn_shifted != nullptr && line_shift_fits(e, out, cols, row_stride)) ? e.fn_shifted : e.fn;
     int block;
     if (e.variant == SOFTMAX_VARIANT_PACKED) {
         const int64_t rows_per_wave = int64_t(64 / e.lanes) * e.groups;
@@ -392,7 +396,7 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
         a.nblocks = (waves + wpb - 1) / wpb;
     } else if (e.variant == SOFTMAX_VARIANT_ROW_PF) {
         block = e.block;
-        const int64_t res = resident_workgroups(e, block);
+        const int64_t res = resident_workgroups(e, fn, block);
         a.nblocks = rows < res ? rows : res;
     } else {
         block = e.block;
@@ -400,7 +404,6 @@ int launch(const Entry& e, const void* in, void* out, int64_t rows, int64_t cols
     }
     const int64_t grid = a.nblocks < kMaxGrid ? a.nblocks : kMaxGrid;
     void* args[] = {&a};
-    const void* fn = (e.fn_shifted != nullptr && line_shift_fits(e, out, cols, row_stride)) ? e.fn_shifted : e.fn;
     hipError_t rc = hipLaunchKernel(fn, dim3(unsigned(grid)), dim3(unsigned(block)), args, 0, stream);
     if (rc != hipSuccess) {
         (void)hipGetLastError();  // do not leave our failure for the caller's next check
