@@ -121,7 +121,8 @@ def test_large_scale_and_huge_values():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape,diag", [((2, 3, 100, 100), 0), ((4, 5, 40, 40), 3), ((2, 2, 300, 320), 20),
-                                        ((1, 2, 64, 4096), 4032), ((3, 1, 1000, 1000), -5)])
+                                        ((1, 2, 64, 4096), 4032), ((3, 1, 1000, 1000), -5),
+                                        ((2, 3, 37, 53), 5)])  # odd width: every row at another chunk offset
 def test_batched_causal_masks_each_matrix(dtype, shape, diag):
     """softmax_fwd_causal_batched: every matrix of [b][h][n][m] scores masked on
     its own row index, against the oracle run matrix by matrix; the torch call
