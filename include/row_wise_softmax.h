@@ -73,6 +73,7 @@ extern "C" {
 #define SOFTMAX_VARIANT_ROW 1    /* one workgroup per row, row held in registers (single pass) */
 #define SOFTMAX_VARIANT_ONLINE 2 /* one workgroup per row, two reads + one write (any width) */
 #define SOFTMAX_VARIANT_ROW_PF 3 /* row kernel, persistent: each workgroup loops over rows and prefetches the next */
+#define SOFTMAX_VARIANT_ROW16 4  /* 16-bit types: one workgroup per row, the row kept in registers as stored (wide rows) */
 
 /*
  * softmax_fwd -- the fused row softmax, with the library's width dispatch.
@@ -103,7 +104,7 @@ extern "C" {
  * keep only `rows` of the 256 compute units busy.  The measured lines: fp32
  * rows of >= 2 MiB up to 192 rows, >= 1 MiB up to 128, >= 512 KiB up to 64,
  * >= 256 KiB up to 16; fp16 / bf16 rows of >= 2 MiB up to 256 rows, >= 1 MiB
- * up to 192, >= 256 KiB up to 128, >= 128 KiB up to 64.  Results are
+ * up to 192, >= 512 KiB up to 128, >= 256 KiB up to 64.  Results are
  * bit-identical to softmax_fwd_split's.
  */
 int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
@@ -181,7 +182,7 @@ int softmax_select(const void *in, const void *out, int64_t rows, int64_t cols, 
  * size, the way the width sweep of "GPU Kernels - Implementing and
  * optimizing Softmax" (sections "CUDA scaling threads" and "Autotuning")
  * forces a block size per width:
- *   variant  SOFTMAX_VARIANT_PACKED, _ROW, _ONLINE or _ROW_PF;
+ *   variant  SOFTMAX_VARIANT_PACKED, _ROW, _ONLINE, _ROW_PF or _ROW16 (16-bit only);
  *   block    packed: lanes per row (1, 2, 4, ..., 64); the others: threads per
  *            workgroup (64 x waves).
  * Of the compiled entries with that variant and size that take the call, it

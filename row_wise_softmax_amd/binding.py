@@ -22,7 +22,7 @@ def library_path() -> str:
 # dtype codes of the C ABI
 F32, F16, BF16 = 0, 1, 2
 # kernel variants of the C ABI
-VARIANT_NAMES = {0: "packed", 1: "row", 2: "online", 3: "row_pf"}
+VARIANT_NAMES = {0: "packed", 1: "row", 2: "online", 3: "row_pf", 4: "row16"}
 
 _lib = None
 
@@ -168,7 +168,7 @@ def softmax_select(in_ptr: int, out_ptr: int, cols: int, row_stride: int, dtype:
 
 def softmax_fwd_variant(in_ptr: int, out_ptr: int, rows: int, cols: int, row_stride: int, dtype: int,
                         variant: int, block: int, stream: int = 0) -> None:
-    """Raw entry point through a forced variant (0 packed, 1 row, 2 online, 3 row_pf) and size
+    """Raw entry point through a forced variant (0 packed, 1 row, 2 online, 3 row_pf, 4 row16) and size
     (packed: lanes per row; else threads per workgroup)."""
     lib = _load()
     _check(lib.softmax_fwd_variant(in_ptr, out_ptr, rows, cols, row_stride, dtype, variant, block, stream),

@@ -210,13 +210,35 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // chunks, eight waves of eight up to 4096 (32001 bf16 columns: 5039
         // GB/s against 4326 on sixteen of four) and sixteen waves of eight
         // up to 8192 (50257 columns: 4211 against 3663 online).
-        if (any) {
+        // Plain (not causal, aligned) rows past 4096 chunks (32768 columns)
+        // keep their stored 16-bit values in registers (softmax_row16, half the
+        // registers of widened values), up to 24576 chunks (196608
+        // columns): one read instead of the online kernel's two.  Shapes by
+        // width from a sweep at about 200 MB per tensor (bf16, GB/s, against
+        // the online kernel or the widened row kernel before): eight waves
+        // of 12, 16 or 20 accesses up to 6144, 8192 and 10240 chunks (40960
+        // columns: 5580 against 4771; 65536: 5643 against 4934; 81920: 5075
+        // against 4488), sixteen waves of 12, 16, 20 or 24 beyond (98304:
+        // 4627 against 4485; 128256: 4255 against 4145, 5092 against 4694
+        // at 4096 rows; 151936: 4484 against 4256).
+        if (!any && !causal && nacc > 4096) {
+            struct Shape { int64_t chunks; int waves, vpl; };
+            constexpr Shape kRow16[] = {{6144, 8, 12},   {8192, 8, 16},   {10240, 8, 20}, {12288, 16, 12},
+                                        {16384, 16, 16}, {20480, 16, 20}, {24576, 16, 24}};
+            for (const Shape& r : kRow16) {
+                if (nacc <= r.chunks) {
+                    e = find(dtype, SOFTMAX_VARIANT_ROW16, false, vec16, 64 * r.waves, r.vpl, 1, false);
+                    break;
+                }
+            }
+        }
+        if (e == nullptr && any) {
             if (nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, true);
             else if (nacc <= 4096) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 8, 8, 1, true);
             else if (nacc <= 8192) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, true);
-        } else if (nacc <= 4096) {
+        } else if (e == nullptr && nacc <= 4096) {
             e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 4, 1, false);
-        } else if (nacc <= 8192 && nacc * 10 >= 8192 * 9) {
+        } else if (e == nullptr && nacc <= 8192 && nacc * 10 >= 8192 * 9) {
             e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, false);
         }
         if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ONLINE, causal, vec16, 64 * 16, any ? 4 : 2, 1, any);
@@ -356,7 +378,8 @@ int64_t resident_workgroups(const Entry& e, const void* fn, int block) {
 // largest shift pushes past its last slot.  Row r's shift is
 // (out / 16 + r * pitch / 16) mod 8, a sequence with period at most 8.
 bool line_shift_fits(const Entry& e, const void* out, int64_t cols, int64_t row_stride) {
-    if (e.variant != SOFTMAX_VARIANT_ROW && e.variant != SOFTMAX_VARIANT_ROW_PF) return false;
+    if (e.variant != SOFTMAX_VARIANT_ROW && e.variant != SOFTMAX_VARIANT_ROW_PF && e.variant != SOFTMAX_VARIANT_ROW16)
+        return false;
     const int64_t esz = elem_bytes(e.dtype);
     if (e.vec * esz != 16) return false;
     // row r's first chunk is line (out + r * pitch bytes) / 16 mod 8 of its
@@ -594,7 +617,7 @@ struct SlotSplitRule {
 constexpr SlotSplitRule kSlotSplitF32[] = {
     {int64_t(2) << 20, 192}, {int64_t(1) << 20, 128}, {int64_t(512) << 10, 64}, {int64_t(256) << 10, 16}};
 constexpr SlotSplitRule kSlotSplit16[] = {
-    {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(256) << 10, 128}, {int64_t(128) << 10, 64}};
+    {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(512) << 10, 128}, {int64_t(256) << 10, 64}};
 
 bool splits_through_out(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
                         int dtype) {
@@ -723,7 +746,7 @@ int softmax_fwd_variant(const void* in, void* out, int64_t rows, int64_t cols, i
     bool empty;
     int st = validate(in, out, rows, cols, row_stride, dtype, &empty);
     if (st != SOFTMAX_OK) return st;
-    if (variant < SOFTMAX_VARIANT_PACKED || variant > SOFTMAX_VARIANT_ROW_PF) return SOFTMAX_ERR_BAD_KERNEL;
+    if (variant < SOFTMAX_VARIANT_PACKED || variant > SOFTMAX_VARIANT_ROW16) return SOFTMAX_ERR_BAD_KERNEL;
     if (empty) return SOFTMAX_OK;
     const Entry* e = entry_for_variant(in, out, cols, row_stride, dtype, variant, block);
     if (e == nullptr) return SOFTMAX_ERR_BAD_KERNEL;

@@ -684,6 +684,136 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
     }
 }
 
+// ------------------------------------------ 16-bit rows held as stored values
+//
+// For 16-bit rows wider than the row kernel's registers hold once widened
+// (eight floats per 16-byte access): the same one workgroup per row, one read
+// and one write, but each lane keeps its accesses as loaded, four registers
+// each, and widens them again for every step; each exponential is computed
+// twice, once for the sum and once for the output, where the online kernel
+// would read the row twice.  Same frame, same order of operations as the row
+// kernel, so the same bits wherever both take a row.
+//
+// A lane slot outside the row (past its end, or before its start in a
+// line-shifted launch) loads the row's nearest access instead of nothing, so
+// every load goes straight into the registers that keep it, and each step
+// leaves such slots out: the max skips them and the sum keeps its value, as
+// the row kernel's -inf entries (exponential +0) leave it.
+//
+// An empty asm statement that takes the stored values and gives them back
+// comes before the sum and before the output: the compiler must then widen
+// them afresh, instead of keeping an earlier step's widened values alive,
+// which would take the registers this kernel exists to save.
+template <int V>
+__device__ inline void fresh(u32x4 (&xr)[V]) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) asm volatile("" : "+v"(xr[v]));
+}
+
+template <class E>
+__device__ inline void widen_access(u32x4 r, float* f) {
+    widen_dword<E>(r.x, f);
+    widen_dword<E>(r.y, f + 2);
+    widen_dword<E>(r.z, f + 4);
+    widen_dword<E>(r.w, f + 6);
+}
+
+// The row's exponentials in frame fr added to s in the row kernel's order,
+// each entry first less `sub`: the max for rows rebased as in
+// rebase_large_max, else +0, which leaves every entry as it is.
+template <class E, int V>
+__device__ inline float row16_sum(const u32x4 (&xr)[V], int i0, int nacc, float sub, float coef, float fr) {
+    float s = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int idx = v * kWave + i0;
+        float f[8];
+        widen_access<E>(xr[v], f);
+        float t = s;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += exp_in_frame(f[e] - sub, coef, fr);
+        s = idx >= 0 && idx < nacc ? t : s;
+    }
+    return s;
+}
+
+template <class E, int V>
+__device__ inline void row16_store(const u32x4 (&xr)[V], u32x4* q, int i0, int nacc, float sub, float coef,
+                                   float fr, float r) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int idx = v * kWave + i0;
+        if (idx >= 0 && idx < nacc) {
+            float f[8];
+            widen_access<E>(xr[v], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = exp_in_frame(f[e] - sub, coef, fr) * r;
+            store_elems<E, 8>(q + v * kWave, f);
+        }
+    }
+}
+
+template <class E, int W, int V, bool Shift = false>
+__global__ void __launch_bounds__(W * kWave) softmax_row16(Args a) {
+    static_assert(E::kBytes == 2, "16-bit types only");
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    const float coef = a.coef;
+    const int nacc = a.nacc;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const u32x4* in = static_cast<const u32x4*>(a.in) + row * a.stride;
+        u32x4* out = static_cast<u32x4*>(a.out) + row * a.stride;
+        int i0 = first_access<V>(t, line_shift<E, 8, Shift>(out));
+        // taken per row: per-access offsets and masks hoisted out of the row
+        // loop would hold registers through all of it
+        asm volatile("" : "+v"(i0));
+        u32x4 xr[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int idx = v * kWave + i0;
+            xr[v] = ld<true>(in + (idx < 0 ? 0 : idx < nacc ? idx : nacc - 1));
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int idx = v * kWave + i0;
+            float f[8];
+            widen_access<E>(xr[v], f);
+            float cm = f[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
+            m = idx >= 0 && idx < nacc ? fmaxf(m, cm) : m;
+        }
+        m = group_reduce<kWave, OpMax>(m);
+        if (W > 1) {
+            if (lane == 0) red_max[wave] = m;
+            __syncthreads();
+            m = red_max[0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) m = fmaxf(m, red_max[w]);
+        }
+        const bool rebase = !frame_small(m, coef);  // m is the same in every lane
+        const float sub = rebase ? m : 0.0f;
+        const float fr = frame_of(rebase ? 0.0f : m, coef);
+        fresh<V>(xr);
+        float s = row16_sum<E, V>(xr, i0, nacc, sub, coef, fr);
+        s = group_reduce<kWave, OpSum>(s);
+        if (W > 1) {
+            if (lane == 0) red_sum[wave] = s;
+            __syncthreads();
+            s = red_sum[0];
+#pragma unroll
+            for (int w = 1; w < W; ++w) s += red_sum[w];
+        }
+        const float r = recip_sum(s);
+        fresh<V>(xr);
+        row16_store<E, V>(xr, out + i0, i0, nacc, sub, coef, fr, r);
+    }
+}
+
 // ------------------------------------------------------------ online kernel
 //
 // One workgroup of W waves per row of any width.  Pass 1 walks the row in

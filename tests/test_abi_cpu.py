@@ -123,7 +123,9 @@ def test_kernel_table_is_consistent(lib):
     names = [k.name for k in table]
     assert len(set(names)) == len(names)
     for k in table:
-        assert k.variant in ("packed", "row", "row_pf", "online")
+        assert k.variant in ("packed", "row", "row_pf", "online", "row16")
+        if k.variant == "row16":  # 16-bit rows kept as stored: plain, aligned, 16-bit only
+            assert k.dtype in (1, 2) and not k.causal and "any_" not in k.name and k.vec_elems == 8
         assert k.name.startswith("causal_") == k.causal
         assert k.dtype in (0, 1, 2)
         if k.variant == "online":
@@ -325,13 +327,13 @@ def test_few_very_wide_rows_split_through_the_output(lib):
     assert sel(1 << 17, 0, 1) == S and sel(1 << 17, 0, 64) == S and sel(1 << 17, 0, 65) != S
     assert sel(1 << 16, 0, 16) == S and sel(1 << 16, 0, 17) != S
     assert sel((1 << 16) - 4, 0, 8) != S
-    # fp16 / bf16: >= 2 MiB up to 256, >= 1 MiB up to 192, >= 256 KiB up to 128, >= 128 KiB up to 64
+    # fp16 / bf16: >= 2 MiB up to 256, >= 1 MiB up to 192, >= 512 KiB up to 128, >= 256 KiB up to 64
     for code in (1, 2):
         assert sel(1 << 20, code, 256) == S and sel(1 << 20, code, 257) != S
         assert sel(1 << 19, code, 192) == S and sel(1 << 19, code, 193) != S
-        assert sel(1 << 17, code, 128) == S and sel(1 << 17, code, 129) != S
-        assert sel(1 << 16, code, 64) == S and sel(1 << 16, code, 65) != S
-        assert sel((1 << 16) - 8, code, 8) != S
+        assert sel(1 << 18, code, 128) == S and sel(1 << 18, code, 129) != S
+        assert sel(1 << 17, code, 64) == S and sel(1 << 17, code, 65) != S
+        assert sel((1 << 17) - 8, code, 8) != S  # 128 KiB rows: the stored-value row kernel
     assert sel((1 << 17) + 4, 0, 3, stride=(1 << 17) + 8) == S          # ragged last tile, padded stride
     assert sel(1 << 17, 0, 8, y=a) != S                                 # in place
     assert sel(1 << 17, 0, 8, x=a + 4, y=b + 4) != S                    # not on the 16-byte path
@@ -364,18 +366,41 @@ def test_any_alignment_dispatch(lib):
 
 
 def test_wide_16bit_rows_take_sixteen_waves(lib):
-    """16-bit rows past 16384 columns: sixteen waves of four (up to 4096 chunks) or
-    eight (at least nine tenths of 8192 chunks) accesses, else the online kernel;
-    fp32 keeps four or eight waves of sixteen."""
+    """16-bit rows past 16384 columns: sixteen waves of four (up to 4096 chunks);
+    causal rows past that sixteen of eight (at least nine tenths of 8192 chunks),
+    else the online kernel; fp32 keeps four or eight waves of sixteen."""
     a, b = 1 << 40, 1 << 41
     table = binding.kernel_table()
     pick = lambda cols, code, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=2000,
                                                                         causal=causal)].name
     assert pick(24576, 2) == "row_bf16_w16_v4" and pick(32000, 1) == "row_f16_w16_v4"
-    assert pick(65536, 2) == "row_bf16_w16_v8" and pick(50304, 2) == "online_bf16_vec_w16_v2"
     assert pick(32000, 2, causal=True) == "causal_row_bf16_w16_v4"
+    assert pick(65536, 2, causal=True) == "causal_row_bf16_w16_v8"
+    assert pick(50304, 2, causal=True) == "causal_online_bf16_vec_w16_v2"
     assert pick(16384, 2) == "row_bf16_w16_v2"  # 2048 chunks: the two-access rule
     assert pick(32000, 0) == "row_f32_w8_v16" and pick(16384, 0) == "row_f32_w4_v16"
+
+
+def test_wide_16bit_rows_keep_stored_values(lib):
+    """Plain, aligned 16-bit rows of 4097..24576 chunks keep their stored values
+    in registers (row16): eight waves of 12, 16, 20 accesses up to 6144, 8192,
+    10240 chunks, sixteen waves of 12, 16, 20, 24 up to 24576; wider rows take
+    the online kernel, and so do causal and any-offset rows."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+
+    def pick(cols, code, rows=2000, x=a, y=b, causal=False):
+        return table[binding.softmax_select(x, y, cols, cols, code, rows=rows, causal=causal)].name
+
+    assert pick(32768, 2) == "row_bf16_w16_v4" and pick(32776, 2) == "row16_bf16_w8_v12"
+    assert pick(49152, 1) == "row16_f16_w8_v12" and pick(49160, 1) == "row16_f16_w8_v16"
+    assert pick(50304, 2) == "row16_bf16_w8_v16" and pick(65536, 2) == "row16_bf16_w8_v16"
+    assert pick(81920, 2) == "row16_bf16_w8_v20" and pick(81928, 2) == "row16_bf16_w16_v12"
+    assert pick(128256, 2) == "row16_bf16_w16_v16" and pick(151936, 2) == "row16_bf16_w16_v20"
+    assert pick(196608, 1) == "row16_f16_w16_v24" and pick(196616, 1) == "online_f16_vec_w16_v2"
+    assert pick(128256, 2, causal=True) == "causal_online_bf16_vec_w16_v2"
+    assert pick(128256, 2, x=a + 2, y=b + 2) == "any_online_bf16_w16_v4"
+    assert pick(50000, 0) == "row_f32_w16_v16"  # fp32 keeps its rule
 
 
 def test_ragged_rule_follows_the_row_count(lib):

@@ -308,8 +308,10 @@ def _magnitude_rows(dtype, cols=512, seed=51):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("family", _FAMILIES + _CAUSAL_FAMILIES)
+@pytest.mark.parametrize("family", _FAMILIES + _CAUSAL_FAMILIES + ["row16_{d}_w8_v12"])
 def test_magnitudes_every_family(dtype, family):
+    if family.startswith("row16_") and dtype == "f32":
+        pytest.skip("the stored-value row kernel is 16-bit only")
     name = family.format(d=dtype)
     k = next((k for k in _TABLE if k.name == name), None)
     assert k is not None, f"no table entry {name}"
@@ -501,3 +503,29 @@ def test_forced_variant_and_size(dtype, variant, block, cols):
                                 torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     check(to_host(out, dtype), x, dtype, O.softmax(x, dtype), label=f"variant {variant}/{block} {dtype} {cols}")
+
+
+# ------------------------- 16-bit rows kept as stored values, against widened
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("cols,stride", [(65536, 65536), (65536 - 8, 65536), (40000, 40008), (8, 8)])
+def test_row16_bits_equal_the_widened_row_kernel(dtype, cols, stride):
+    """row16 (stored 16-bit values, exponentials taken twice) gives the bits of
+    the row kernel of the same shape (values widened once) on the same rows:
+    ordinary, partly and wholly -inf, huge maxima (the rebase), and rows
+    starting inside a 128-byte line (the line-shifted launch)."""
+    table = {k.name: k for k in _TABLE}
+    a = table[f"row_{dtype}_w16_v8"]
+    b = table[f"row16_{dtype}_w16_v8"]
+    rows = 37
+    _say(f"row16 vs row {dtype} rows={rows} cols={cols} stride={stride}")
+    x = W.random_matrix(seed=cols + stride, rows=rows, cols=cols, dtype=dtype, sigma=3.0, row_stride=stride)
+    x[1, : cols // 2] = W.neg_inf(dtype)
+    x[2, :cols] = W.neg_inf(dtype)
+    top = W.cast(np.array([6.0e4 if dtype == "f16" else 3.0e38]), dtype)[0]
+    x[3, : max(1, cols // 7)] = top
+    x[4, :cols] = W.cast(np.linspace(-3.0e4, -2.9e4, cols), dtype)
+    ya = run(x, dtype, cols=cols, kernel_id=a.kid)
+    yb = run(x, dtype, cols=cols, kernel_id=b.kid)
+    assert np.array_equal(ya[:, :cols].view(np.uint16), yb[:, :cols].view(np.uint16)), "bits differ"
+    check(yb, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"row16 {dtype} {cols}")
