@@ -210,24 +210,27 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // chunks, eight waves of eight up to 4096 (32001 bf16 columns: 5039
         // GB/s against 4326 on sixteen of four) and sixteen waves of eight
         // up to 8192 (50257 columns: 4211 against 3663 online).
-        // Plain (not causal, aligned) rows past 4096 chunks (32768 columns)
-        // keep their stored 16-bit values in registers (softmax_row16, half the
-        // registers of widened values), up to 24576 chunks (196608
-        // columns): one read instead of the online kernel's two.  Shapes by
-        // width from a sweep at about 200 MB per tensor (bf16, GB/s, against
-        // the online kernel or the widened row kernel before): eight waves
-        // of 12, 16 or 20 accesses up to 6144, 8192 and 10240 chunks (40960
-        // columns: 5580 against 4771; 65536: 5643 against 4934; 81920: 5075
-        // against 4488), sixteen waves of 12, 16, 20 or 24 beyond (98304:
-        // 4627 against 4485; 128256: 4255 against 4145, 5092 against 4694
-        // at 4096 rows; 151936: 4484 against 4256).
-        if (!any && !causal && nacc > 4096) {
+        // Rows past 4096 chunks (32768 columns) keep their stored 16-bit
+        // values in registers (softmax_row16, half the registers of widened
+        // values), up to 24576 chunks (196608 columns; causal and any-offset
+        // rows, whose masked forms would spill beyond, up to 16384): one read
+        // instead of the online kernel's two.  Shapes by width from a sweep
+        // at about 200 MB per tensor (bf16, GB/s, against the online kernel
+        // or the widened row kernel before): eight waves of 12, 16 or 20
+        // accesses up to 6144, 8192 and 10240 chunks (40960 columns: 5580
+        // against 4771; 65536: 5643 against 4934; 81920: 5075 against 4488),
+        // sixteen waves of 12, 16, 20 or 24 beyond (98304: 4627 against
+        // 4485; 128256: 4255 against 4145, 5092 against 4694 at 4096 rows;
+        // 151936: 4484 against 4256).  Any-offset rows gain 7-43% (50257
+        // columns: 5038 against 4189), causal rows up to 13% (the last 2048
+        // queries of a 65536-key causal matrix: 5575 against 4983).
+        if (nacc > 4096) {
             struct Shape { int64_t chunks; int waves, vpl; };
             constexpr Shape kRow16[] = {{6144, 8, 12},   {8192, 8, 16},   {10240, 8, 20}, {12288, 16, 12},
                                         {16384, 16, 16}, {20480, 16, 20}, {24576, 16, 24}};
             for (const Shape& r : kRow16) {
                 if (nacc <= r.chunks) {
-                    e = find(dtype, SOFTMAX_VARIANT_ROW16, false, vec16, 64 * r.waves, r.vpl, 1, false);
+                    e = find(dtype, SOFTMAX_VARIANT_ROW16, causal, vec16, 64 * r.waves, r.vpl, 1, any);
                     break;
                 }
             }

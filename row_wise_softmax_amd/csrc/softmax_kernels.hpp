@@ -694,11 +694,13 @@ __global__ void __launch_bounds__(W * kWave) softmax_row_pf(Args a) {
 // would read the row twice.  Same frame, same order of operations as the row
 // kernel, so the same bits wherever both take a row.
 //
-// A lane slot outside the row (past its end, or before its start in a
-// line-shifted launch) loads the row's nearest access instead of nothing, so
+// A lane slot outside the accesses that hold the row's loaded elements (past
+// its end or a causal row's kept columns, or before its start in a
+// line-shifted launch) loads the nearest such access instead of nothing, so
 // every load goes straight into the registers that keep it, and each step
 // leaves such slots out: the max skips them and the sum keeps its value, as
-// the row kernel's -inf entries (exponential +0) leave it.
+// the row kernel's -inf entries (exponential +0) leave it.  Causal and
+// any-offset rows mask their boundary accesses as the row kernel does.
 //
 // An empty asm statement that takes the stored values and gives them back
 // comes before the sum and before the output: the compiler must then widen
@@ -718,11 +720,37 @@ __device__ inline void widen_access(u32x4 r, float* f) {
     widen_dword<E>(r.w, f + 6);
 }
 
+template <class E> __device__ inline unsigned short neg_inf_half();
+template <> __device__ inline unsigned short neg_inf_half<F16>() { return 0xFC00u; }
+template <> __device__ inline unsigned short neg_inf_half<BF16>() { return 0xFF80u; }
+
+// Causal and any-offset rows: the stored values outside the row's loaded
+// elements [lo, hi) of access idx -- past a causal row's kept columns, or the
+// neighbouring rows' elements in a shared chunk -- become -inf in place, once,
+// so that every later step reads the row as the row kernel's masked loads
+// leave it.  Only boundary accesses, and the slots outside the row, change.
+template <class E>
+__device__ inline void mask_stored(u32x4& r, int idx, int lo, int hi) {
+    const int first = idx * 8;
+    if (first >= lo && first + 8 <= hi) return;
+    unsigned w[4] = {r.x, r.y, r.z, r.w};
+    const unsigned ninf = neg_inf_half<E>();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (first + e < lo || first + e >= hi) {
+            const int sh = 16 * (e & 1);
+            w[e >> 1] = (w[e >> 1] & ~(0xFFFFu << sh)) | (ninf << sh);
+        }
+    }
+    r = u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // The row's exponentials in frame fr added to s in the row kernel's order,
 // each entry first less `sub`: the max for rows rebased as in
-// rebase_large_max, else +0, which leaves every entry as it is.
+// rebase_large_max, else +0, which leaves every entry as it is.  Accesses
+// outside [0, nread) keep s as it is, as the row kernel's -inf entries do.
 template <class E, int V>
-__device__ inline float row16_sum(const u32x4 (&xr)[V], int i0, int nacc, float sub, float coef, float fr) {
+__device__ inline float row16_sum(const u32x4 (&xr)[V], int i0, int nread, float sub, float coef, float fr) {
     float s = 0.0f;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
@@ -732,49 +760,60 @@ __device__ inline float row16_sum(const u32x4 (&xr)[V], int i0, int nacc, float 
         float t = s;
 #pragma unroll
         for (int e = 0; e < 8; ++e) t += exp_in_frame(f[e] - sub, coef, fr);
-        s = idx >= 0 && idx < nacc ? t : s;
+        s = idx >= 0 && idx < nread ? t : s;
     }
     return s;
 }
 
-template <class E, int V>
-__device__ inline void row16_store(const u32x4 (&xr)[V], u32x4* q, int i0, int nacc, float sub, float coef,
-                                   float fr, float r) {
+// The normalised output of accesses [0, nstore) of the row (any-offset rows:
+// only its own elements, see store_any).
+template <class E, int V, bool Any>
+__device__ inline void row16_store(const u32x4 (&xr)[V], u32x4* q, int i0, int nstore, int lo, int cols, float sub,
+                                   float coef, float fr, float r) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int idx = v * kWave + i0;
-        if (idx >= 0 && idx < nacc) {
+        if (idx >= 0 && idx < nstore) {
             float f[8];
             widen_access<E>(xr[v], f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) f[e] = exp_in_frame(f[e] - sub, coef, fr) * r;
-            store_elems<E, 8>(q + v * kWave, f);
+            if constexpr (Any) store_any<E, 8>(q + v * kWave, idx, lo, lo + cols, f);
+            else store_elems<E, 8>(q + v * kWave, f);
         }
     }
 }
 
-template <class E, int W, int V, bool Shift = false>
+template <class E, int W, int V, bool Causal, bool Shift = false, bool Any = false>
 __global__ void __launch_bounds__(W * kWave) softmax_row16(Args a) {
     static_assert(E::kBytes == 2, "16-bit types only");
+    constexpr bool kMasked = Causal || Any;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int wave = t / kWave;
     const float coef = a.coef;
-    const int nacc = a.nacc;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const u32x4* in = static_cast<const u32x4*>(a.in) + row * a.stride;
-        u32x4* out = static_cast<u32x4*>(a.out) + row * a.stride;
-        int i0 = first_access<V>(t, line_shift<E, 8, Shift>(out));
+        const RowPos<E, 8> pos = row_pos<E, 8, Any>(a, row);
+        const int lo = pos.lo;
+        const int hi = lo + kept_cols<Causal>(row, a);  // the row's loaded elements are [lo, hi)
+        const int nread = kMasked ? (hi + 7) / 8 : a.nacc;  // accesses holding any of them
+        const int nstore = row_chunks<E, 8, Any>(a, lo);    // accesses the output covers
+        int i0 = first_access<V>(t, line_shift<E, 8, Shift>(pos.out));
         // taken per row: per-access offsets and masks hoisted out of the row
         // loop would hold registers through all of it
         asm volatile("" : "+v"(i0));
         u32x4 xr[V];
+        const int last = nread > 0 ? nread - 1 : 0;  // a row's first access always lies within it
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int idx = v * kWave + i0;
-            xr[v] = ld<true>(in + (idx < 0 ? 0 : idx < nacc ? idx : nacc - 1));
+            xr[v] = ld<true>(pos.in + (idx < 0 ? 0 : idx < last ? idx : last));
+        }
+        if constexpr (kMasked) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) mask_stored<E>(xr[v], v * kWave + i0, lo, hi);
         }
         float m = -INFINITY;
 #pragma unroll
@@ -785,7 +824,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row16(Args a) {
             float cm = f[0];
 #pragma unroll
             for (int e = 1; e < 8; ++e) cm = fmaxf(cm, f[e]);
-            m = idx >= 0 && idx < nacc ? fmaxf(m, cm) : m;
+            m = idx >= 0 && idx < nread ? fmaxf(m, cm) : m;
         }
         m = group_reduce<kWave, OpMax>(m);
         if (W > 1) {
@@ -799,7 +838,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row16(Args a) {
         const float sub = rebase ? m : 0.0f;
         const float fr = frame_of(rebase ? 0.0f : m, coef);
         fresh<V>(xr);
-        float s = row16_sum<E, V>(xr, i0, nacc, sub, coef, fr);
+        float s = row16_sum<E, V>(xr, i0, nread, sub, coef, fr);
         s = group_reduce<kWave, OpSum>(s);
         if (W > 1) {
             if (lane == 0) red_sum[wave] = s;
@@ -810,7 +849,7 @@ __global__ void __launch_bounds__(W * kWave) softmax_row16(Args a) {
         }
         const float r = recip_sum(s);
         fresh<V>(xr);
-        row16_store<E, V>(xr, out + i0, i0, nacc, sub, coef, fr, r);
+        row16_store<E, V, Any>(xr, pos.out + i0, i0, nstore, lo, a.cols, sub, coef, fr, r);
     }
 }
 

@@ -124,8 +124,8 @@ def test_kernel_table_is_consistent(lib):
     assert len(set(names)) == len(names)
     for k in table:
         assert k.variant in ("packed", "row", "row_pf", "online", "row16")
-        if k.variant == "row16":  # 16-bit rows kept as stored: plain, aligned, 16-bit only
-            assert k.dtype in (1, 2) and not k.causal and "any_" not in k.name and k.vec_elems == 8
+        if k.variant == "row16":  # 16-bit rows kept as stored: 16-bit types only
+            assert k.dtype in (1, 2) and k.vec_elems == 8
         assert k.name.startswith("causal_") == k.causal
         assert k.dtype in (0, 1, 2)
         if k.variant == "online":
@@ -358,7 +358,7 @@ def test_any_alignment_dispatch(lib):
     assert pick(4097, 2) == "any_row_bf16_w4_v3"      # 513 chunks
     assert pick(2049, 0) == "any_row_f32_w4_v3" and pick(4097, 0) == "any_row_f32_w8_v3"
     assert pick(16385, 2) == "any_row_bf16_w16_v3" and pick(32001, 2) == "any_row_bf16_w8_v8"
-    assert pick(50257, 2) == "any_row_bf16_w16_v8"
+    assert pick(50257, 2) == "any_row16_bf16_w8_v16"
     assert pick(4097, 2, rows=64) == "any_rowpf_bf16_w4_v3"  # few rows: the persistent twin
     assert pick(4097, 2, causal=True) == "causal_any_row_bf16_w4_v3"
     assert pick(4096, 2, x=a + 2, y=b + 2) == "any_row_bf16_w4_v3"  # aligned width, pointers inside a chunk
@@ -366,26 +366,26 @@ def test_any_alignment_dispatch(lib):
 
 
 def test_wide_16bit_rows_take_sixteen_waves(lib):
-    """16-bit rows past 16384 columns: sixteen waves of four (up to 4096 chunks);
-    causal rows past that sixteen of eight (at least nine tenths of 8192 chunks),
-    else the online kernel; fp32 keeps four or eight waves of sixteen."""
+    """16-bit rows past 16384 columns: sixteen waves of four, up to 4096 chunks
+    (past that the stored-value kernel, tested on its own); fp32 keeps four or
+    eight waves of sixteen."""
     a, b = 1 << 40, 1 << 41
     table = binding.kernel_table()
     pick = lambda cols, code, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=2000,
                                                                         causal=causal)].name
     assert pick(24576, 2) == "row_bf16_w16_v4" and pick(32000, 1) == "row_f16_w16_v4"
     assert pick(32000, 2, causal=True) == "causal_row_bf16_w16_v4"
-    assert pick(65536, 2, causal=True) == "causal_row_bf16_w16_v8"
-    assert pick(50304, 2, causal=True) == "causal_online_bf16_vec_w16_v2"
+    assert pick(65536, 2, causal=True) == "causal_row16_bf16_w8_v16"
+    assert pick(50304, 2, causal=True) == "causal_row16_bf16_w8_v16"
     assert pick(16384, 2) == "row_bf16_w16_v2"  # 2048 chunks: the two-access rule
     assert pick(32000, 0) == "row_f32_w8_v16" and pick(16384, 0) == "row_f32_w4_v16"
 
 
 def test_wide_16bit_rows_keep_stored_values(lib):
-    """Plain, aligned 16-bit rows of 4097..24576 chunks keep their stored values
-    in registers (row16): eight waves of 12, 16, 20 accesses up to 6144, 8192,
-    10240 chunks, sixteen waves of 12, 16, 20, 24 up to 24576; wider rows take
-    the online kernel, and so do causal and any-offset rows."""
+    """16-bit rows of 4097..24576 chunks keep their stored values in registers
+    (row16): eight waves of 12, 16, 20 accesses up to 6144, 8192, 10240 chunks,
+    sixteen waves of 12, 16, 20, 24 up to 24576 (causal and any-offset rows up
+    to 16384); wider rows take the online kernel."""
     a, b = 1 << 40, 1 << 41
     table = binding.kernel_table()
 
@@ -398,8 +398,12 @@ def test_wide_16bit_rows_keep_stored_values(lib):
     assert pick(81920, 2) == "row16_bf16_w8_v20" and pick(81928, 2) == "row16_bf16_w16_v12"
     assert pick(128256, 2) == "row16_bf16_w16_v16" and pick(151936, 2) == "row16_bf16_w16_v20"
     assert pick(196608, 1) == "row16_f16_w16_v24" and pick(196616, 1) == "online_f16_vec_w16_v2"
-    assert pick(128256, 2, causal=True) == "causal_online_bf16_vec_w16_v2"
-    assert pick(128256, 2, x=a + 2, y=b + 2) == "any_online_bf16_w16_v4"
+    assert pick(128256, 2, causal=True) == "causal_row16_bf16_w16_v16"
+    assert pick(128256, 2, x=a + 2, y=b + 2) == "any_row16_bf16_w16_v16"
+    assert pick(50257, 2) == "any_row16_bf16_w8_v16" and pick(65535, 1) == "any_row16_f16_w8_v20"
+    # masked forms stop at 16384 chunks (131072 columns); plain rows go on to 24576
+    assert pick(151936, 2, causal=True) == "causal_online_bf16_vec_w16_v2"
+    assert pick(151937, 2) == "any_online_bf16_w16_v4"
     assert pick(50000, 0) == "row_f32_w16_v16"  # fp32 keeps its rule
 
 

@@ -508,24 +508,54 @@ def test_forced_variant_and_size(dtype, variant, block, cols):
 # ------------------------- 16-bit rows kept as stored values, against widened
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("cols,stride", [(65536, 65536), (65536 - 8, 65536), (40000, 40008), (8, 8)])
-def test_row16_bits_equal_the_widened_row_kernel(dtype, cols, stride):
+@pytest.mark.parametrize("kind", ["plain", "causal", "any", "causal_any"])
+@pytest.mark.parametrize("cols,stride,offset", [(65536, 65536, 0), (65536 - 8, 65536, 0), (40000, 40008, 0),
+                                                (8, 8, 0), (65529, 65529, 3), (40001, 40003, 1)])
+def test_row16_bits_equal_the_widened_row_kernel(dtype, kind, cols, stride, offset):
     """row16 (stored 16-bit values, exponentials taken twice) gives the bits of
     the row kernel of the same shape (values widened once) on the same rows:
-    ordinary, partly and wholly -inf, huge maxima (the rebase), and rows
-    starting inside a 128-byte line (the line-shifted launch)."""
+    ordinary, partly and wholly -inf, huge maxima (the rebase), rows starting
+    inside a 128-byte line (the line-shifted launch); causal (scaled, kept
+    columns only) and at any element offset (odd widths and pitches, pointers
+    inside a chunk)."""
+    import torch
+    from gpu_util import to_device, to_host
+    aligned = offset == 0 and (cols * 2) % 16 == 0 and (stride * 2) % 16 == 0
+    if (kind in ("any", "causal_any")) == aligned:
+        pytest.skip("alignment decides between the aligned and any-offset kernels")
+    pre = {"plain": "", "causal": "causal_", "any": "any_", "causal_any": "causal_any_"}[kind]
     table = {k.name: k for k in _TABLE}
-    a = table[f"row_{dtype}_w16_v8"]
-    b = table[f"row16_{dtype}_w16_v8"]
+    a = table[f"{pre}row_{dtype}_w16_v8"]
+    b = table[f"{pre}row16_{dtype}_w16_v8"]
     rows = 37
-    _say(f"row16 vs row {dtype} rows={rows} cols={cols} stride={stride}")
+    causal = kind.startswith("causal")
+    diag = cols - rows - 5
+    _say(f"row16 vs row {kind} {dtype} rows={rows} cols={cols} stride={stride} offset={offset}")
     x = W.random_matrix(seed=cols + stride, rows=rows, cols=cols, dtype=dtype, sigma=3.0, row_stride=stride)
     x[1, : cols // 2] = W.neg_inf(dtype)
     x[2, :cols] = W.neg_inf(dtype)
     top = W.cast(np.array([6.0e4 if dtype == "f16" else 3.0e38]), dtype)[0]
     x[3, : max(1, cols // 7)] = top
     x[4, :cols] = W.cast(np.linspace(-3.0e4, -2.9e4, cols), dtype)
-    ya = run(x, dtype, cols=cols, kernel_id=a.kid)
-    yb = run(x, dtype, cols=cols, kernel_id=b.kid)
-    assert np.array_equal(ya[:, :cols].view(np.uint16), yb[:, :cols].view(np.uint16)), "bits differ"
-    check(yb, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"row16 {dtype} {cols}")
+    code = W.dtype_code(dtype)
+    flat = np.zeros(offset + x.size, dtype=x.dtype)
+    flat[offset:] = x.ravel()
+    xd = to_device(flat, dtype)
+    outs = []
+    for k in (a, b):
+        yd = torch.zeros_like(xd)
+        pi, po = xd.data_ptr() + 2 * offset, yd.data_ptr() + 2 * offset
+        stream = torch.cuda.current_stream().cuda_stream
+        if causal:
+            binding.softmax_fwd_causal_kernel(k.kid, pi, po, rows, cols, stride, 0.5, diag, code, stream)
+        else:
+            binding.softmax_fwd_kernel(k.kid, pi, po, rows, cols, stride, code, stream)
+        torch.cuda.synchronize()
+        outs.append(to_host(yd, dtype)[offset:].reshape(rows, stride))
+    assert np.array_equal(outs[0], outs[1]), "bits differ"
+    if causal:
+        ref = O.softmax_causal(x, dtype, 0.5, diag, cols=cols)
+        check(outs[1], x, dtype, ref, cols=cols, label=f"row16 {kind} {dtype} {cols}",
+              keep=causal_mask(rows, cols, diag))
+    else:
+        check(outs[1], x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"row16 {kind} {dtype} {cols}")
