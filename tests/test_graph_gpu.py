@@ -4,7 +4,8 @@ They allocate nothing, never synchronise and issue no memset, so a caller may
 record them in a graph.  One graph here holds a plain softmax, a scaled causal
 softmax, the same over a batch of score matrices, a split-row softmax (caller
 workspace), softmax_fwd's own split of few, very wide rows (three kernels, the
-partials kept in the output) and an attention forward.  It
+partials kept in the output), a vocabulary-width 16-bit softmax (the row kept
+in registers as stored) and an attention forward.  It
 is replayed three times on fresh inputs written between replays by ordinary
 eager work, and after every replay each output must equal, bit for bit, the
 same call made eagerly on the same inputs (every kernel here is
@@ -43,6 +44,7 @@ def _calls(bufs, stream):
                                        W.dtype_code("f32"), stream)
     vr, vc = bufs["vshape"]
     binding.softmax_fwd(bufs["wide"].data_ptr(), bufs["ywide"].data_ptr(), vr, vc, vc, W.dtype_code("bf16"), stream)
+    binding.softmax_fwd(bufs["voc"].data_ptr(), bufs["yvoc"].data_ptr(), 64, 50304, 50304, W.dtype_code("bf16"), stream)
     wr, wc = bufs["wshape"]
     binding.softmax_fwd_split(bufs["w"].data_ptr(), bufs["yw"].data_ptr(), wr, wc, wc, W.dtype_code("f32"),
                               bufs["ws"].data_ptr(), bufs["ws"].numel(), 1, stream)
@@ -58,6 +60,7 @@ def _inputs(seed):
         "s": W.cast(rng.standard_normal((256, 256)), "f32"),
         "sb": W.cast(rng.standard_normal((6 * 64, 64)), "f32"),
         "wide": W.cast(2.0 * rng.standard_normal((8, 1 << 18)), "bf16"),
+        "voc": W.cast(2.0 * rng.standard_normal((64, 50304)), "bf16"),
         "w": W.cast(2.0 * rng.standard_normal((3, 70000)), "f32"),
         "q": W.cast(rng.standard_normal((1, 4, 200, 128)), "f16"),
         "k": W.cast(rng.standard_normal((1, 4, 200, 128)), "f16"),
@@ -79,18 +82,23 @@ def test_captured_graph_replays_match_eager_calls():
     dev = {key: torch.empty(arr.shape, dtype=torch.float16 if arr.dtype == np.uint16 else torch.float32,
                             device="cuda") for key, arr in host.items()}
     dev["wide"] = torch.empty(host["wide"].shape, dtype=torch.bfloat16, device="cuda")
+    dev["voc"] = torch.empty(host["voc"].shape, dtype=torch.bfloat16, device="cuda")
     bufs = dict(dev, shape=(300, 4096), wshape=(3, 70000), vshape=(8, 1 << 18), ashape=(1, 4, 200, 128))
     bufs["y"] = torch.empty_like(dev["x"])
     bufs["ys"] = torch.empty_like(dev["s"])
     bufs["ysb"] = torch.empty_like(dev["sb"])
     bufs["ywide"] = torch.empty_like(dev["wide"])
+    bufs["yvoc"] = torch.empty_like(dev["voc"])
+    kid = binding.softmax_select(dev["voc"].data_ptr(), bufs["yvoc"].data_ptr(), 50304, 50304, W.dtype_code("bf16"),
+                                 rows=64)
+    assert binding.kernel_table()[kid].name.startswith("row16_")  # 16-bit row kept as stored
     assert binding.softmax_select(dev["wide"].data_ptr(), bufs["ywide"].data_ptr(), 1 << 18, 1 << 18,
                                   W.dtype_code("bf16"), rows=8) == binding.SPLIT_KERNEL
     bufs["yw"] = torch.empty_like(dev["w"])
     bufs["o"] = torch.empty_like(dev["q"])
     nbytes = binding.split_workspace_bytes(3, 70000, W.dtype_code("f32"))
     bufs["ws"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
-    outs = ("y", "ys", "ysb", "ywide", "yw", "o")
+    outs = ("y", "ys", "ysb", "ywide", "yvoc", "yw", "o")
 
     _upload(dev, host)
     side = torch.cuda.Stream()
@@ -141,6 +149,8 @@ def test_captured_graph_replays_match_eager_calls():
             check(ysb, host["sb"], "f32", ref, label="graph batched causal", keep=keep)
             ywide = to_host(got["ywide"], "bf16")
             check(ywide, host["wide"], "bf16", O.softmax(host["wide"], "bf16"), label="graph fwd split")
+            yvoc = to_host(got["yvoc"], "bf16")
+            check(yvoc, host["voc"], "bf16", O.softmax(host["voc"], "bf16"), label="graph stored-value row")
             yw = to_host(got["yw"], "f32")
             check(yw, host["w"], "f32", O.softmax(host["w"], "f32"), label="graph split")
             o = decode(to_host(got["o"], "f16"), "f16")
