@@ -612,7 +612,7 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
 // a launch of 2-4 us.  Measured for fp32, fp16 and bf16 at 8 .. 256 rows of
 // 64 KiB .. 4 MiB against one workgroup per row; each line is where the split
 // gained at least 5% (e.g. fp32 4 MiB rows: 9.7x at 8 rows, 1.5x at 128; bf16
-// 512 KiB rows: 3.3x at 8, 1.2x at 128).
+// 512 KiB rows: 3.3x at 8, 1.2x at 128; bf16 224 KiB rows: 1.5x at 8).
 struct SlotSplitRule {
     int64_t min_row_bytes;
     int64_t max_rows;
@@ -620,14 +620,19 @@ struct SlotSplitRule {
 constexpr SlotSplitRule kSlotSplitF32[] = {
     {int64_t(2) << 20, 192}, {int64_t(1) << 20, 128}, {int64_t(512) << 10, 64}, {int64_t(256) << 10, 16}};
 constexpr SlotSplitRule kSlotSplit16[] = {
-    {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(512) << 10, 128}, {int64_t(256) << 10, 64}};
+    {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(512) << 10, 128}, {int64_t(224) << 10, 64},
+    {int64_t(192) << 10, 32}};
 
 bool splits_through_out(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
                         int dtype) {
     if (in == out || !aligned16(in, out, cols, row_stride, dtype)) return false;
     const int64_t row_bytes = cols * elem_bytes(dtype);
-    for (const SlotSplitRule& r : dtype == SOFTMAX_F32 ? kSlotSplitF32 : kSlotSplit16)
-        if (row_bytes >= r.min_row_bytes) return rows <= r.max_rows;
+    const bool f32 = dtype == SOFTMAX_F32;
+    const SlotSplitRule* rules = f32 ? kSlotSplitF32 : kSlotSplit16;
+    const int n = f32 ? int(sizeof(kSlotSplitF32) / sizeof(kSlotSplitF32[0]))
+                      : int(sizeof(kSlotSplit16) / sizeof(kSlotSplit16[0]));
+    for (int i = 0; i < n; ++i)
+        if (row_bytes >= rules[i].min_row_bytes) return rows <= rules[i].max_rows;
     return false;
 }
 
