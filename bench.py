@@ -928,7 +928,7 @@ def chunk_copy(steps: int, warmup: int, mib: int = CHUNK_COPY_MIB, rounds: int =
 
 
 SPLIT_CROSS_ROWS = (8, 16, 32, 64, 128, 192, 256)
-SPLIT_CROSS_ROW_KIB = (64, 128, 192, 224, 256, 512, 1024, 2048, 4096)
+SPLIT_CROSS_ROW_KIB = (64, 128, 192, 224, 256, 384, 512, 1024, 2048, 4096)
 SPLIT_CROSS_MAX_BYTES = 512 << 20
 
 

@@ -102,10 +102,10 @@ extern "C" {
  * is kept in the first 8 bytes of that tile's own output, and a third kernel
  * merges each row's pairs between the other two.  One workgroup per row would
  * keep only `rows` of the 256 compute units busy.  The measured lines: fp32
- * rows of >= 2 MiB up to 192 rows, >= 1 MiB up to 128, >= 512 KiB up to 64,
- * >= 256 KiB up to 16; fp16 / bf16 rows of >= 2 MiB up to 256 rows, >= 1 MiB
- * up to 192, >= 512 KiB up to 128, >= 224 KiB up to 64, >= 192 KiB up to 32.  Results are
- * bit-identical to softmax_fwd_split's.
+ * rows of >= 2 MiB up to 192 rows, >= 1 MiB up to 128, > 256 KiB up to 64,
+ * 256 KiB up to 16; fp16 / bf16 rows of >= 2 MiB up to 256 rows, >= 1 MiB up
+ * to 192, >= 512 KiB up to 128, >= 224 KiB up to 64, >= 192 KiB up to 32.
+ * Results are bit-identical to softmax_fwd_split's.
  */
 int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
                 int dtype, void *stream);

@@ -612,13 +612,18 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
 // a launch of 2-4 us.  Measured for fp32, fp16 and bf16 at 8 .. 256 rows of
 // 64 KiB .. 4 MiB against one workgroup per row; each line is where the split
 // gained at least 5% (e.g. fp32 4 MiB rows: 9.7x at 8 rows, 1.5x at 128; bf16
-// 512 KiB rows: 3.3x at 8, 1.2x at 128; bf16 224 KiB rows: 1.5x at 8).
+// 512 KiB rows: 3.3x at 8, 1.2x at 128; bf16 224 KiB rows: 1.5x at 8).  fp32
+// rows past 256 KiB (65536 columns) leave the register-resident kernels for
+// the two-pass one, and there the split gains up to 64 rows (384 KiB x 32:
+// 1.5x).
 struct SlotSplitRule {
     int64_t min_row_bytes;
     int64_t max_rows;
 };
-constexpr SlotSplitRule kSlotSplitF32[] = {
-    {int64_t(2) << 20, 192}, {int64_t(1) << 20, 128}, {int64_t(512) << 10, 64}, {int64_t(256) << 10, 16}};
+constexpr SlotSplitRule kSlotSplitF32[] = {{int64_t(2) << 20, 192},
+                                           {int64_t(1) << 20, 128},
+                                           {(int64_t(256) << 10) + 16, 64},  // past the register-resident rows
+                                           {int64_t(256) << 10, 16}};
 constexpr SlotSplitRule kSlotSplit16[] = {
     {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(512) << 10, 128}, {int64_t(224) << 10, 64},
     {int64_t(192) << 10, 32}};

@@ -321,10 +321,12 @@ def test_few_very_wide_rows_split_through_the_output(lib):
     def sel(cols, code, rows, x=a, y=b, stride=None, causal=False):
         return binding.softmax_select(x, y, cols, stride or cols, code, rows=rows, causal=causal)
 
-    # fp32: >= 2 MiB rows up to 192 rows, >= 1 MiB up to 128, >= 512 KiB up to 64, >= 256 KiB up to 16
+    # fp32: >= 2 MiB rows up to 192 rows, >= 1 MiB up to 128, past 256 KiB (the two-pass kernel's
+    # widths) up to 64, 256 KiB up to 16
     assert sel(1 << 20, 0, 192) == S and sel(1 << 20, 0, 193) != S
     assert sel(1 << 18, 0, 128) == S and sel(1 << 18, 0, 129) != S
     assert sel(1 << 17, 0, 1) == S and sel(1 << 17, 0, 64) == S and sel(1 << 17, 0, 65) != S
+    assert sel((1 << 16) + 4, 0, 64) == S and sel((1 << 16) + 4, 0, 65) != S and sel(128256, 0, 64) == S
     assert sel(1 << 16, 0, 16) == S and sel(1 << 16, 0, 17) != S
     assert sel((1 << 16) - 4, 0, 8) != S
     # fp16 / bf16: >= 2 MiB up to 256, >= 1 MiB up to 192, >= 512 KiB up to 128, >= 224 KiB up to 64,
