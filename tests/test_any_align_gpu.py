@@ -120,3 +120,38 @@ def test_odd_widths_every_row(dtype, rows, cols):
     y = full[:x.size].reshape(x.shape)
     check_every_row(y, x, dtype, label=f"odd width {dtype} {rows}x{cols}")
     _untouched(full, x, dtype, cols, 0, "odd width")
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_wide_16bit_rows_random_calls(case):
+    """16-bit rows of 32769..200000 columns (the stored-value kernels, plain,
+    causal and at any offset, and the online kernel past them): seeded random
+    width, 1..12 rows, row padding 0..9, offset 0..7 elements, in place or not,
+    plain or causal; every output element against the oracle, and nothing
+    outside the rows written."""
+    rng = np.random.default_rng([96, case])
+    dtype = ["f16", "bf16"][int(rng.integers(0, 2))]
+    cols = int(round(float(np.exp(rng.uniform(np.log(32769.0), np.log(200000.0))))))
+    if rng.random() < 0.4:
+        cols = -(-cols // 8) * 8  # a whole number of 16-byte accesses
+    rows = int(rng.integers(1, 13))
+    stride = cols + int(rng.choice([0, 0, 0, 3, 8, 9]))
+    offset = int(rng.choice([0, 0, 1, 3, 7]))
+    inplace = bool(rng.random() < 0.2)
+    causal = bool(rng.random() < 0.35)
+    diag = int(rng.integers(-rows, cols + 1))
+    label = (f"wide 16-bit #{case}: {dtype} rows={rows} cols={cols} stride={stride} offset={offset} "
+             f"inplace={inplace} causal={causal} diag={diag}")
+    _say(label)
+    x = W.random_matrix(seed=980 + case, rows=rows, cols=cols, dtype=dtype, sigma=float(rng.uniform(0.5, 4.0)),
+                        row_stride=stride)
+    x[0, : cols // 5] = W.neg_inf(dtype)
+    full, name = _run(x, dtype, cols, offset, inplace=inplace, causal=causal, scale=0.5, diag=diag)
+    y = full[offset:offset + x.size].reshape(x.shape)
+    if causal:
+        ref = O.softmax_causal(x, dtype, 0.5, diag, cols=cols)
+        check(y, x, dtype, ref, cols=cols, label=f"{label} ({name})", keep=causal_mask(rows, cols, diag))
+    else:
+        check(y, x, dtype, O.softmax(x, dtype, cols=cols), cols=cols, label=f"{label} ({name})")
+    if not inplace:
+        _untouched(full, x, dtype, cols, offset, label)
