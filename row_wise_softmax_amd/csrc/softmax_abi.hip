@@ -142,15 +142,15 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         e = find(dtype, SOFTMAX_VARIANT_PACKED, causal, vec16, 64, 2, 1, any);
     } else if (nacc <= 2048) {
         // Ragged rows of 129..255 accesses take the general two-wave shape
-        // below (bf16 1200 columns x 64 K rows: 5650 GB/s, against 4590 on
-        // four waves of one; fp32 600 columns: 6026 against 4934 on four
+        // below (bf16 1200 columns x 64 K rows: 5650 GB/s, against 4597 on
+        // four waves of one; fp32 600 columns: 6020 against 4977 on four
         // waves of two), with three exceptions measured across 2 K-64 K
         // rows.  fp32 rows of 240 accesses or more (960 columns), from 8192
         // rows on: four waves of two, half the slots idle (1000 columns x
-        // 64 K rows: 6409 against 6287).  16-bit rows of more than 250
+        // 64 K rows: 6446 against 6244).  16-bit rows of more than 250
         // accesses past 8192 rows: four waves of one, whose 512 slots hold
         // the line shift that 256 cannot (bf16 2040 columns x 64 K rows:
-        // 5921 against 5466).  (16-bit jobs of few rows take four waves of
+        // 5987 against 5532).  (16-bit jobs of few rows take four waves of
         // one by the one-round rule below.)
         if (nacc < 256) {
             int v = 0;
@@ -187,8 +187,8 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         }
         // 16-bit jobs that twice the waves, one access each, still hold in
         // one round: the twin on those, for twice the rows' loads issued at
-        // once (bf16, 256-2048 rows of 2048-8192 columns: 0.5-13% faster;
-        // 512 x 2048: 1048 -> 1188 GB/s).  At two rounds it is 9-16% slower.
+        // once (bf16, 256-2048 rows of 2048-8192 columns: 0.5-8% faster;
+        // 256 x 8192: 1832 -> 1980 GB/s).  At two rounds it is 9-16% slower.
         if (e != nullptr && e->variant == SOFTMAX_VARIANT_ROW_PF && elem_bytes(dtype) == 2 && e->vpl == 2 &&
             rows * (2 * e->lanes / 64) <= kOneRoundWaves) {
             const Entry* one = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, 2 * e->lanes, 1, 1, any);
