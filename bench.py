@@ -237,7 +237,8 @@ def split_shapes(steps: int, warmup: int) -> dict:
              "one_wg_per_row": {"variant": variant, "block": block, "us": round(one * 1e3, 3), "gbps": rate(one)},
              "split_workspace": {"us": round(spl * 1e3, 3), "gbps": rate(spl)},
              "note": "gbps by the metric's 2*rows*cols*size bytes; softmax_fwd splits these rows with the tile pairs "
-                     "kept in its output (three kernels), softmax_fwd_split with a workspace (two); in the counter runs "
+                     "kept in its output (three kernels, two for calls of up to 1024 tiles), softmax_fwd_split with a "
+                     "workspace (two); in the counter runs "
                      "(profiles/counters_wide_rows.txt) the split moved 1.5x those bytes, one workgroup per row 1.0x"}
         log(f"[bench] {wl.name}: softmax_fwd {d['us']} us ({d['gbps']} GB/s, {d['kernel']})"
             f"  one wg per row {d['one_wg_per_row']['us']} us  split+workspace {d['split_workspace']['us']} us")
@@ -986,7 +987,8 @@ def summarize_split_crossover(json_path: str) -> None:
            "Microseconds per call over rotating buffers of at least 768 MiB, seeded N(0, 1) inputs.  `one wg/row`:",
            "the width's one-workgroup-per-row kernel forced (softmax_fwd_variant at softmax_select_variant's pick);",
            "`split+ws`: softmax_fwd_split with a caller workspace, always split (two kernels); `softmax_fwd`: the",
-           "library's own choice, which splits through its output (three kernels) where the path column says so.",
+           "library's own choice, which splits through its output where the path column says so (two kernels up to",
+           "1024 tiles in all, else three).",
            "`gain` = one wg/row / softmax_fwd.", "",
            "| dtype | row KiB | rows | one wg/row us | split+ws us | softmax_fwd us | softmax_fwd path | gain |",
            "|---|---|---|---|---|---|---|---|"]

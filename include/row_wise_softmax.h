@@ -99,13 +99,16 @@ extern "C" {
  * sections "CUDA scaling threads" and "Autotuning").
  * Few, very wide rows, out of place on the 16-byte path, take the split path
  * of softmax_fwd_split below without a workspace: each tile's (max, sum) pair
- * is kept in the first 8 bytes of that tile's own output, and a third kernel
+ * is kept in the first 8 bytes of that tile's own output.  Calls of up to
+ * 1024 tiles merge the pairs in the second kernel, whose last workgroup of
+ * each row writes the tiles' first accesses after the others have read them
+ * (a counter in the row's first slot); larger ones run a third kernel that
  * merges each row's pairs between the other two.  One workgroup per row would
  * keep only `rows` of the 256 compute units busy.  The measured lines: fp32
  * rows of >= 2 MiB up to 192 rows, >= 1 MiB up to 128, > 256 KiB up to 64,
- * 256 KiB up to 16; fp16 / bf16 rows of >= 2 MiB up to 256 rows, >= 1 MiB up
- * to 192, >= 512 KiB up to 128, >= 224 KiB up to 64, >= 192 KiB up to 32.
- * Results are bit-identical to softmax_fwd_split's.
+ * >= 224 KiB up to 32, >= 192 KiB up to 16; fp16 / bf16 rows of >= 2 MiB up to
+ * 256 rows, >= 1 MiB up to 192, >= 512 KiB up to 128, >= 192 KiB up to 64,
+ * >= 128 KiB up to 16.  Results are bit-identical to softmax_fwd_split's.
  */
 int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int64_t row_stride,
                 int dtype, void *stream);

@@ -504,16 +504,28 @@ constexpr int64_t kSplitMaxRows = 1024;  // below this many rows, split when ask
 // 2^28 columns (65536 tiles) 530 us instead of 2350.
 constexpr int64_t kSplitMergeKernelTiles = 4096;
 
+// Calls of up to this many tiles in all take softmax_fwd's own split in two
+// kernels: every workgroup of the norm kernel merges its row's pairs from
+// their slots (scattered 8-byte reads, one per tile of the row) and the last
+// one of the row writes the tiles' first accesses, instead of a merge kernel
+// in between.  That saves the merge kernel's launch and round trips, about
+// 1 us (bf16 256 KiB x 8 rows: 10.7 -> 9.8 us); with more tiles the
+// scattered reads, tiles^2 per row, cost more than that (bf16 512 KiB x 64
+// rows, 2048 tiles: 21.4 us with the merge kernel, 22.9 without).
+constexpr int64_t kSlotDirectTiles = 1024;
+
 struct SplitPair {
     const void* stats;
     const void* norm;         // merges the row's pairs itself
     const void* merge;        // workspace pairs merged once per row ...
     const void* norm_merged;  // ... and read back by the norm kernel
     // 16-byte path only: stats, merge and norm with each tile's pair in its
-    // own output slot (softmax_fwd's own split)
+    // own output slot (softmax_fwd's own split); for rows of few tiles the
+    // norm kernel that merges the slots itself instead
     const void* stats_slot;
     const void* merge_slot;
     const void* norm_slot;
+    const void* norm_slot_direct;
     int vec;
     int tile;  // accesses per tile
 };
@@ -525,11 +537,12 @@ SplitPair split_kernels_of() {
                    (const void*)&rws::softmax_split_norm<E, N, W, V, false, false>,
                    (const void*)&rws::softmax_split_merge<E, N, W, V, false>,
                    (const void*)&rws::softmax_split_norm<E, N, W, V, false, true>,
-                   nullptr, nullptr, nullptr, N, W * 64 * V};
+                   nullptr, nullptr, nullptr, nullptr, N, W * 64 * V};
     if constexpr (N > 1) {
         k.stats_slot = (const void*)&rws::softmax_split_stats<E, N, W, V, true>;
         k.merge_slot = (const void*)&rws::softmax_split_merge<E, N, W, V, true>;
         k.norm_slot = (const void*)&rws::softmax_split_norm<E, N, W, V, true, true>;
+        k.norm_slot_direct = (const void*)&rws::softmax_split_norm<E, N, W, V, true, false>;
     }
     return k;
 }
@@ -565,8 +578,9 @@ int64_t split_workspace(int64_t rows, int64_t cols, int dtype) {
 
 // The split path's kernels in order.  With a workspace (`part`): stats, norm,
 // with the per-row merge between them for rows of many tiles.  Without one
-// (part == nullptr, the 16-byte path, out != in): stats, merge and norm
-// keeping the pairs in the output's tile slots.
+// (part == nullptr, the 16-byte path, out != in): the pairs kept in the
+// output's tile slots, stats and norm for rows of few tiles, stats, merge and
+// norm for the rest.
 int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t row_stride, int dtype, float* part,
                  hipStream_t stream) {
     const SplitPair k = split_for(dtype, aligned16(in, out, cols, row_stride, dtype));
@@ -589,9 +603,12 @@ int launch_split(const void* in, void* out, int64_t rows, int64_t cols, int64_t 
     const Step with_part[] = {{k.stats, grid}, {k.norm, grid}};
     const Step with_part_merged[] = {{k.stats, grid}, {k.merge, row_grid}, {k.norm_merged, grid}};
     const Step in_slots[] = {{k.stats_slot, grid}, {k.merge_slot, row_grid}, {k.norm_slot, grid}};
+    const Step in_slots_direct[] = {{k.stats_slot, grid}, {k.norm_slot_direct, grid}};
     const bool merge_kernel = a.tiles > kSplitMergeKernelTiles;
-    const Step* steps = part == nullptr ? in_slots : merge_kernel ? with_part_merged : with_part;
-    const int nsteps = part != nullptr && !merge_kernel ? 2 : 3;
+    const bool direct = a.work <= kSlotDirectTiles;
+    const Step* steps = part == nullptr ? (direct ? in_slots_direct : in_slots)
+                                        : merge_kernel ? with_part_merged : with_part;
+    const int nsteps = part != nullptr ? (merge_kernel ? 3 : 2) : (direct ? 2 : 3);
     if (part == nullptr && (k.stats_slot == nullptr || in == out)) return SOFTMAX_ERR_BAD_KERNEL;
     void* args[] = {&a};
     for (int i = 0; i < nsteps; ++i) {
@@ -623,10 +640,10 @@ struct SlotSplitRule {
 constexpr SlotSplitRule kSlotSplitF32[] = {{int64_t(2) << 20, 192},
                                            {int64_t(1) << 20, 128},
                                            {(int64_t(256) << 10) + 16, 64},  // past the register-resident rows
-                                           {int64_t(256) << 10, 16}};
-constexpr SlotSplitRule kSlotSplit16[] = {
-    {int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(512) << 10, 128}, {int64_t(224) << 10, 64},
-    {int64_t(192) << 10, 32}};
+                                           {int64_t(224) << 10, 32},
+                                           {int64_t(192) << 10, 16}};
+constexpr SlotSplitRule kSlotSplit16[] = {{int64_t(2) << 20, 256}, {int64_t(1) << 20, 192}, {int64_t(512) << 10, 128},
+                                          {int64_t(192) << 10, 64},  {int64_t(128) << 10, 16}};
 
 bool splits_through_out(const void* in, const void* out, int64_t rows, int64_t cols, int64_t row_stride,
                         int dtype) {

@@ -975,9 +975,16 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
 //
 // With Slot = true there is no workspace: each tile's pair goes to the first
 // 8 bytes of the tile's own output (every tile holds at least one 16-byte
-// access), the merge kernel always runs, and kernel 2 reads its own tile's
-// slot before any thread of its workgroup overwrites it.  This needs an
-// output distinct from the input.
+// access), and the next 4 bytes start at zero.  This needs an output distinct
+// from the input.  Rows of many tiles run the merge kernel, and kernel 2 reads
+// its own tile's slot before any thread of its workgroup overwrites it.  Rows
+// of few tiles skip it (Slot, not Merged): every workgroup of kernel 2 merges
+// the row's pairs from the slots itself and writes its tile except the
+// tile's first access, which holds the slot; then it counts itself done on
+// the counter in the row's first slot, and the workgroup that counts last --
+// every other one of the row has read its pairs by then -- writes the first
+// access of every tile of the row.  Nothing waits for anything, and the bits
+// are the same as on the other paths.
 struct SplitArgs {
     const void* in;
     void* out;
@@ -1047,8 +1054,14 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_stats(SplitArgs a) {
             s = red_s[0];
 #pragma unroll
             for (int w = 1; w < W; ++w) s += red_s[w];
-            f32x2 pr = {m, s};
-            *pair_at<E, N, W, V, Slot>(a, row, int(b - row * a.tiles)) = pr;
+            f32x2* slot = pair_at<E, N, W, V, Slot>(a, row, int(b - row * a.tiles));
+            if constexpr (Slot) {
+                // the pair, then the row's counter (used in the row's first slot) at zero
+                *reinterpret_cast<u32x4*>(slot) = u32x4{__builtin_bit_cast(unsigned, m),
+                                                        __builtin_bit_cast(unsigned, s), 0u, 0u};
+            } else {
+                *slot = f32x2{m, s};
+            }
         }
         __syncthreads();  // red_m / red_s are rewritten for the next tile
     }
@@ -1113,8 +1126,8 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_merge(SplitArgs a) {
 
 template <class E, int N, int W, int V, bool Slot, bool Merged>
 __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
-    static_assert(Merged || !Slot, "the slots are merged by softmax_split_merge");
     typedef typename Access<E, N>::raw raw;
+    constexpr bool kDirect = Slot && !Merged;  // few tiles: the slots merged here, last workgroup finishes
     constexpr int kThreads = W * kWave;
     constexpr int kTile = kThreads * V;
     __shared__ float red_m[W];
@@ -1137,20 +1150,50 @@ __global__ void __launch_bounds__(W * kWave) softmax_split_norm(SplitArgs a) {
             s = pr.y;
             if constexpr (Slot) __syncthreads();  // all have read the slot before the tile's first access is rewritten
         } else {
-            merge_row<E, N, W, V, false>(a, row, red_m, red_s, m, s);
+            merge_row<E, N, W, V, Slot>(a, row, red_m, red_s, m, s);
         }
         const float mu = m == -INFINITY ? 0.0f : m;  // all -inf row: every term exp(-inf) = 0
         const float r = recip_sum(s);
         raw* q = out + row * a.stride + base + t;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            if (base + v * kThreads + t < a.nacc) {
+            // (kDirect: the tile's first access holds the slot, written last)
+            if (base + v * kThreads + t < a.nacc && !(kDirect && v == 0 && t == 0)) {
 #pragma unroll
                 for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - mu, a.coef) * r;
                 store_elems<E, N>(q + v * kThreads, x[v]);
             }
         }
-        __syncthreads();  // red_m / red_s are rewritten for the next tile
+        if constexpr (kDirect) {
+            // merge_row's reads of the slots are complete in every thread
+            // (their values went into its reduction, which ends at a
+            // barrier); count this tile done.  The count needs no release or
+            // acquire: the slots were written by the previous kernel, and the
+            // last workgroup's stores depend on the count's result.  (An
+            // agent-scope release would write back this XCD's L2 for every
+            // tile.)
+            __shared__ int last;
+            if (t == 0) {
+                unsigned* counter = reinterpret_cast<unsigned*>(pair_at<E, N, W, V, Slot>(a, row, 0)) + 2;
+                const unsigned done =
+                    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = done == unsigned(a.tiles - 1);
+            }
+            __syncthreads();
+            if (last) {
+                // every workgroup of the row has read its pairs: write the
+                // first access of each tile (slot and counter included)
+                for (int j = t; j < a.tiles; j += kThreads) {
+                    const int64_t at = row * a.stride + int64_t(j) * kTile;
+                    float f[N];
+                    load_access<E, N, false>(in + at, j * kTile, a.nacc, 0, f);
+#pragma unroll
+                    for (int e = 0; e < N; ++e) f[e] = exp_diff(f[e] - mu, a.coef) * r;
+                    store_elems<E, N>(out + at, f);
+                }
+            }
+        }
+        __syncthreads();  // red_m / red_s (and `last`) are rewritten for the next tile
     }
 }
 

@@ -322,23 +322,24 @@ def test_few_very_wide_rows_split_through_the_output(lib):
         return binding.softmax_select(x, y, cols, stride or cols, code, rows=rows, causal=causal)
 
     # fp32: >= 2 MiB rows up to 192 rows, >= 1 MiB up to 128, past 256 KiB (the two-pass kernel's
-    # widths) up to 64, 256 KiB up to 16
+    # widths) up to 64, >= 224 KiB up to 32, >= 192 KiB up to 16
     assert sel(1 << 20, 0, 192) == S and sel(1 << 20, 0, 193) != S
     assert sel(1 << 18, 0, 128) == S and sel(1 << 18, 0, 129) != S
     assert sel(1 << 17, 0, 1) == S and sel(1 << 17, 0, 64) == S and sel(1 << 17, 0, 65) != S
     assert sel((1 << 16) + 4, 0, 64) == S and sel((1 << 16) + 4, 0, 65) != S and sel(128256, 0, 64) == S
-    assert sel(1 << 16, 0, 16) == S and sel(1 << 16, 0, 17) != S
-    assert sel((1 << 16) - 4, 0, 8) != S
-    # fp16 / bf16: >= 2 MiB up to 256, >= 1 MiB up to 192, >= 512 KiB up to 128, >= 224 KiB up to 64,
-    # >= 192 KiB up to 32
+    assert sel(1 << 16, 0, 32) == S and sel(1 << 16, 0, 33) != S
+    assert sel(57344, 0, 32) == S and sel(57344, 0, 33) != S
+    assert sel(49152, 0, 16) == S and sel(49152, 0, 17) != S and sel(49152 - 4, 0, 8) != S
+    # fp16 / bf16: >= 2 MiB up to 256, >= 1 MiB up to 192, >= 512 KiB up to 128, >= 192 KiB up to 64,
+    # >= 128 KiB up to 16
     for code in (1, 2):
         assert sel(1 << 20, code, 256) == S and sel(1 << 20, code, 257) != S
         assert sel(1 << 19, code, 192) == S and sel(1 << 19, code, 193) != S
         assert sel(1 << 18, code, 128) == S and sel(1 << 18, code, 129) != S
         assert sel(1 << 17, code, 64) == S and sel(1 << 17, code, 65) != S
-        assert sel(114688, code, 64) == S and sel(114688, code, 65) != S
-        assert sel(98304, code, 32) == S and sel(98304, code, 33) != S
-        assert sel(98304 - 8, code, 8) != S  # below 192 KiB: the stored-value row kernel
+        assert sel(98304, code, 64) == S and sel(98304, code, 65) != S
+        assert sel(65536, code, 16) == S and sel(65536, code, 17) != S
+        assert sel(65536 - 8, code, 8) != S  # below 128 KiB: one workgroup per row
     assert sel((1 << 17) + 4, 0, 3, stride=(1 << 17) + 8) == S          # ragged last tile, padded stride
     assert sel(1 << 17, 0, 8, y=a) != S                                 # in place
     assert sel(1 << 17, 0, 8, x=a + 4, y=b + 4) != S                    # not on the 16-byte path

@@ -3,7 +3,7 @@
 They allocate nothing, never synchronise and issue no memset, so a caller may
 record them in a graph.  One graph here holds a plain softmax, a scaled causal
 softmax, the same over a batch of score matrices, a split-row softmax (caller
-workspace), softmax_fwd's own split of few, very wide rows (three kernels, the
+workspace), softmax_fwd's own split of few, very wide rows (two kernels, the
 partials kept in the output), a vocabulary-width 16-bit softmax (the row kept
 in registers as stored) and an attention forward.  It
 is replayed three times on fresh inputs written between replays by ordinary
