@@ -159,10 +159,13 @@ def _run_fwd(x, dtype, cols, inplace=False):
 @pytest.mark.parametrize("dtype,rows,cols,stride", [
     ("f32", 1, 1 << 17, None), ("f32", 5, (1 << 17) + 4, (1 << 17) + 8), ("f32", 64, 1 << 17, None),
     ("f32", 16, 1 << 16, None), ("f32", 3, 1 << 20, None), ("f16", 2, 1 << 18, None),
-    ("bf16", 9, (1 << 18) + 8, (1 << 18) + 16), ("bf16", 64, 1 << 17, None), ("bf16", 128, 1 << 18, None)])
+    ("bf16", 9, (1 << 18) + 8, (1 << 18) + 16), ("bf16", 64, 1 << 17, None), ("bf16", 128, 1 << 18, None),
+    # 1024 tiles in all (two kernels, the last workgroup of each row finishing) and 1056 (the merge kernel)
+    ("bf16", 32, 1 << 18, None), ("bf16", 33, 1 << 18, None), ("f32", 3, 7 * 16384 + 4, None)])
 def test_fwd_splits_few_very_wide_rows(dtype, rows, cols, stride):
     """softmax_fwd on few, very wide rows out of place: the split path with each
-    tile's (max, sum) in its own output slot.  Every row against the oracle, the
+    tile's (max, sum) in its own output slot, in two kernels or, past 1024
+    tiles in all, three.  Every row against the oracle, the
     same bits as softmax_fwd_split's workspace path, padding untouched."""
     from gpu_util import check_every_row
     stride = stride or cols
