@@ -881,21 +881,27 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const RowPos<E, N> pos = row_pos<E, N, Any>(a, row);
-        const raw* p = pos.in + t;
+        // Slot i of a chunk holds access i - sh (the line shift of the row
+        // kernels): each wave's 64 accesses then cover whole 128-byte lines of
+        // the output, where a row starting inside a line would split one at
+        // every wave.  Slots before the row's first access stay empty.
+        const int sh = line_shift<E, N, true>(pos.out);
+        const int t0 = t - sh;  // this thread's access in chunk 0
+        const raw* p = pos.in + t0;
         const int kept = kept_cols<Causal>(row, a);
         // accesses that hold at least one kept column
         const int nread = Causal || Any ? (pos.lo + kept + N - 1) / N : a.nacc;
         const int nacc = row_chunks<E, N, Any>(a, pos.lo);
         float lm = -INFINITY;  // lane running max; -inf: nothing finite seen yet
         float ls = 0.0f;       // lane sum of e^(c (x - lm))
-        for (int c = 0; c < nread; c += kChunk) {
+        for (int c = 0; c < nread + sh; c += kChunk) {
             float x[V][N];
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                load_one<E, N, Causal, Any, true>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, pos.lo, kept,
+                load_one<E, N, Causal, Any, true>(p + c + v * kThreads, c + v * kThreads + t0, a.nacc, pos.lo, kept,
                                                   x[v]);
 #pragma unroll
-            for (int v = 0; v < V; ++v) mask_one<N, Any>(c + v * kThreads + t, pos.lo, kept, x[v]);
+            for (int v = 0; v < V; ++v) mask_one<N, Any>(c + v * kThreads + t0, pos.lo, kept, x[v]);
             float cm = x[0][0];
 #pragma unroll
             for (int v = 0; v < V; ++v)
@@ -926,22 +932,22 @@ __global__ void __launch_bounds__(W * kWave) softmax_online(Args a) {
         const float m = lm == -INFINITY ? 0.0f : lm;  // all -inf row: every term exp(-inf) = 0
         const float r = recip_sum(ls);
 
-        raw* q = pos.out + t;
-        for (int c = 0; c < nacc; c += kChunk) {
+        raw* q = pos.out + t0;
+        for (int c = 0; c < nacc + sh; c += kChunk) {
             float x[V][N];
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                load_one<E, N, Causal, Any>(p + c + v * kThreads, c + v * kThreads + t, a.nacc, pos.lo, kept, x[v]);
+                load_one<E, N, Causal, Any>(p + c + v * kThreads, c + v * kThreads + t0, a.nacc, pos.lo, kept, x[v]);
 #pragma unroll
-            for (int v = 0; v < V; ++v) mask_one<N, Any>(c + v * kThreads + t, pos.lo, kept, x[v]);
+            for (int v = 0; v < V; ++v) mask_one<N, Any>(c + v * kThreads + t0, pos.lo, kept, x[v]);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const int idx = c + v * kThreads + t;
+                const int idx = c + v * kThreads + t0;
                 if constexpr (Any) {
 #pragma unroll
                     for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m, coef) * r;
                     store_any<E, N>(q + c + v * kThreads, idx, pos.lo, pos.lo + a.cols, x[v]);
-                } else if (idx < a.nacc) {
+                } else if (idx >= 0 && idx < a.nacc) {
 #pragma unroll
                     for (int e = 0; e < N; ++e) x[v][e] = exp_diff(x[v][e] - m, coef) * r;
                     store_elems<E, N>(q + c + v * kThreads, x[v]);
