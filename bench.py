@@ -1076,6 +1076,86 @@ def summarize_ragged_rows(json_path: str) -> None:
     print("\n".join(out))
 
 
+PAST_POW2_CHUNKS = (300, 340, 375, 420, 520, 580, 625, 700, 750, 800, 960, 1100, 1250, 1400, 1500, 1650, 1950,
+                    2200, 2500, 2800, 3300, 3800)
+PAST_POW2_BYTES = (200_000_000, 50_000_000)
+
+
+def past_pow2(steps: int, warmup: int) -> list:
+    """Aligned rows of 300..3800 16-byte accesses (chunk counts between powers
+    of two), bf16 and fp32, at about 200 MB and 50 MB per tensor: softmax_fwd
+    and every plain row kernel (widened or, 16-bit, stored values) whose slots
+    hold the row without doubling it.  Seeded N(0, 1) inputs drawn on the
+    device, rotating buffers of at least 1 GiB, the median of three interleaved
+    timings each."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    table = binding.kernel_table()
+    out = []
+    for dt in ("bf16", "f32"):
+        code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
+        for nacc in PAST_POW2_CHUNKS:
+            cols = nacc * 16 // esz
+            for size in PAST_POW2_BYTES:
+                rows = size // (cols * esz)
+                nbytes = rows * cols * esz
+                n = n_buffers(2 * nbytes)
+                g = torch.Generator(device="cuda").manual_seed(cols + rows)
+                xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
+                ys = [torch.empty_like(x) for x in xs]
+                kid = binding.softmax_select(xs[0].data_ptr(), ys[0].data_ptr(), cols, cols, code, rows=rows)
+                runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols,
+                                                                     cols, code, stream)}
+                for k in table:
+                    if k.dtype != code or k.causal or not k.name.startswith(("row_", "row16_")):
+                        continue
+                    if nacc <= k.lanes * k.vecs_per_lane <= 2 * nacc:
+                        runs[k.name] = (lambda kk: lambda i: binding.softmax_fwd_kernel(
+                            kk, xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols, code, stream))(k.kid)
+                spin_up(runs["softmax_fwd"], n, 0.2)
+                got = {k: [] for k in runs}
+                for _ in range(3):
+                    for k, f in runs.items():
+                        ms = time_launches(f, n, steps, warmup, spin_s=0.01)
+                        got[k].append(2 * nbytes / (ms * 1e-3) / 1e9)
+                r = {"dtype": dt, "rows": rows, "cols": cols, "accesses": nacc, "kernel": table[kid].name,
+                     "gbps": {k: round(sorted(v)[1], 1) for k, v in got.items()}}
+                log(f"[bench] past-pow2 {dt} {rows}x{cols}: {r}")
+                out.append(r)
+                del xs, ys
+                torch.cuda.empty_cache()
+    return out
+
+
+def summarize_past_pow2(json_path: str) -> None:
+    """Write profiles/past_pow2_widths.md from `bench.py --past-pow2 --past-pow2-out` JSON."""
+    rows = json.load(open(json_path))
+    src = os.path.relpath(os.path.abspath(json_path), ROOT)
+    out = ["# Rows between powers of two of 16-byte accesses: row shapes by waves and accesses per lane, MI355X (gfx950)",
+           "", "Commands (repository root):", "",
+           f"    python3 bench.py --past-pow2 --past-pow2-out {src}",
+           f"    python3 bench.py --summarize-past-pow2 {src}", "",
+           "Contiguous aligned tensors of about 200 MB and 50 MB, seeded N(0, 1) inputs, rotating buffers of at",
+           "least 1 GiB, median of three interleaved timings; GB/s by the metric's 2·rows·cols·size bytes.",
+           "`wWvV`: the plain row kernel forced on W waves of V accesses per lane (`16wWvV`: the 16-bit kernel",
+           "that keeps stored values), the shapes whose slots hold the row at most twice over.  `pick / best`: softmax_fwd against the fastest shape of its line.", "",
+           "| dtype | cols | accesses | rows | pick | softmax_fwd | best shape | best | next | pick / best |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        g = r["gbps"]
+        shapes = sorted(((v, k) for k, v in g.items() if k != "softmax_fwd"), reverse=True)
+        best = max([g["softmax_fwd"]] + [v for v, _ in shapes])
+        short = lambda k: ("16" if k.startswith("row16_") else "") + k.split("_", 2)[2].replace("_", "")
+        nxt = ", ".join(f"{short(k)} {v:.0f}" for v, k in shapes[1:4])
+        bname = short(shapes[0][1])
+        out.append(f"| {r['dtype']} | {r['cols']} | {r['accesses']} | {r['rows']} | {r['kernel']} | "
+                   f"{g['softmax_fwd']:.0f} | {bname} | {shapes[0][0]:.0f} | {nxt} | {g['softmax_fwd'] / best:.3f} |")
+    path = os.path.join(PROFILE_DIR, "past_pow2_widths.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 FEW_ROWS_WIDTHS = {"f32": (1024, 2048, 4096, 8192), "bf16": (2048, 4096, 8192, 16384)}
 FEW_ROWS = (256, 512, 1024, 2048, 4096)
 
@@ -1545,6 +1625,11 @@ def main() -> int:
     ap.add_argument("--ragged-out", default=None, help="JSON file for --ragged-rows")
     ap.add_argument("--summarize-ragged-rows", metavar="JSON", default=None,
                     help="write profiles/ragged_widths_rows.md from --ragged-rows JSON and exit")
+    ap.add_argument("--past-pow2", action="store_true",
+                    help="time rows of 300..3800 accesses: the pick and each row shape that holds them")
+    ap.add_argument("--past-pow2-out", default=None, help="JSON file for --past-pow2")
+    ap.add_argument("--summarize-past-pow2", metavar="JSON", default=None,
+                    help="write profiles/past_pow2_widths.md from --past-pow2 JSON and exit")
     ap.add_argument("--split-crossover", action="store_true",
                     help="time one workgroup per row, the split path and softmax_fwd on few, very wide rows")
     ap.add_argument("--split-out", default=None, help="JSON file for --split-crossover")
@@ -1581,6 +1666,9 @@ def main() -> int:
         return 0
     if args.summarize_ragged_rows:
         summarize_ragged_rows(args.summarize_ragged_rows)
+        return 0
+    if args.summarize_past_pow2:
+        summarize_past_pow2(args.summarize_past_pow2)
         return 0
     if args.summarize_chunk_copy:
         summarize_chunk_copy(*args.summarize_chunk_copy[:2])
@@ -1650,6 +1738,12 @@ def main() -> int:
         table = few_rows(args.steps, args.warmup)
         if args.few_out:
             with open(args.few_out, "w") as f:
+                json.dump(table, f, indent=1)
+        return 0
+    if args.past_pow2:
+        table = past_pow2(args.steps, args.warmup)
+        if args.past_pow2_out:
+            with open(args.past_pow2_out, "w") as f:
                 json.dump(table, f, indent=1)
         return 0
     if args.ragged_rows:

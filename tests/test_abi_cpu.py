@@ -311,6 +311,60 @@ def test_few_16bit_rows_take_one_access_on_twice_the_waves(lib):
     assert pick(4097, 2, 64) == "any_rowpf_bf16_w4_v3"    # three accesses: the twin as it is
 
 
+def test_rows_just_past_a_power_of_two_take_three_accesses(lib):
+    """Aligned rows that fill little of the two-access shape's slots take three
+    accesses on half the waves, by the measured fill lines (16-bit: 75% on
+    sixteen waves, 70% on eight, 62% on four; fp32: 62% on sixteen, 53% on
+    eight); fuller rows, jobs of few rows and causal rows keep two accesses."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
+                                                                               causal=causal)].name
+    assert pick(8800, 2, 11363) == "row_bf16_w8_v3"          # 1100 chunks of 2048 slots
+    assert pick(12000, 2, 8333) == "row_bf16_w8_v3"          # 1500 chunks of 2048
+    assert pick(8 * 1536, 2, 8000) == "row_bf16_w8_v3"       # 1536: the last inside 75%
+    assert pick(8 * 1537, 2, 8000) == "row_bf16_w16_v2"
+    assert pick(4160, 2, 24038) == "row_bf16_w4_v3"          # 520 chunks of 1024
+    assert pick(8 * 716, 1, 20000) == "row_f16_w4_v3" and pick(8 * 717, 1, 20000) == "row_f16_w8_v2"
+    assert pick(2400, 2, 41666) == "row_bf16_w2_v3"          # 300 chunks of 512
+    assert pick(8 * 317, 2, 40000) == "row_bf16_w2_v3" and pick(8 * 318, 2, 40000) == "row_bf16_w4_v2"
+    assert pick(6000, 2, 16666) == "row_bf16_w8_v2"          # 750 chunks: full enough
+    assert pick(4400, 0, 11363) == "row_f32_w8_v3"           # 1100 chunks of 2048
+    assert pick(4 * 1269, 0, 8000) == "row_f32_w8_v3" and pick(4 * 1270, 0, 8000) == "row_f32_w16_v2"
+    assert pick(2080, 0, 24038) == "row_f32_w4_v3"           # 520 chunks of 1024
+    assert pick(4 * 542, 0, 24000) == "row_f32_w4_v3" and pick(4 * 543, 0, 24000) == "row_f32_w8_v2"
+    assert pick(1200, 0, 41666) == "row_f32_w4_v2"           # fp32 on four waves keeps two
+    # few rows: the two-access shape's persistent twin, as before
+    assert pick(8800, 2, 1024) == "rowpf_bf16_w16_v2" and pick(8800, 2, 2048) == "row_bf16_w16_v2"
+    assert pick(8800, 2, 2049) == "row_bf16_w8_v3"
+    assert pick(8800, 2, 11363, causal=True) == "causal_row_bf16_w16_v2"  # no causal three-access entry
+
+
+def test_rows_past_2048_chunks_take_sixteen_waves_of_three(lib):
+    """Aligned rows of 2049..3072 16-byte accesses take sixteen waves of three,
+    plain, both element sizes; wider rows keep their shapes, and so do causal
+    rows (no such causal entry).  16-bit rows past 75% of sixteen waves of two
+    and at most 2000 accesses, in jobs of 1025..3072 rows, take eight waves of
+    four, not their persistent twin."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
+                                                                               causal=causal)].name
+    assert pick(20000, 2, 5000) == "row_bf16_w16_v3" and pick(8 * 3072, 1, 4000) == "row_f16_w16_v3"
+    assert pick(8 * 3073, 2, 4000) == "row_bf16_w16_v4"
+    assert pick(10000, 0, 5000) == "row_f32_w16_v3" and pick(4 * 3072, 0, 5000) == "row_f32_w16_v3"
+    assert pick(4 * 3073, 0, 5000) == "row_f32_w4_v16" and pick(16384, 0, 3051) == "row_f32_w4_v16"
+    assert pick(20000, 2, 5000, causal=True) == "causal_row_bf16_w16_v4"
+    assert pick(10000, 0, 5000, causal=True) == "causal_row_f32_w4_v16"
+    assert pick(15600, 2, 1602) == "row_bf16_w8_v4" and pick(8 * 1537, 1, 3072) == "row_f16_w8_v4"
+    assert pick(8 * 2000, 2, 1025) == "row_bf16_w8_v4"
+    assert pick(15600, 2, 3073) == "row_bf16_w16_v2" and pick(15600, 2, 1024) == "rowpf_bf16_w16_v2"
+    assert pick(8 * 2001, 2, 2000) == "row_bf16_w16_v2" and pick(16384, 2, 2000) == "row_bf16_w16_v2"
+    assert pick(8 * 1536, 2, 1500) == "row_bf16_w16_v2"   # inside 75%: sixteen waves of two
+    assert pick(15600, 2, 1602, causal=True) == "causal_row_bf16_w16_v2"
+    assert pick(7800, 0, 1602) == "row_f32_w16_v2"        # fp32 keeps sixteen waves of two
+
+
 def test_few_very_wide_rows_split_through_the_output(lib):
     """softmax_fwd splits few, very wide rows out of place on the 16-byte path,
     by the measured (row bytes, most rows) lines; anything else takes the
@@ -372,14 +426,15 @@ def test_any_alignment_dispatch(lib):
 
 
 def test_wide_16bit_rows_take_sixteen_waves(lib):
-    """16-bit rows past 16384 columns: sixteen waves of four, up to 4096 chunks
-    (past that the stored-value kernel, tested on its own); fp32 keeps four or
-    eight waves of sixteen."""
+    """16-bit rows past 16384 columns: sixteen waves of three up to 3072
+    chunks, of four up to 4096 (past that the stored-value kernel, tested on
+    its own); causal rows sixteen waves of four; fp32 keeps four or eight waves
+    of sixteen past 3072 chunks."""
     a, b = 1 << 40, 1 << 41
     table = binding.kernel_table()
     pick = lambda cols, code, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=2000,
                                                                         causal=causal)].name
-    assert pick(24576, 2) == "row_bf16_w16_v4" and pick(32000, 1) == "row_f16_w16_v4"
+    assert pick(24576, 2) == "row_bf16_w16_v3" and pick(32000, 1) == "row_f16_w16_v4"
     assert pick(32000, 2, causal=True) == "causal_row_bf16_w16_v4"
     assert pick(65536, 2, causal=True) == "causal_row16_bf16_w8_v16"
     assert pick(50304, 2, causal=True) == "causal_row16_bf16_w8_v16"

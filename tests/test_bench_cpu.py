@@ -301,3 +301,17 @@ def test_few_rows_summary(profile_dir, tmp_path):
     text = (profile_dir / "few_rows_shapes.md").read_text()
     assert ("| bf16 | 2048 | 512 | rowpf_bf16_w4_v1 | 1180 | rowpf_bf16_w4_v1 | 1188 | 0.993 | "
             "w8_v1 1148, w2_v2 1048, w4_v2 1031 |") in text
+
+
+def test_past_pow2_summary(profile_dir, tmp_path):
+    """One line per (width, rows): the pick, the fastest forced row shape, the
+    next three, and the pick against the fastest of all."""
+    r = {"dtype": "bf16", "rows": 11363, "cols": 8800, "accesses": 1100, "kernel": "row_bf16_w8_v3",
+         "gbps": {"softmax_fwd": 5950.0, "row_bf16_w8_v3": 5962.0, "row_bf16_w16_v2": 4774.0,
+                  "row_bf16_w8_v4": 5800.0, "row_bf16_w16_v3": 5100.0}}
+    src = tmp_path / "past.json"
+    src.write_text(json.dumps([r]))
+    bench.summarize_past_pow2(str(src))
+    text = (profile_dir / "past_pow2_widths.md").read_text()
+    assert ("| bf16 | 8800 | 1100 | 11363 | row_bf16_w8_v3 | 5950 | w8v3 | 5962 | w8v4 5800, w16v3 5100, "
+            "w16v2 4774 | 0.998 |") in text

@@ -88,6 +88,33 @@ def test_sweep_full_size_every_row(key):
     _say(f"sweep {wl.name} rows {wl.rows} max abs err {err:.3e}")
 
 
+# Rows just past a power of two of 16-byte accesses, in job sizes that take
+# three accesses per lane on half the waves (and one that stays past the fill
+# line), rows of 2049..3072 accesses on sixteen waves of three, and 16-bit rows
+# of 1537..2000 accesses in jobs of 1025..3072 rows on eight waves of four;
+# softmax_fwd picks the kernel, every row is compared.
+_V3_CASES = [("bf16", 2100, 8800, "row_bf16_w8_v3"), ("f16", 2100, 8 * 1536, "row_f16_w8_v3"),
+             ("bf16", 4200, 4160, "row_bf16_w4_v3"), ("bf16", 8300, 2400, "row_bf16_w2_v3"),
+             ("f32", 2100, 4400, "row_f32_w8_v3"), ("f32", 4200, 2080, "row_f32_w4_v3"),
+             ("bf16", 4200, 6000, "row_bf16_w8_v2"), ("bf16", 2100, 20000, "row_bf16_w16_v3"),
+             ("f16", 1500, 24576, "row_f16_w16_v3"), ("f32", 1100, 10000, "row_f32_w16_v3"),
+             ("bf16", 1700, 14400, "row_bf16_w8_v4"), ("f16", 3072, 8 * 1537, "row_f16_w8_v4")]
+
+
+@pytest.mark.parametrize("dtype,rows,cols,kernel", _V3_CASES)
+def test_three_access_dispatch_every_row(dtype, rows, cols, kernel):
+    import torch
+    _say(f"three-access dispatch {dtype} {rows}x{cols} -> {kernel}")
+    x = W.random_matrix(seed=cols, rows=rows, cols=cols, dtype=dtype, sigma=3.0)
+    x[3, : cols // 2] = W.neg_inf(dtype)
+    xd = to_device(x, dtype)
+    yd = torch.empty_like(xd)
+    kid = binding.softmax_select(xd.data_ptr(), yd.data_ptr(), cols, cols, W.dtype_code(dtype), rows=rows)
+    assert binding.kernel_table()[kid].name == kernel
+    y = run(x, dtype, prefill_out=False)
+    check_every_row(y, x, dtype, label=f"{dtype} {rows}x{cols}")
+
+
 # ------------------------------------------------------------ edge shapes
 
 EDGE_WIDTHS = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 257, 511, 513,
