@@ -154,7 +154,9 @@ int softmax_fwd_causal_batched(const void *in, void *out, int64_t rows, int64_t 
 
 /*
  * softmax_fwd_kernel -- the same operation through one forced entry of the
- * compiled kernel table (for width sweeps and tests).  Same arguments and
+ * compiled kernel table, for width sweeps and tests: the per-width search over
+ * launch configurations of "GPU Kernels - Implementing and optimizing Softmax"
+ * (sections "CUDA scaling threads" and "Autotuning").  Same arguments and
  * errors as softmax_fwd, plus SOFTMAX_ERR_BAD_KERNEL when `kernel_id` is out of
  * range, is compiled for another dtype, or cannot take this width, stride or
  * pointer alignment (see softmax_kernel_fits).
@@ -173,7 +175,10 @@ int softmax_fwd_causal_kernel(int kernel_id, const void *in, void *out, int64_t 
 /*
  * softmax_select -- the kernel id softmax_fwd would launch for these
  * arguments, written to *kernel_id, or SOFTMAX_KERNEL_SPLIT when softmax_fwd
- * takes the split path (few, very wide rows).  Validates like softmax_fwd;
+ * takes the split path (few, very wide rows): the choice of kernel shape by
+ * row width from measured crossovers ("fused-softmax-roofline", the closing
+ * discussion of where the fused kernel loses; "GPU Kernels - Implementing and
+ * optimizing Softmax", section "Autotuning").  Validates like softmax_fwd;
  * launches nothing.
  */
 #define SOFTMAX_KERNEL_SPLIT (-1)
