@@ -173,16 +173,16 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         if (e == nullptr && any && w2 >= 4 && nacc <= (w2 / 2) * 64 * 3)
             e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * (w2 / 2), 3, 1, any);
         // Aligned rows just past a power of two do the same where a scan
-        // found it faster (chunk counts 300..1950 at about 200 MB and 50 MB
-        // per tensor, GB/s): 16-bit rows that fill at most 75% of the
-        // two-access shape's slots on sixteen waves (1100 chunks, 8800 bf16
-        // columns: 4774 -> 5962; 1500 chunks: 5594 -> 5935), 70% on eight
-        // (520 chunks: 5222 -> 6146) or 62% on four (300 chunks: 5845 ->
-        // 6128), fp32 rows that fill at most 62% of
-        // sixteen waves (1100 chunks, 4400 columns: 5881 -> 6331) or 53% of
-        // eight (520 chunks: 6134 -> 6339).  Fuller rows keep two accesses
-        // (750 chunks, bf16: 6071 against 5919 on three; fp32: 6385 against
-        // 5935), and so do jobs of few rows, for the persistent twin below.
+        // found it faster (bench.py --past-pow2: chunk counts 300..3800 at
+        // about 200 MB and 50 MB per tensor, GB/s): 16-bit rows that fill at
+        // most 75% of the two-access shape's slots on sixteen waves (1100
+        // chunks, 8800 bf16 columns: 4772 -> 5984; 1500 chunks: 5604 ->
+        // 5951), 70% on eight (520 chunks: 5219 -> 6150) or 62% on four (300
+        // chunks: 5827 -> 6128), fp32 rows that fill at most 62% of sixteen
+        // waves (1100 chunks, 4400 columns: 5894 -> 6373) or 53% of eight
+        // (520 chunks: 6181 -> 6393).  Fuller rows keep two accesses (750
+        // chunks, bf16: 6061 against 5903 on three; fp32: 6409 against 5945),
+        // and so do jobs of few rows, for the persistent twin below.
         if (e == nullptr && !any && w2 >= 4 && rows * (w2 / 2) > kFewRowWaves) {
             const int64_t slots2 = int64_t(w2) * 128;
             const bool v3 = elem_bytes(dtype) == 2
@@ -216,11 +216,10 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         }
         // 16-bit rows of 1537..2000 accesses in jobs of 1025..3072 rows (two
         // to six rounds of sixteen-wave workgroups): eight waves of four, as
-        // they are (1800 chunks x 1700 bf16 rows: 4535 -> 5100 GB/s; 1600 x
-        // 2600: 5086 -> 5342; 1950 x 1602: 4852 -> 5229).  Their persistent
-        // twin is no faster than sixteen waves of two; those lead again from
-        // about 6400 rows (1950 x 6410: 5934 against 5778), and at 2048
-        // chunks from 1700 rows.
+        // they are (1950 chunks x 1602 bf16 rows: 4856 -> 5197 GB/s; 1650 x
+        // 1893: 4739 -> 4973).  Their persistent twin is no faster than
+        // sixteen waves of two; those lead again from about 6400 rows (1950
+        // x 6410: 5924 against 5779), and at 2048 chunks from 1700 rows.
         if (!any && elem_bytes(dtype) == 2 && nacc > 1536 && nacc <= 2000 && rows > 1024 && rows <= 3072) {
             const Entry* w8 = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 8, 4, 1, false);
             if (w8 != nullptr) e = w8;
@@ -272,7 +271,7 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
             else if (nacc <= 8192) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, true);
         } else if (e == nullptr && nacc <= 4096) {
             // up to 3072 chunks sixteen waves of three (2500 chunks, 20000
-            // bf16 columns: 5303 -> 5802 GB/s; 2200: 5113 -> 5642)
+            // bf16 columns: 5306 -> 5807 GB/s; 2200: 5109 -> 5624)
             if (nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, false);
             if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 4, 1, false);
         } else if (e == nullptr && nacc <= 8192 && nacc * 10 >= 8192 * 9) {
@@ -285,8 +284,8 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // columns: 5825 GB/s, against 5625 on eight waves and 5613 on
         // sixteen); where the table has no such shape, 8 or 16 waves
         // Up to 3072 chunks sixteen waves of three instead (2800 chunks,
-        // 11200 columns: 5928 -> 6154 GB/s; 2200: 5881 -> 6166; at 1116
-        // rows 4979 -> 5298).
+        // 11200 columns: 5932 -> 6148 GB/s; 2200: 5896 -> 6156; at 1116
+        // rows 4994 -> 5288).
         if (!any && nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, false);
         const int v4 = pow2_at_least((nacc + 255) / 256);
         for (int w = 4; w <= 16 && e == nullptr; w *= 2) {
