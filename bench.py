@@ -1079,51 +1079,53 @@ def summarize_ragged_rows(json_path: str) -> None:
 PAST_POW2_CHUNKS = (300, 340, 375, 420, 520, 580, 625, 700, 750, 800, 960, 1100, 1250, 1400, 1500, 1650, 1950,
                     2200, 2500, 2800, 3300, 3800)
 PAST_POW2_BYTES = (200_000_000, 50_000_000)
+# fp32 rows that fill the two-access shape exactly, across row counts
+FULL_ROWS_POINTS = tuple(("f32", nacc, rows) for nacc in (256, 512) for rows in (8192, 12288, 16384, 24576, 49152))
 
 
 def past_pow2(steps: int, warmup: int) -> list:
     """Aligned rows of 300..3800 16-byte accesses (chunk counts between powers
-    of two), bf16 and fp32, at about 200 MB and 50 MB per tensor: softmax_fwd
-    and every plain row kernel (widened or, 16-bit, stored values) whose slots
-    hold the row without doubling it.  Seeded N(0, 1) inputs drawn on the
+    of two), bf16 and fp32, at about 200 MB and 50 MB per tensor, and fp32 rows
+    of exactly 256 and 512 accesses at 8 K-48 K rows: softmax_fwd and every
+    plain row kernel (widened or, 16-bit, stored values) whose slots hold the
+    row at most twice over.  Seeded N(0, 1) inputs drawn on the
     device, rotating buffers of at least 1 GiB, the median of three interleaved
     timings each."""
     import torch
     stream = torch.cuda.current_stream().cuda_stream
     table = binding.kernel_table()
     out = []
-    for dt in ("bf16", "f32"):
+    points = [(dt, nacc, size // (nacc * 16)) for dt in ("bf16", "f32") for nacc in PAST_POW2_CHUNKS
+              for size in PAST_POW2_BYTES] + list(FULL_ROWS_POINTS)
+    for dt, nacc, rows in points:
         code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
-        for nacc in PAST_POW2_CHUNKS:
-            cols = nacc * 16 // esz
-            for size in PAST_POW2_BYTES:
-                rows = size // (cols * esz)
-                nbytes = rows * cols * esz
-                n = n_buffers(2 * nbytes)
-                g = torch.Generator(device="cuda").manual_seed(cols + rows)
-                xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
-                ys = [torch.empty_like(x) for x in xs]
-                kid = binding.softmax_select(xs[0].data_ptr(), ys[0].data_ptr(), cols, cols, code, rows=rows)
-                runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols,
-                                                                     cols, code, stream)}
-                for k in table:
-                    if k.dtype != code or k.causal or not k.name.startswith(("row_", "row16_")):
-                        continue
-                    if nacc <= k.lanes * k.vecs_per_lane <= 2 * nacc:
-                        runs[k.name] = (lambda kk: lambda i: binding.softmax_fwd_kernel(
-                            kk, xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols, code, stream))(k.kid)
-                spin_up(runs["softmax_fwd"], n, 0.2)
-                got = {k: [] for k in runs}
-                for _ in range(3):
-                    for k, f in runs.items():
-                        ms = time_launches(f, n, steps, warmup, spin_s=0.01)
-                        got[k].append(2 * nbytes / (ms * 1e-3) / 1e9)
-                r = {"dtype": dt, "rows": rows, "cols": cols, "accesses": nacc, "kernel": table[kid].name,
-                     "gbps": {k: round(sorted(v)[1], 1) for k, v in got.items()}}
-                log(f"[bench] past-pow2 {dt} {rows}x{cols}: {r}")
-                out.append(r)
-                del xs, ys
-                torch.cuda.empty_cache()
+        cols = nacc * 16 // esz
+        nbytes = rows * cols * esz
+        n = n_buffers(2 * nbytes)
+        g = torch.Generator(device="cuda").manual_seed(cols + rows)
+        xs = [torch.randn((rows, cols), generator=g, device="cuda").to(tdt) for _ in range(n)]
+        ys = [torch.empty_like(x) for x in xs]
+        kid = binding.softmax_select(xs[0].data_ptr(), ys[0].data_ptr(), cols, cols, code, rows=rows)
+        runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols,
+                                                             cols, code, stream)}
+        for k in table:
+            if k.dtype != code or k.causal or not k.name.startswith(("row_", "row16_")):
+                continue
+            if nacc <= k.lanes * k.vecs_per_lane <= 2 * nacc:
+                runs[k.name] = (lambda kk: lambda i: binding.softmax_fwd_kernel(
+                    kk, xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols, code, stream))(k.kid)
+        spin_up(runs["softmax_fwd"], n, 0.2)
+        got = {k: [] for k in runs}
+        for _ in range(3):
+            for k, f in runs.items():
+                ms = time_launches(f, n, steps, warmup, spin_s=0.01)
+                got[k].append(2 * nbytes / (ms * 1e-3) / 1e9)
+        r = {"dtype": dt, "rows": rows, "cols": cols, "accesses": nacc, "kernel": table[kid].name,
+             "gbps": {k: round(sorted(v)[1], 1) for k, v in got.items()}}
+        log(f"[bench] past-pow2 {dt} {rows}x{cols}: {r}")
+        out.append(r)
+        del xs, ys
+        torch.cuda.empty_cache()
     return out
 
 

@@ -176,13 +176,24 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // found it faster (bench.py --past-pow2: chunk counts 300..3800 at
         // about 200 MB and 50 MB per tensor, GB/s): 16-bit rows that fill at
         // most 75% of the two-access shape's slots on sixteen waves (1100
-        // chunks, 8800 bf16 columns: 4772 -> 5984; 1500 chunks: 5604 ->
-        // 5951), 70% on eight (520 chunks: 5219 -> 6150) or 62% on four (300
-        // chunks: 5827 -> 6128), fp32 rows that fill at most 62% of sixteen
-        // waves (1100 chunks, 4400 columns: 5894 -> 6373) or 53% of eight
-        // (520 chunks: 6181 -> 6393).  Fuller rows keep two accesses (750
-        // chunks, bf16: 6061 against 5903 on three; fp32: 6409 against 5945),
+        // chunks, 8800 bf16 columns: 4765 -> 5979; 1500 chunks: 5616 ->
+        // 5933), 70% on eight (520 chunks: 5212 -> 6137) or 62% on four (300
+        // chunks: 5846 -> 6106), fp32 rows that fill at most 62% of sixteen
+        // waves (1100 chunks, 4400 columns: 5890 -> 6344) or 53% of eight
+        // (520 chunks: 6157 -> 6364).  Fuller rows keep two accesses (750
+        // chunks, bf16: 6069 against 5924 on three; fp32: 6394 against 5934),
         // and so do jobs of few rows, for the persistent twin below.
+        // fp32 rows that fill the two-access shape exactly (256 or 512
+        // accesses), in jobs of 16384 rows or more: twice the waves, half the
+        // slots idle (bench.py --past-pow2, GB/s: 2048 columns x 49152 rows
+        // 6415 -> 6646, x 16384 rows 6240 -> 6330; 1024 x 49152: 6370 ->
+        // 6518).  Below 16384 rows the gain is within 1% or a loss (1024
+        // columns x 8192 rows: 5186 against 5125).  16-bit rows lost 10-20%
+        // on twice the waves at 4 K-48 K rows (2048 bf16 columns x 49152
+        // rows: 5529 against 6378, a probe), so they keep theirs.
+        if (e == nullptr && !any && !causal && dtype == SOFTMAX_F32 && (nacc == 256 || nacc == 512) &&
+            rows >= 16384)
+            e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 2 * w2, 2, 1, false);
         if (e == nullptr && !any && w2 >= 4 && rows * (w2 / 2) > kFewRowWaves) {
             const int64_t slots2 = int64_t(w2) * 128;
             const bool v3 = elem_bytes(dtype) == 2
@@ -216,10 +227,10 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         }
         // 16-bit rows of 1537..2000 accesses in jobs of 1025..3072 rows (two
         // to six rounds of sixteen-wave workgroups): eight waves of four, as
-        // they are (1950 chunks x 1602 bf16 rows: 4856 -> 5197 GB/s; 1650 x
-        // 1893: 4739 -> 4973).  Their persistent twin is no faster than
+        // they are (1950 chunks x 1602 bf16 rows: 4861 -> 5186 GB/s; 1650 x
+        // 1893: 4732 -> 4957).  Their persistent twin is no faster than
         // sixteen waves of two; those lead again from about 6400 rows (1950
-        // x 6410: 5924 against 5779), and at 2048 chunks from 1700 rows.
+        // x 6410: 5924 against 5794), and at 2048 chunks from 1700 rows.
         if (!any && elem_bytes(dtype) == 2 && nacc > 1536 && nacc <= 2000 && rows > 1024 && rows <= 3072) {
             const Entry* w8 = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 8, 4, 1, false);
             if (w8 != nullptr) e = w8;
@@ -271,7 +282,7 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
             else if (nacc <= 8192) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, true);
         } else if (e == nullptr && nacc <= 4096) {
             // up to 3072 chunks sixteen waves of three (2500 chunks, 20000
-            // bf16 columns: 5306 -> 5807 GB/s; 2200: 5109 -> 5624)
+            // bf16 columns: 5300 -> 5808 GB/s; 2200: 5120 -> 5617)
             if (nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, false);
             if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 4, 1, false);
         } else if (e == nullptr && nacc <= 8192 && nacc * 10 >= 8192 * 9) {
@@ -284,8 +295,8 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // columns: 5825 GB/s, against 5625 on eight waves and 5613 on
         // sixteen); where the table has no such shape, 8 or 16 waves
         // Up to 3072 chunks sixteen waves of three instead (2800 chunks,
-        // 11200 columns: 5932 -> 6148 GB/s; 2200: 5896 -> 6156; at 1116
-        // rows 4994 -> 5288).
+        // 11200 columns: 5918 -> 6118 GB/s; 2200: 5901 -> 6155; at 1116
+        // rows 5006 -> 5294).
         if (!any && nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, false);
         const int v4 = pow2_at_least((nacc + 255) / 256);
         for (int w = 4; w <= 16 && e == nullptr; w *= 2) {

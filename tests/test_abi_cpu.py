@@ -265,7 +265,7 @@ _PICKS = {
     "c5_bf16_16384": "row_bf16_w16_v2",
     "c5_f32_32": "packed_f32_l8_v1_g2", "c5_f32_64": "packed_f32_l16_v1_g2", "c5_f32_128": "packed_f32_l32_v1_g2",
     "c5_f32_256": "packed_f32_l64_v1_g2", "c5_f32_512": "packed_f32_l64_v2_g1", "c5_f32_1000": "row_f32_w4_v2",
-    "c5_f32_1024": "row_f32_w2_v2", "c5_f32_2048": "row_f32_w4_v2", "c5_f32_3000": "row_f32_w8_v2",
+    "c5_f32_1024": "row_f32_w4_v2", "c5_f32_2048": "row_f32_w8_v2", "c5_f32_3000": "row_f32_w8_v2",
     "c5_f32_4096": "row_f32_w8_v2", "c5_f32_8192": "row_f32_w16_v2", "c5_f32_16384": "row_f32_w4_v16",
 }
 
@@ -338,6 +338,23 @@ def test_rows_just_past_a_power_of_two_take_three_accesses(lib):
     assert pick(8800, 2, 1024) == "rowpf_bf16_w16_v2" and pick(8800, 2, 2048) == "row_bf16_w16_v2"
     assert pick(8800, 2, 2049) == "row_bf16_w8_v3"
     assert pick(8800, 2, 11363, causal=True) == "causal_row_bf16_w16_v2"  # no causal three-access entry
+
+
+def test_full_fp32_rows_of_many_rows_take_twice_the_waves(lib):
+    """fp32 rows of exactly 256 or 512 16-byte accesses in jobs of 16384 rows
+    or more take twice the waves of two accesses; fewer rows, other widths,
+    16-bit rows and causal rows keep the general shape."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
+                                                                               causal=causal)].name
+    assert pick(1024, 0, 16384) == "row_f32_w4_v2" and pick(1024, 0, 16383) == "row_f32_w2_v2"
+    assert pick(2048, 0, 16384) == "row_f32_w8_v2" and pick(2048, 0, 16383) == "row_f32_w4_v2"
+    assert pick(2048, 0, 4096) == "rowpf_f32_w4_v2"          # c2's shape: the persistent twin
+    assert pick(4096, 0, 16384) == "row_f32_w8_v2"           # 1024 accesses keep eight waves
+    assert pick(2044, 0, 16384) == "row_f32_w4_v2"           # 511 accesses: not full
+    assert pick(4096, 2, 24414) == "row_bf16_w4_v2"          # 16-bit keeps its shape
+    assert pick(2048, 0, 16384, causal=True) == "causal_row_f32_w4_v2"
 
 
 def test_rows_past_2048_chunks_take_sixteen_waves_of_three(lib):
