@@ -1081,14 +1081,21 @@ PAST_POW2_CHUNKS = (300, 340, 375, 420, 520, 580, 625, 700, 750, 800, 960, 1100,
 PAST_POW2_BYTES = (200_000_000, 50_000_000)
 # fp32 rows that fill the two-access shape exactly, across row counts
 FULL_ROWS_POINTS = tuple(("f32", nacc, rows) for nacc in (256, 512) for rows in (8192, 12288, 16384, 24576, 49152))
+# jobs just past the persistent twin's two rounds (16 waves: 1024 rows; 8 waves: 2048)
+ROUND_POINTS = tuple([("bf16", 2048, r) for r in (1025, 1100, 1200, 1280, 1400, 1700)] +
+                     [("bf16", 1600, r) for r in (1025, 1200, 1280, 1400)] +
+                     [("f32", 2048, r) for r in (1025, 1200, 1400, 1700)] +
+                     [("bf16", 1024, r) for r in (2049, 2200, 2560, 2800)] +
+                     [("f32", 1024, r) for r in (2049, 2400)])
 
 
 def past_pow2(steps: int, warmup: int) -> list:
     """Aligned rows of 300..3800 16-byte accesses (chunk counts between powers
     of two), bf16 and fp32, at about 200 MB and 50 MB per tensor, and fp32 rows
-    of exactly 256 and 512 accesses at 8 K-48 K rows: softmax_fwd and every
-    plain row kernel (widened or, 16-bit, stored values) whose slots hold the
-    row at most twice over.  Seeded N(0, 1) inputs drawn on the
+    of exactly 256 and 512 accesses at 8 K-48 K rows, and jobs of 1 K-3 K
+    rows just past the persistent twin's two rounds: softmax_fwd and every row
+    kernel (widened or, 16-bit, stored values; persistent too where the job has
+    at most 4096 rows) whose slots hold the row at most twice over.  Seeded N(0, 1) inputs drawn on the
     device, rotating buffers of at least 1 GiB, the median of three interleaved
     timings each."""
     import torch
@@ -1096,7 +1103,7 @@ def past_pow2(steps: int, warmup: int) -> list:
     table = binding.kernel_table()
     out = []
     points = [(dt, nacc, size // (nacc * 16)) for dt in ("bf16", "f32") for nacc in PAST_POW2_CHUNKS
-              for size in PAST_POW2_BYTES] + list(FULL_ROWS_POINTS)
+              for size in PAST_POW2_BYTES] + list(FULL_ROWS_POINTS) + list(ROUND_POINTS)
     for dt, nacc, rows in points:
         code, esz, tdt = W.dtype_code(dt), (4 if dt == "f32" else 2), torch_dtype(dt)
         cols = nacc * 16 // esz
@@ -1109,8 +1116,10 @@ def past_pow2(steps: int, warmup: int) -> list:
         runs = {"softmax_fwd": lambda i: binding.softmax_fwd(xs[i].data_ptr(), ys[i].data_ptr(), rows, cols,
                                                              cols, code, stream)}
         for k in table:
-            if k.dtype != code or k.causal or not k.name.startswith(("row_", "row16_")):
+            if k.dtype != code or k.causal or not k.name.startswith(("row_", "row16_", "rowpf_")):
                 continue
+            if k.name.startswith("rowpf_") and rows > 4096:
+                continue  # the persistent twins matter for jobs of few rows only
             if nacc <= k.lanes * k.vecs_per_lane <= 2 * nacc:
                 runs[k.name] = (lambda kk: lambda i: binding.softmax_fwd_kernel(
                     kk, xs[i].data_ptr(), ys[i].data_ptr(), rows, cols, cols, code, stream))(k.kid)
@@ -1140,14 +1149,16 @@ def summarize_past_pow2(json_path: str) -> None:
            "Contiguous aligned tensors of about 200 MB and 50 MB, seeded N(0, 1) inputs, rotating buffers of at",
            "least 1 GiB, median of three interleaved timings; GB/s by the metric's 2·rows·cols·size bytes.",
            "`wWvV`: the plain row kernel forced on W waves of V accesses per lane (`16wWvV`: the 16-bit kernel",
-           "that keeps stored values), the shapes whose slots hold the row at most twice over.  `pick / best`: softmax_fwd against the fastest shape of its line.", "",
+           "that keeps stored values, `pfwWvV`: the persistent twin, timed on jobs of at most 4096 rows), the",
+           "shapes whose slots hold the row at most twice over.  `pick / best`: softmax_fwd against the fastest shape of its line.", "",
            "| dtype | cols | accesses | rows | pick | softmax_fwd | best shape | best | next | pick / best |",
            "|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         g = r["gbps"]
         shapes = sorted(((v, k) for k, v in g.items() if k != "softmax_fwd"), reverse=True)
         best = max([g["softmax_fwd"]] + [v for v, _ in shapes])
-        short = lambda k: ("16" if k.startswith("row16_") else "") + k.split("_", 2)[2].replace("_", "")
+        short = lambda k: ({"row16": "16", "rowpf": "pf"}.get(k.split("_")[0], "") +
+                           k.split("_", 2)[2].replace("_", ""))
         nxt = ", ".join(f"{short(k)} {v:.0f}" for v, k in shapes[1:4])
         bname = short(shapes[0][1])
         out.append(f"| {r['dtype']} | {r['cols']} | {r['accesses']} | {r['rows']} | {r['kernel']} | "

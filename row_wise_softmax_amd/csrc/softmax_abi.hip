@@ -172,28 +172,29 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // half the waves with three accesses each hold it instead.
         if (e == nullptr && any && w2 >= 4 && nacc <= (w2 / 2) * 64 * 3)
             e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * (w2 / 2), 3, 1, any);
-        // Aligned rows just past a power of two do the same where a scan
-        // found it faster (bench.py --past-pow2: chunk counts 300..3800 at
-        // about 200 MB and 50 MB per tensor, GB/s): 16-bit rows that fill at
-        // most 75% of the two-access shape's slots on sixteen waves (1100
-        // chunks, 8800 bf16 columns: 4765 -> 5979; 1500 chunks: 5616 ->
-        // 5933), 70% on eight (520 chunks: 5212 -> 6137) or 62% on four (300
-        // chunks: 5846 -> 6106), fp32 rows that fill at most 62% of sixteen
-        // waves (1100 chunks, 4400 columns: 5890 -> 6344) or 53% of eight
-        // (520 chunks: 6157 -> 6364).  Fuller rows keep two accesses (750
-        // chunks, bf16: 6069 against 5924 on three; fp32: 6394 against 5934),
-        // and so do jobs of few rows, for the persistent twin below.
         // fp32 rows that fill the two-access shape exactly (256 or 512
         // accesses), in jobs of 16384 rows or more: twice the waves, half the
         // slots idle (bench.py --past-pow2, GB/s: 2048 columns x 49152 rows
-        // 6415 -> 6646, x 16384 rows 6240 -> 6330; 1024 x 49152: 6370 ->
-        // 6518).  Below 16384 rows the gain is within 1% or a loss (1024
-        // columns x 8192 rows: 5186 against 5125).  16-bit rows lost 10-20%
+        // 6526 -> 6668, x 16384 rows 6308 -> 6366; 1024 x 49152: 6478 ->
+        // 6545).  Below 16384 rows the gain is within 1% or a loss (1024
+        // columns x 8192 rows: 5248 against 5177).  16-bit rows lost 10-20%
         // on twice the waves at 4 K-48 K rows (2048 bf16 columns x 49152
         // rows: 5529 against 6378, a probe), so they keep theirs.
         if (e == nullptr && !any && !causal && dtype == SOFTMAX_F32 && (nacc == 256 || nacc == 512) &&
             rows >= 16384)
             e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 2 * w2, 2, 1, false);
+        // Aligned rows just past a power of two take half the waves with
+        // three accesses each too, where a scan found it faster
+        // (bench.py --past-pow2: chunk counts 300..3800 at about 200 MB and
+        // 50 MB per tensor, GB/s): 16-bit rows that fill at most 75% of the
+        // two-access shape's slots on sixteen waves (1100 chunks, 8800 bf16
+        // columns: 4819 -> 6042; 1500 chunks: 5654 -> 6022), 70% on eight
+        // (520 chunks: 5260 -> 6192) or 62% on four (300 chunks: 5889 ->
+        // 6185), fp32 rows that fill at most 62% of sixteen waves (1100
+        // chunks, 4400 columns: 5971 -> 6451) or 53% of eight (520 chunks:
+        // 6207 -> 6483).  Fuller rows keep two accesses (750 chunks, bf16:
+        // 6140 against 6024 on three; fp32: 6495 against 6049), and so do jobs
+        // of few rows, for the persistent twin below.
         if (e == nullptr && !any && w2 >= 4 && rows * (w2 / 2) > kFewRowWaves) {
             const int64_t slots2 = int64_t(w2) * 128;
             const bool v3 = elem_bytes(dtype) == 2
@@ -212,7 +213,13 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // loads in flight: 1-5% faster at one round or less, 2-21% at two
         // (4096 x 4096 bf16: 5044 -> 5973 GB/s; 2048 x 2048 fp32: 5080 ->
         // 5170).  From four rounds on the plain kernel is 1-7% ahead.
-        if (e != nullptr && rows * (e->lanes / 64) <= kFewRowWaves) {
+        // fp32 rows on sixteen waves keep the twin up to two and a half
+        // rounds (bench.py --past-pow2, 2048 accesses: 1025 rows 4844 ->
+        // 5588 GB/s, 1200 rows 4980 -> 5596; at 1400 rows the two are even,
+        // 5196 against 5231).
+        const int64_t few_waves =
+            dtype == SOFTMAX_F32 && e != nullptr && e->lanes == 64 * 16 ? kFewRowWaves + kFewRowWaves / 4 : kFewRowWaves;
+        if (e != nullptr && rows * (e->lanes / 64) <= few_waves) {
             const Entry* pf = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, e->lanes, e->vpl, 1, any);
             if (pf != nullptr) e = pf;
         }
@@ -225,15 +232,32 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
             const Entry* one = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, 2 * e->lanes, 1, 1, any);
             if (one != nullptr) e = one;
         }
-        // 16-bit rows of 1537..2000 accesses in jobs of 1025..3072 rows (two
+        // 16-bit rows of 1537..2000 accesses in jobs of 1281..3072 rows (two
         // to six rounds of sixteen-wave workgroups): eight waves of four, as
-        // they are (1950 chunks x 1602 bf16 rows: 4861 -> 5186 GB/s; 1650 x
-        // 1893: 4732 -> 4957).  Their persistent twin is no faster than
+        // they are (1950 chunks x 1602 bf16 rows: 4875 -> 5289 GB/s; 1650 x
+        // 1893: 4784 -> 5056).  Their persistent twin is no faster than
         // sixteen waves of two; those lead again from about 6400 rows (1950
-        // x 6410: 5924 against 5794), and at 2048 chunks from 1700 rows.
-        if (!any && elem_bytes(dtype) == 2 && nacc > 1536 && nacc <= 2000 && rows > 1024 && rows <= 3072) {
+        // x 6410: 5988 against 5889), and at 2048 chunks from 1400 rows.
+        if (!any && elem_bytes(dtype) == 2 && nacc > 1536 && nacc <= 2000 && rows > 1280 && rows <= 3072) {
             const Entry* w8 = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 8, 4, 1, false);
             if (w8 != nullptr) e = w8;
+        }
+        // 16-bit jobs just past the twin's two rounds: a quarter of the
+        // waves with eight accesses each, plain, holds the whole job in one
+        // round.  At 86 registers that shape keeps five waves per SIMD: five
+        // workgroups of four waves per CU (1280 rows) or ten of two (2560).
+        // Past one round it falls behind (bench.py --past-pow2, GB/s: 2048
+        // accesses x 1025 rows 4523 -> 5483, x 1280 rows 4915 -> 5895, x
+        // 1400 rows 4975 against 4520; 1600 accesses x 1200 rows 4541 ->
+        // 5349; 1024 accesses x 2049 rows 4933 -> 5423, x 2560 rows 5180 ->
+        // 5827, x 2800 rows 5328 against 4496).
+        if (!any && !causal && elem_bytes(dtype) == 2) {
+            const Entry* q = nullptr;
+            if (nacc > 1536 && rows > 1024 && rows <= 1280)
+                q = find(dtype, SOFTMAX_VARIANT_ROW, false, vec16, 64 * 4, 8, 1, false);
+            else if (nacc > 768 && nacc <= 1024 && rows > 2048 && rows <= 2560)
+                q = find(dtype, SOFTMAX_VARIANT_ROW, false, vec16, 64 * 2, 8, 1, false);
+            if (q != nullptr) e = q;
         }
     } else if (elem_bytes(dtype) == 2) {
         // 16-bit rows past 2048 chunks (16384 columns) hold 8 values per
@@ -282,7 +306,7 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
             else if (nacc <= 8192) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 8, 1, true);
         } else if (e == nullptr && nacc <= 4096) {
             // up to 3072 chunks sixteen waves of three (2500 chunks, 20000
-            // bf16 columns: 5300 -> 5808 GB/s; 2200: 5120 -> 5617)
+            // bf16 columns: 5354 -> 5880 GB/s; 2200: 5188 -> 5674)
             if (nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, false);
             if (e == nullptr) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 4, 1, false);
         } else if (e == nullptr && nacc <= 8192 && nacc * 10 >= 8192 * 9) {
@@ -295,8 +319,8 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // columns: 5825 GB/s, against 5625 on eight waves and 5613 on
         // sixteen); where the table has no such shape, 8 or 16 waves
         // Up to 3072 chunks sixteen waves of three instead (2800 chunks,
-        // 11200 columns: 5918 -> 6118 GB/s; 2200: 5901 -> 6155; at 1116
-        // rows 5006 -> 5294).
+        // 11200 columns: 6063 -> 6254 GB/s; 2200: 6022 -> 6240; at 1116
+        // rows 5075 -> 5340).
         if (!any && nacc <= 3072) e = find(dtype, SOFTMAX_VARIANT_ROW, causal, vec16, 64 * 16, 3, 1, false);
         const int v4 = pow2_at_least((nacc + 255) / 256);
         for (int w = 4; w <= 16 && e == nullptr; w *= 2) {

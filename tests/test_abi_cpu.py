@@ -288,7 +288,7 @@ def test_few_rows_take_the_persistent_twin(lib):
     pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
                                                                                causal=causal)].name
     assert pick(4096, 2, 4096) == "rowpf_bf16_w4_v2" and pick(4096, 2, 4097) == "row_bf16_w4_v2"
-    assert pick(8192, 2, 2048) == "rowpf_bf16_w8_v2" and pick(8192, 2, 2049) == "row_bf16_w8_v2"
+    assert pick(8192, 2, 2048) == "rowpf_bf16_w8_v2" and pick(8192, 2, 2561) == "row_bf16_w8_v2"
     assert pick(2048, 0, 2048, causal=True) == "causal_rowpf_f32_w4_v2"
     assert pick(16384, 0, 16) == "row_f32_w4_v16"  # rows past the register-resident two-access shapes keep theirs
 
@@ -357,11 +357,45 @@ def test_full_fp32_rows_of_many_rows_take_twice_the_waves(lib):
     assert pick(2048, 0, 16384, causal=True) == "causal_row_f32_w4_v2"
 
 
+def test_jobs_just_past_two_rounds(lib):
+    """16-bit jobs just past the persistent twin's two rounds take a quarter of
+    the waves with eight accesses each, plain, while the job fits one round of
+    that shape (1280 rows of 1537..2048 accesses, 2560 rows of 769..1024);
+    fp32 rows on sixteen waves keep the twin up to 1280 rows."""
+    a, b = 1 << 40, 1 << 41
+    table = binding.kernel_table()
+    pick = lambda cols, code, rows, causal=False: table[binding.softmax_select(a, b, cols, cols, code, rows=rows,
+                                                                               causal=causal)].name
+    assert pick(16384, 2, 1024) == "rowpf_bf16_w16_v2"
+    assert pick(16384, 2, 1025) == "row_bf16_w4_v8" and pick(16384, 1, 1280) == "row_f16_w4_v8"
+    assert pick(16384, 2, 1281) == "row_bf16_w16_v2"
+    assert pick(8 * 1537, 2, 1100) == "row_bf16_w4_v8" and pick(8 * 1536, 2, 1100) == "row_bf16_w16_v2"
+    assert pick(8192, 2, 2048) == "rowpf_bf16_w8_v2"
+    assert pick(8192, 2, 2049) == "row_bf16_w2_v8" and pick(8192, 2, 2560) == "row_bf16_w2_v8"
+    assert pick(8192, 2, 2561) == "row_bf16_w8_v2" and pick(8 * 768, 2, 2200) == "row_bf16_w8_v2"
+    assert pick(16384, 2, 1100, causal=True) == "causal_row_bf16_w16_v2"
+    assert pick(8192, 0, 1024) == "rowpf_f32_w16_v2" and pick(8192, 0, 1280) == "rowpf_f32_w16_v2"
+    assert pick(8192, 0, 1281) == "row_f32_w16_v2"
+    assert pick(4096, 0, 2049) == "row_f32_w8_v2"             # eight waves: the twin up to two rounds
+
+
+def test_quarter_wave_shapes_keep_five_waves_per_simd():
+    """The one-round limits of the rule above assume the 16-bit row kernels of
+    four and two waves with eight accesses each run five waves per SIMD; the
+    committed resource table (from the compiler's remarks) must agree."""
+    text = open(os.path.join(os.path.dirname(__file__), "..", "profiles", "kernel_resources.md")).read()
+    for dt in ("F16", "BF16"):
+        for w in (4, 2):
+            line = next(l for l in text.splitlines()
+                        if f"`rws::softmax_row<rws::{dt}, 8, {w}, 8, false, false, false>`" in l)
+            assert line.rstrip(" |").split("|")[-1].strip() == "5", line
+
+
 def test_rows_past_2048_chunks_take_sixteen_waves_of_three(lib):
     """Aligned rows of 2049..3072 16-byte accesses take sixteen waves of three,
     plain, both element sizes; wider rows keep their shapes, and so do causal
     rows (no such causal entry).  16-bit rows past 75% of sixteen waves of two
-    and at most 2000 accesses, in jobs of 1025..3072 rows, take eight waves of
+    and at most 2000 accesses, in jobs of 1281..3072 rows, take eight waves of
     four, not their persistent twin."""
     a, b = 1 << 40, 1 << 41
     table = binding.kernel_table()
@@ -374,7 +408,7 @@ def test_rows_past_2048_chunks_take_sixteen_waves_of_three(lib):
     assert pick(20000, 2, 5000, causal=True) == "causal_row_bf16_w16_v4"
     assert pick(10000, 0, 5000, causal=True) == "causal_row_f32_w4_v16"
     assert pick(15600, 2, 1602) == "row_bf16_w8_v4" and pick(8 * 1537, 1, 3072) == "row_f16_w8_v4"
-    assert pick(8 * 2000, 2, 1025) == "row_bf16_w8_v4"
+    assert pick(8 * 2000, 2, 1281) == "row_bf16_w8_v4" and pick(8 * 2000, 2, 1280) == "row_bf16_w4_v8"
     assert pick(15600, 2, 3073) == "row_bf16_w16_v2" and pick(15600, 2, 1024) == "rowpf_bf16_w16_v2"
     assert pick(8 * 2001, 2, 2000) == "row_bf16_w16_v2" and pick(16384, 2, 2000) == "row_bf16_w16_v2"
     assert pick(8 * 1536, 2, 1500) == "row_bf16_w16_v2"   # inside 75%: sixteen waves of two

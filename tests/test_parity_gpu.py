@@ -91,14 +91,18 @@ def test_sweep_full_size_every_row(key):
 # Rows just past a power of two of 16-byte accesses, in job sizes that take
 # three accesses per lane on half the waves (and one that stays past the fill
 # line), rows of 2049..3072 accesses on sixteen waves of three, and 16-bit rows
-# of 1537..2000 accesses in jobs of 1025..3072 rows on eight waves of four;
+# of 1537..2000 accesses in jobs of 1281..3072 rows on eight waves of four,
+# jobs just past the persistent twin's two rounds (a quarter of the waves with
+# eight accesses each; fp32 sixteen-wave rows on the twin up to 1280 rows);
 # softmax_fwd picks the kernel, every row is compared.
 _V3_CASES = [("bf16", 2100, 8800, "row_bf16_w8_v3"), ("f16", 2100, 8 * 1536, "row_f16_w8_v3"),
              ("bf16", 4200, 4160, "row_bf16_w4_v3"), ("bf16", 8300, 2400, "row_bf16_w2_v3"),
              ("f32", 2100, 4400, "row_f32_w8_v3"), ("f32", 4200, 2080, "row_f32_w4_v3"),
              ("bf16", 4200, 6000, "row_bf16_w8_v2"), ("bf16", 2100, 20000, "row_bf16_w16_v3"),
              ("f16", 1500, 24576, "row_f16_w16_v3"), ("f32", 1100, 10000, "row_f32_w16_v3"),
-             ("bf16", 1700, 14400, "row_bf16_w8_v4"), ("f16", 3072, 8 * 1537, "row_f16_w8_v4")]
+             ("bf16", 1700, 14400, "row_bf16_w8_v4"), ("f16", 3072, 8 * 1537, "row_f16_w8_v4"),
+             ("bf16", 1100, 16384, "row_bf16_w4_v8"), ("f16", 2200, 8192, "row_f16_w2_v8"),
+             ("f32", 1200, 8192, "rowpf_f32_w16_v2")]
 
 
 @pytest.mark.parametrize("dtype,rows,cols,kernel", _V3_CASES)
