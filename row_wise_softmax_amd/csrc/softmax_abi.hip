@@ -213,12 +213,14 @@ const Entry* pick_16byte(int dtype, bool causal, bool any, int64_t rows, int64_t
         // loads in flight: 1-5% faster at one round or less, 2-21% at two
         // (4096 x 4096 bf16: 5044 -> 5973 GB/s; 2048 x 2048 fp32: 5080 ->
         // 5170).  From four rounds on the plain kernel is 1-7% ahead.
-        // fp32 rows on sixteen waves keep the twin up to two and a half
-        // rounds (bench.py --past-pow2, 2048 accesses: 1025 rows 4844 ->
-        // 5588 GB/s, 1200 rows 4980 -> 5596; at 1400 rows the two are even,
-        // 5196 against 5231).
+        // Plain aligned fp32 rows on sixteen waves keep the twin up to two
+        // and a half rounds (bench.py --past-pow2, 2048 accesses: 1025 rows
+        // 4844 -> 5588 GB/s, 1200 rows 4980 -> 5596; at 1400 rows the two
+        // are even, 5196 against 5231).
         const int64_t few_waves =
-            dtype == SOFTMAX_F32 && e != nullptr && e->lanes == 64 * 16 ? kFewRowWaves + kFewRowWaves / 4 : kFewRowWaves;
+            dtype == SOFTMAX_F32 && !causal && !any && e != nullptr && e->lanes == 64 * 16
+                ? kFewRowWaves + kFewRowWaves / 4
+                : kFewRowWaves;
         if (e != nullptr && rows * (e->lanes / 64) <= few_waves) {
             const Entry* pf = find(dtype, SOFTMAX_VARIANT_ROW_PF, causal, vec16, e->lanes, e->vpl, 1, any);
             if (pf != nullptr) e = pf;

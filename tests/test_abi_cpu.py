@@ -375,7 +375,7 @@ def test_jobs_just_past_two_rounds(lib):
     assert pick(8192, 2, 2561) == "row_bf16_w8_v2" and pick(8 * 768, 2, 2200) == "row_bf16_w8_v2"
     assert pick(16384, 2, 1100, causal=True) == "causal_row_bf16_w16_v2"
     assert pick(8192, 0, 1024) == "rowpf_f32_w16_v2" and pick(8192, 0, 1280) == "rowpf_f32_w16_v2"
-    assert pick(8192, 0, 1281) == "row_f32_w16_v2"
+    assert pick(8192, 0, 1281) == "row_f32_w16_v2" and pick(8192, 0, 1100, causal=True) == "causal_row_f32_w16_v2"
     assert pick(4096, 0, 2049) == "row_f32_w8_v2"             # eight waves: the twin up to two rounds
 
 
